@@ -1,0 +1,336 @@
+"""CPU oracle for the TokenGate gated-prefill path (test infrastructure only).
+
+This module is the slow, plain, float64 statement of what the gated prefill
+path computes. It exists to check the HIP library, and only the tests, the
+smoke check and the CPU-baseline leg of the benchmark may import it. It shares
+no code with the HIP path and imports nothing from the package.
+
+Sources (five web pages about "Token-Gated Language Models", cited by page and
+section):
+  [TC]  Tencent Cloud developer article on TokenGate (Chinese): sections
+        "TokenGate 提前筛选 Token" (early token filtering),
+        "门控机制为评分网络建立梯度路径" (the gate gives the scorer a gradient path),
+        "选择器与模型主干共同适应剪枝" (selector and backbone co-adapt),
+        "TokenGate 的工程验证仍有限" (engineering validation is limited).
+  [FW]  farwalk.ai news summary: section "论文的方法" (the method).
+  [HF]  Hugging Face paper-page mirror: the abstract.
+  [AI]  ai.866data.com article: section "可学习剪枝的机制设计" (mechanism design).
+
+What the pages leave open is fixed by the specification of this project and
+stated at each function: the logit form L = t_h * q.k / sqrt(d) + g_h * s_j,
+an erf-GELU / sigmoid two-layer scorer with biases, forced tokens counted
+inside the budget K, lowest-index tie-break, rotate-half RoPE at the tokens'
+original positions (base 1e6), RMSNorm with eps 1e-6, contiguous GQA groups.
+
+Every function here has pins in the CPU test suite (closed forms, brute force
+on tiny inputs, reductions to library routines and invariants). The only part
+with no pin beyond its own definition is fidelity to the authors' unpublished
+implementation: parity unpinned for that, since no code or worked numbers are
+published.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+# Device status flags (mirrors of the library's documented values; the oracle
+# reports the same conditions for the same inputs).
+FORCED_GT_BUDGET = 1
+BUDGET_GT_LEN = 2
+NAN_SCORE = 4
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Gate scorer
+# ----------------------------------------------------------------------------
+
+def gelu(z):
+    """Exact (erf) GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)).
+
+    The pages call the scorer a lightweight MLP ([AI] mechanism design;
+    [TC] early token filtering); its hidden activation is GELU by the
+    project's specification, in the exact erf form.
+    """
+    z = _f64(z)
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def sigmoid(u):
+    """Logistic function 1 / (1 + exp(-u)); maps the scorer logit into (0, 1)."""
+    u = _f64(u)
+    return 1.0 / (1.0 + np.exp(-u))
+
+
+def gate_score(h, W1, b1, w2, b2) -> np.ndarray:
+    """Importance score of every token from its post-attention residual at layer L.
+
+    [TC] early token filtering and [AI] mechanism design: after layer L's
+    attention, a small MLP reads each token's current representation and
+    emits an importance score. Form: s = sigmoid(w2 . GELU(W1 h + b1) + b2),
+    W1 in nn.Linear layout [H1, D]. No normalisation precedes the scorer.
+    """
+    h = _f64(h)
+    z = h @ _f64(W1).T + _f64(b1)[None, :]
+    u = gelu(z) @ _f64(w2) + float(_f64(b2).reshape(-1)[0])
+    return sigmoid(u)
+
+
+# ----------------------------------------------------------------------------
+# Top-K selection with forced keep
+# ----------------------------------------------------------------------------
+
+def _canon(s: np.ndarray) -> np.ndarray:
+    """Scores as float64 with -0.0 folded onto +0.0 (they compare equal)."""
+    s = _f64(s).copy()
+    s[s == 0.0] = 0.0
+    return s
+
+
+def select_one(s, forced, K: int):
+    """Kept local indices (ascending) of one sequence, and its status flags.
+
+    [TC] early token filtering: a Top-K selector keeps K of the N tokens and
+    designated tokens such as the user's question are never pruned; [AI]
+    mechanism design: only the document body may be pruned. Reading fixed by
+    the specification: the forced tokens count inside K, the remaining
+    K - |F| slots go to the highest scores among the others, equal scores are
+    broken by the lower index, NaN ranks below every number.
+    """
+    s = _canon(s)
+    forced = np.asarray(forced, dtype=bool)
+    n = s.shape[0]
+    flags = 0
+    if np.isnan(s).any():
+        flags |= NAN_SCORE
+    nf = int(forced.sum())
+    if K > n:
+        flags |= BUDGET_GT_LEN
+    if nf > K:
+        flags |= FORCED_GT_BUDGET
+    if flags & (BUDGET_GT_LEN | FORCED_GT_BUDGET):
+        return None, flags
+    r = K - nf
+    cand = np.flatnonzero(~forced)
+    cs = s[cand]
+    isn = np.isnan(cs)
+    neg = np.where(isn, 0.0, -cs)
+    # lexsort: last key is primary -> (isnan, -s, index)
+    order = np.lexsort((cand, neg, isn))
+    chosen = cand[order[:r]]
+    kept = np.sort(np.concatenate([np.flatnonzero(forced), chosen]))
+    return kept.astype(np.int64), flags
+
+
+def topk_select(s, keep_mask, cu_in, cu_kept):
+    """Per-sequence selection over a packed batch.
+
+    Returns (kept_idx [T] int64 global indices, ascending within each
+    sequence and laid out at cu_kept offsets; flags [B] int). Sequences with
+    an error flag leave their slots at -1.
+    """
+    s = np.asarray(s)
+    cu_in = np.asarray(cu_in, dtype=np.int64)
+    cu_kept = np.asarray(cu_kept, dtype=np.int64)
+    B = len(cu_in) - 1
+    mask = np.zeros(s.shape[0], dtype=bool) if keep_mask is None else np.asarray(keep_mask).astype(bool)
+    out = np.full(int(cu_kept[-1]), -1, dtype=np.int64)
+    flags = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        lo, hi = int(cu_in[b]), int(cu_in[b + 1])
+        K = int(cu_kept[b + 1] - cu_kept[b])
+        kept, f = select_one(s[lo:hi], mask[lo:hi], K)
+        flags[b] = f
+        if kept is not None:
+            out[int(cu_kept[b]):int(cu_kept[b + 1])] = kept + lo
+    return out, flags
+
+
+# ----------------------------------------------------------------------------
+# Compaction
+# ----------------------------------------------------------------------------
+
+def compact(h, pos, s, kept_idx, cu_in, cu_kept):
+    """Gather kept rows, their original positions and their scores.
+
+    [TC] early token filtering: only the selected tokens continue into layer
+    L's FFN and the layers above; [FW] the method: above the gate only the K
+    kept tokens are processed. ``pos`` None means each token's position is its
+    index inside its own sequence.
+    """
+    kept = np.asarray(kept_idx, dtype=np.int64)
+    h = np.asarray(h)
+    s = np.asarray(s)
+    if pos is None:
+        cu_in = np.asarray(cu_in, dtype=np.int64)
+        cu_kept = np.asarray(cu_kept, dtype=np.int64)
+        pos_c = np.empty(kept.shape[0], dtype=np.int64)
+        for b in range(len(cu_in) - 1):
+            sl = slice(int(cu_kept[b]), int(cu_kept[b + 1]))
+            pos_c[sl] = kept[sl] - cu_in[b]
+    else:
+        pos_c = np.asarray(pos, dtype=np.int64)[kept]
+    return h[kept], pos_c, s[kept]
+
+
+# ----------------------------------------------------------------------------
+# Upper-layer pieces
+# ----------------------------------------------------------------------------
+
+def rmsnorm(x, w, eps: float):
+    """x / sqrt(mean(x^2) + eps) * w, per row (pre-norm of a Qwen3-style layer)."""
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * _f64(w)
+
+
+def rope(x, pos, base: float):
+    """Rotate-half rotary embedding at the given positions.
+
+    x: [T, H, d]; pos: [T]. For i < d/2, theta_i = pos * base^(-2i/d);
+    x'_i = x_i cos - x_{i+d/2} sin, x'_{i+d/2} = x_{i+d/2} cos + x_i sin.
+    Kept tokens keep their original positions (specification reading: the
+    pages do not say; the original position is the only one under which a
+    kept token's relative offsets are unchanged).
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    inv = base ** (-2.0 * i / d)
+    theta = _f64(pos)[:, None] * inv[None, :]          # [T, d/2]
+    c = np.cos(theta)[:, None, :]
+    sn = np.sin(theta)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * sn, b * c + a * sn], axis=-1)
+
+
+def gated_attention(q, k, v, s_c, t, g, cu_kept, rows: Optional[Sequence[int]] = None,
+                    chunk: int = 512):
+    """Token-gated causal GQA attention over the kept tokens.
+
+    [TC] gradient-path section: the selected tokens' scores keep entering the
+    upper layers' attention and shape its weights, with a per-head learnable
+    gain and temperature; [TC] engineering section: the score enters as a
+    bias on the attention logit of each key; [AI] mechanism design: a bias on
+    the logits above the gate layer. Logit (specification):
+        L_ij = t_h * (q_i,h . k_j,h') / sqrt(d) + g_h * s_c[j],  j <= i,
+    h' = h // (Hq / Hkv); P = softmax_j L; o_i = sum_j P_ij v_j. Causality is
+    within each sequence of the packed batch, in compacted (= ascending
+    position) order.
+
+    Returns (o [T, Hq, d], lse [Hq, T] natural-log log-sum-exp). With
+    ``rows`` only those global rows are computed (others stay zero).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s_c, t, g = _f64(s_c), _f64(t), _f64(g)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    grp = Hq // Hkv
+    o = np.zeros((T, Hq, d))
+    lse = np.zeros((Hq, T))
+    cu = np.asarray(cu_kept, dtype=np.int64)
+    want = None if rows is None else np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    scale = 1.0 / math.sqrt(d)
+    for b in range(len(cu) - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi <= lo:
+            continue
+        if want is None:
+            rs = np.arange(lo, hi)
+        else:
+            rs = want[(want >= lo) & (want < hi)]
+        if rs.size == 0:
+            continue
+        for h in range(Hq):
+            hk = h // grp
+            kk = k[lo:hi, hk, :]
+            vv = v[lo:hi, hk, :]
+            for c0 in range(0, rs.size, chunk):
+                rr = rs[c0:c0 + chunk]
+                logits = t[h] * (q[rr, h, :] @ kk.T) * scale + g[h] * s_c[lo:hi][None, :]
+                jj = np.arange(lo, hi)[None, :]
+                logits = np.where(jj <= rr[:, None], logits, -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                p = np.exp(logits - m)
+                den = p.sum(axis=1, keepdims=True)
+                o[rr, h, :] = (p @ vv) / den
+                lse[h, rr] = (m + np.log(den))[:, 0]
+    return o, lse
+
+
+def silu(x):
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def upper_layer(x, pos_c, s_c, W: Dict[str, np.ndarray], dims, cu_kept,
+                rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """One decoder layer above the gate, run on the kept tokens only.
+
+    [TC] early token filtering: only kept tokens get the FFN and later layers,
+    and no KV is made for pruned tokens. Layer (Qwen3-shaped, specification):
+      n1 = RMSNorm(x) * attn_norm; q,k,v = n1 Wq^T, n1 Wk^T, n1 Wv^T;
+      RoPE on q, k at pos_c; o = gated attention; x1 = x + o Wo^T;
+      n2 = RMSNorm(x1) * ffn_norm; x2 = x1 + (silu(n2 Wg^T) * (n2 Wu^T)) Wd^T.
+    W keys: wq wk wv wo wg wu wd attn_norm ffn_norm t g (float arrays).
+    Returns every intermediate. With ``rows`` (global row ids) the k/v cache
+    is computed for all tokens and the rest only for those rows.
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    Hq, Hkv, d = dims.Hq, dims.Hkv, dims.d
+    eps, base = dims.rms_eps, dims.rope_base
+    n1 = rmsnorm(x, W["attn_norm"], eps)
+    k = (n1 @ _f64(W["wk"]).T).reshape(T, Hkv, d)
+    v = (n1 @ _f64(W["wv"]).T).reshape(T, Hkv, d)
+    k = rope(k, pos_c, base)
+    if rows is None:
+        sel = np.arange(T)
+    else:
+        sel = np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    q = np.zeros((T, Hq, d))
+    q[sel] = rope((n1[sel] @ _f64(W["wq"]).T).reshape(-1, Hq, d), _f64(pos_c)[sel], base)
+    o, lse = gated_attention(q, k, v, s_c, W["t"], W["g"], cu_kept,
+                             rows=None if rows is None else sel)
+    out = {"n1": n1, "q": q, "k": k, "v": v, "o": o, "lse": lse, "rows": sel}
+    x1 = np.zeros_like(x)
+    x1[sel] = x[sel] + o[sel].reshape(-1, Hq * d) @ _f64(W["wo"]).T
+    n2 = np.zeros_like(x)
+    n2[sel] = rmsnorm(x1[sel], W["ffn_norm"], eps)
+    act = np.zeros((T, _f64(W["wg"]).shape[0]))
+    act[sel] = silu(n2[sel] @ _f64(W["wg"]).T) * (n2[sel] @ _f64(W["wu"]).T)
+    x2 = np.zeros_like(x)
+    x2[sel] = x1[sel] + act[sel] @ _f64(W["wd"]).T
+    out.update({"x1": x1, "n2": n2, "act": act, "x2": x2})
+    return out
+
+
+# ----------------------------------------------------------------------------
+# The whole gated prefill above layer L's attention
+# ----------------------------------------------------------------------------
+
+def gated_prefill(h, W1, b1, w2, b2, keep_mask, cu_in, cu_kept, layers, dims, pos=None):
+    """Scorer, selection, compaction and the stack of upper layers.
+
+    [FW] the method and [AI] mechanism design: the forward splits in three;
+    below the gate all N tokens are processed, the gate keeps the top K, and
+    above it only those K tokens run. This function covers the part from the
+    gate on. Selection here runs on the oracle's own scores.
+    """
+    s = gate_score(h, W1, b1, w2, b2)
+    kept, flags = topk_select(s, keep_mask, cu_in, cu_kept)
+    hc, pc, sc = compact(h, pos, s, kept, cu_in, cu_kept)
+    x = _f64(hc)
+    kv = []
+    for W in layers:
+        r = upper_layer(x, pc, sc, W, dims, cu_kept)
+        kv.append((r["k"], r["v"]))
+        x = r["x2"]
+    return {"s": s, "kept": kept, "flags": flags, "pos_c": pc, "s_c": sc, "x": x, "kv": kv}
