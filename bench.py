@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated prefill path on one MI355X.
+
+One step = the whole path above layer L's attention on one batch: gate scorer
+over all N prompt tokens, Top-K selection with forced keep, compaction, and
+the stack of upper layers on the K kept tokens (27 layers at N=32768,
+K=4096, Qwen3-1.7B-shaped). Inputs and weights are seeded synthetic tensors
+already resident in HBM when timing starts.
+
+Prints ONE JSON line: tokens/s (prompt tokens through the gated path per
+second), the gated-attention TFLOPS and its fraction of the bf16 MFMA peak,
+the roofline entry of the dominant kernel (per-kernel durations from HIP
+events recorded around every kernel on the launch stream inside the timed
+region), per-kernel figures, and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated prefill tokens/s + attn TFLOPS (% MFMA peak) at N=32K,K=4096"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen32k")
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--n", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time only the whole step (no per-kernel events)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+        self.n = n
+
+    def record(self, i, stream):
+        assert self.hip.hipEventRecord(self.ev[i], stream) == 0
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(f), self.ev[a], self.ev[b]) == 0
+        return f.value
+
+    def sub(self, start: int, count: int):
+        """Address of events [start, start+count) as a hipEvent_t* for the C ABI."""
+        assert start + count <= self.n
+        return ctypes.c_void_p(ctypes.addressof(self.ev) + start * ctypes.sizeof(ctypes.c_void_p))
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.ev[i])
+
+
+def cpu_baseline(w, dw_host_gate, host_layer):
+    """The fp64 oracle timed on the host: scorer + selection + compaction on the
+    whole prompt and ONE upper layer on all K kept tokens, extrapolated to the
+    workload's layer count."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle as O
+    gi = dw_host_gate
+    W = {"wq": host_layer.wq.value, "wk": host_layer.wk.value, "wv": host_layer.wv.value,
+         "wo": host_layer.wo.value, "wg": host_layer.wg.value, "wu": host_layer.wu.value,
+         "wd": host_layer.wd.value, "attn_norm": host_layer.attn_norm.value,
+         "ffn_norm": host_layer.ffn_norm.value, "t": host_layer.t, "g": host_layer.g}
+    t0 = time.perf_counter()
+    s = O.gate_score(gi.h.value, gi.W1.value, gi.b1.value, gi.w2.value, gi.b2.value)
+    t1 = time.perf_counter()
+    kept, _ = O.topk_select(s, gi.keep_mask, gi.cu_in, gi.cu_kept)
+    t2 = time.perf_counter()
+    hc, pc, sc = O.compact(gi.h.value, None, s, kept, gi.cu_in, gi.cu_kept)
+    t3 = time.perf_counter()
+    O.upper_layer(hc, pc, sc, W, w.dims, gi.cu_kept)
+    t4 = time.perf_counter()
+    t_est = (t3 - t0) + w.layers * (t4 - t3)
+    threads = 0
+    for p in threadpool_info():
+        if p.get("user_api") == "blas":
+            threads = max(threads, int(p.get("num_threads", 0)))
+    return {
+        "value": w.T_in / t_est, "unit": "tokens/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": "fp64 numpy oracle: scorer+select+compact on the full %d-token prompt (%.2f s) "
+                  "and 1 of %d upper layers on all %d kept tokens (%.2f s), layer time x%d"
+                  % (w.T_in, t3 - t0, w.layers, w.T, t4 - t3, w.layers),
+        "host_cores": len(os.sched_getaffinity(0)),
+        "seconds_measured": round(t4 - t0, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the gated prefill path of one "
+              "device); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from learned_token_pruning_post_amd import binding as tg
+    from learned_token_pruning_post_amd.pipeline import DeviceWorkload, GatedPrefill
+    from learned_token_pruning_post_amd.workloads import workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tg.lib()
+    w = workload(args.workload, k=args.k, n=args.n, layers=args.layers)
+    dm = w.dims
+    print("[bench] generating %s: B=%d N=%s K=%s layers=%d" % (w.name, w.B, w.N[:4], w.K[:4], w.layers),
+          file=sys.stderr, flush=True)
+    want_cpu = not args.no_cpu_baseline
+    dw = DeviceWorkload(w, keep_host=False)
+    gp = GatedPrefill(dw)
+    L = len(dw.layers)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.reset_peak_memory_stats()
+
+    per_step = 4 + L * (tg.LAYER_STAGES + 1)
+    use_ev = not args.no_kernel_events
+    ev = HipEvents(2 + (per_step * args.steps if use_ev else 0))
+
+    def step(sidx=None):
+        if sidx is None:
+            gp.run()
+            return
+        base = 2 + sidx * per_step
+        ev.record(base + 0, stream)
+        gp.score()
+        ev.record(base + 1, stream)
+        gp.select()
+        ev.record(base + 2, stream)
+        gp.compact()
+        ev.record(base + 3, stream)
+        for l in range(L):
+            tg.upper_layer_fwd(dw.layers[l], dw.dims, gp.x, gp.pos_c, gp.s_c, dw.cu_kept, w.max_k,
+                               x_out=gp.x, kcache=gp.kcache[l], vcache=gp.vcache[l], ws=gp.ws,
+                               events=ev.sub(base + 4 + l * (tg.LAYER_STAGES + 1), tg.LAYER_STAGES + 1))
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    ev.record(0, stream)
+    for i in range(args.steps):
+        step(i if use_ev else None)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    t_host1 = time.perf_counter()
+    total_ms = ev.ms(0, 1)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = w.T_in / (ms_per_step / 1e3)
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    # ---- per-kernel durations ----
+    T, D, Hq, Hkv, d, I, H1 = w.T, dm.D, dm.Hq, dm.Hkv, dm.d, dm.I, dm.H1
+    elt = 2 if dm.dtype == "bf16" else 4
+    attn_flop = sum(2.0 * d * Hq * k * (k + 1) for k in w.K)
+    kflop = {
+        "gate_score": 2.0 * w.T_in * D * H1 + 2.0 * w.T_in * H1,
+        "qkv_rope_kv": 2.0 * T * D * (Hq + 2 * Hkv) * d,
+        "gated_attn": attn_flop,
+        "o_proj_resid": 2.0 * T * Hq * d * D,
+        "gate_up_swiglu": 2.0 * T * D * 2 * I,
+        "down_proj_resid": 2.0 * T * I * D,
+    }
+    kbytes = {
+        "gate_score": w.T_in * D * elt + 4.0 * w.T_in + H1 * D * elt,
+        "topk_select": 5.0 * w.T_in + 4.0 * T,
+        "compact": 4.0 * T + 2.0 * T * D * elt + 4.0 * T + 8.0 * T,
+        "rmsnorm_attn": 2.0 * T * D * elt,
+        "rmsnorm_ffn": 2.0 * T * D * elt,
+        "rope_table": 4.0 * T + 4.0 * T * d,
+    }
+    kern = {}
+    if use_ev:
+        acc = {}
+        for i in range(args.steps):
+            base = 2 + i * per_step
+            for name, a in (("gate_score", 0), ("topk_select", 1), ("compact", 2)):
+                acc.setdefault(name, []).append(ev.ms(base + a, base + a + 1))
+            for l in range(L):
+                lb = base + 4 + l * (tg.LAYER_STAGES + 1)
+                for j, name in enumerate(tg.LAYER_STAGE_NAMES):
+                    acc.setdefault(name, []).append(ev.ms(lb + j, lb + j + 1))
+        for name, v in acc.items():
+            avg_ms = float(np.mean(v))
+            per_step_ms = float(np.sum(v)) / args.steps
+            e = {"avg_us": round(avg_ms * 1e3, 2), "launches_per_step": len(v) // args.steps,
+                 "ms_per_step": round(per_step_ms, 4)}
+            if name in kflop:
+                tf = kflop[name] / (avg_ms * 1e-3) / 1e12
+                e["tflops"] = round(tf, 1)
+                e["frac_mfma_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            if name in kbytes:
+                gbs = kbytes[name] / (avg_ms * 1e-3) / 1e9
+                e["gbs"] = round(gbs, 1)
+                e["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+            kern[name] = e
+    ev.close()
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dm.dtype,
+        "data": "synthetic (seeded; no datasets or trained weights)",
+        "config": {
+            "workload": "%s: gated prefill, batch %d, N=%s, K=%s, %d unprunable tail tokens/seq, "
+                        "%d upper layers, D=%d Hq=%d Hkv=%d d=%d I=%d, scorer %d->%d->1"
+                        % (w.name, w.B, "/".join(map(str, w.N[:2])) + ("..." if w.B > 2 else ""),
+                           "/".join(map(str, w.K[:2])) + ("..." if w.B > 2 else ""), w.F, L,
+                           D, Hq, Hkv, d, I, D, H1),
+            "batch": w.B, "n_prompt_tokens": w.T_in, "n_kept_tokens": T, "upper_layers": L,
+        },
+        "host_wall_s_timed": round(t_host1 - t_host0, 3),
+        "peak_device_mem_gb": round(peak_mem / 1e9, 3),
+    }
+    if use_ev:
+        a = kern["gated_attn"]
+        out["attn_tflops"] = a["tflops"]
+        out["attn_frac_mfma_peak"] = a["frac_mfma_peak"]
+        sc_us = kern["topk_select"]["avg_us"] + kern["compact"]["avg_us"]
+        sc_bytes = kbytes["topk_select"] + kbytes["compact"]
+        out["select_compact"] = {"us": round(sc_us, 2), "bytes": sc_bytes,
+                                 "gbs": round(sc_bytes / (sc_us * 1e-6) / 1e9, 1),
+                                 "frac_hbm": round(sc_bytes / (sc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        dom = max(kern, key=lambda n: kern[n]["ms_per_step"])
+        de = kern[dom]
+        if dom in kflop:
+            out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": de["tflops"],
+                               "peak": PEAK_BF16_TFLOPS if dm.dtype == "bf16" else PEAK_F32_TFLOPS,
+                               "unit": "TFLOP/s", "frac": de["frac_mfma_peak"], "traffic": None,
+                               "work_per_launch": kflop[dom]}
+        else:
+            out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": de["gbs"],
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": de["frac_hbm"],
+                               "traffic": None, "work_per_launch": kbytes[dom]}
+        out["kernels"] = kern
+    if want_cpu:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        from learned_token_pruning_post_amd.workloads import gate_inputs, layer_weights
+        del gp, dw
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, gate_inputs(w), layer_weights(w, 0))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

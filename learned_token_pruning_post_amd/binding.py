@@ -1,0 +1,241 @@
+"""ctypes binding of libtokengate.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers and the current HIP stream to the C ABI declared in
+include/tokengate.h, and raises TokenGateError on a non-zero status. No step
+of the computation happens here, and there is no fallback: if the library is
+missing this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtokengate.so")
+
+TG_F32 = 0
+TG_BF16 = 1
+DEV_FORCED_GT_BUDGET = 1
+DEV_BUDGET_GT_LEN = 2
+DEV_NAN_SCORE = 4
+
+# every entry point declared in include/tokengate.h
+ABI_FUNCTIONS = (
+    "tg_status_string", "tg_abi_version",
+    "tg_gate_score_workspace_size", "tg_gate_score",
+    "tg_topk_select_workspace_size", "tg_topk_select",
+    "tg_compact",
+    "tg_gated_attn_workspace_size", "tg_gated_attn_fwd",
+    "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
+    "tg_upper_layer_fwd_timed",
+)
+LAYER_STAGES = 8
+LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
+                     "rmsnorm_ffn", "gate_up_swiglu", "down_proj_resid")
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd", "t", "g")]
+
+
+class LayerDims(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+                ("d", ctypes.c_int), ("I", ctypes.c_int), ("rope_base", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+class LayerWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("norm", "q", "attn", "x1", "act", "rope", "total")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtokengate.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtokengate.so not built (%s); run "
+                           "learned_token_pruning_post_amd/build.py" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.tg_status_string.argtypes = [i32]
+    L.tg_status_string.restype = ctypes.c_char_p
+    L.tg_abi_version.argtypes = []
+    L.tg_abi_version.restype = i32
+    L.tg_gate_score_workspace_size.argtypes = [i64, i32, i32, i32]
+    L.tg_gate_score_workspace_size.restype = sz
+    L.tg_gate_score.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    L.tg_gate_score.restype = i32
+    L.tg_topk_select_workspace_size.argtypes = [i32, i64, i32]
+    L.tg_topk_select_workspace_size.restype = sz
+    L.tg_topk_select.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp, sz, vp]
+    L.tg_topk_select.restype = i32
+    L.tg_compact.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp, vp, vp]
+    L.tg_compact.restype = i32
+    L.tg_gated_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.tg_gated_attn_workspace_size.restype = sz
+    L.tg_gated_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                    vp, vp, vp, sz, vp]
+    L.tg_gated_attn_fwd.restype = i32
+    L.tg_upper_layer_ws_layout.argtypes = [ctypes.POINTER(LayerDims), i64, ctypes.POINTER(LayerWsLayout)]
+    L.tg_upper_layer_ws_layout.restype = i32
+    L.tg_upper_layer_workspace_size.argtypes = [ctypes.POINTER(LayerDims), i64, i32, i32]
+    L.tg_upper_layer_workspace_size.restype = sz
+    L.tg_upper_layer_fwd.argtypes = [ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerDims),
+                                     vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, sz, vp]
+    L.tg_upper_layer_fwd.restype = i32
+    L.tg_upper_layer_fwd_timed.argtypes = L.tg_upper_layer_fwd.argtypes + [vp]
+    L.tg_upper_layer_fwd_timed.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(s: int) -> str:
+    return lib().tg_status_string(int(s)).decode()
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise TokenGateError(st, what)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return TG_BF16
+    if dt == torch.float32:
+        return TG_F32
+    raise ValueError("unsupported dtype %s" % dt)
+
+
+def _empty_ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def gate_score(h, W1, b1, w2, b2, s_out=None, ws=None):
+    T_in, D = h.shape
+    H1 = W1.shape[0]
+    dt = dtype_code(h.dtype)
+    if s_out is None:
+        s_out = torch.empty(T_in, dtype=torch.float32, device=h.device)
+    need = lib().tg_gate_score_workspace_size(T_in, D, H1, dt)
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(need, h.device)
+    _check(lib().tg_gate_score(_p(h), T_in, D, H1, _p(W1), _p(b1), _p(w2), _p(b2), dt,
+                               _p(s_out), _p(ws), ws.numel(), _stream()), "tg_gate_score")
+    return s_out
+
+
+def topk_select(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, kept=None, status=None):
+    B = cu_in.numel() - 1
+    if kept is None:
+        kept = torch.empty(max(T, 0), dtype=torch.int32, device=s.device)
+    if status is None:
+        status = torch.empty(max(B, 1), dtype=torch.int32, device=s.device)
+    _check(lib().tg_topk_select(_p(s), _p(keep_mask), _p(cu_in), _p(cu_kept), B, s.numel(), T,
+                                max_n, _p(kept), _p(status), None, 0, _stream()),
+           "tg_topk_select")
+    return kept, status
+
+
+def compact(h, pos, s, kept, cu_in, cu_kept, h_out=None, pos_out=None, s_out=None):
+    T = kept.numel()
+    D = h.shape[1]
+    B = cu_kept.numel() - 1
+    if h_out is None:
+        h_out = torch.empty((T, D), dtype=h.dtype, device=h.device)
+    if pos_out is None:
+        pos_out = torch.empty(T, dtype=torch.int32, device=h.device)
+    if s_out is None:
+        s_out = torch.empty(T, dtype=torch.float32, device=h.device)
+    _check(lib().tg_compact(_p(h), _p(pos), _p(s), _p(kept), _p(cu_in), _p(cu_kept), B, T, D,
+                            dtype_code(h.dtype), _p(h_out), _p(pos_out), _p(s_out), _stream()),
+           "tg_compact")
+    return h_out, pos_out, s_out
+
+
+def gated_attn_fwd(q, k, v, s_c, t, g, cu_kept, max_k: int, o=None, lse=None, want_lse=False):
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    B = cu_kept.numel() - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _check(lib().tg_gated_attn_fwd(_p(q), _p(k), _p(v), _p(s_c), _p(t), _p(g), _p(cu_kept), B,
+                                   max_k, Hq, Hkv, d, dtype_code(q.dtype), _p(o), _p(lse), None, 0,
+                                   _stream()), "tg_gated_attn_fwd")
+    return o, lse
+
+
+def layer_dims(D, Hq, Hkv, d, I, dtype: torch.dtype, rope_base=1.0e6, rms_eps=1.0e-6) -> LayerDims:
+    return LayerDims(D, Hq, Hkv, d, I, rope_base, rms_eps, dtype_code(dtype))
+
+
+def upper_layer_ws_layout(dims: LayerDims, T: int) -> LayerWsLayout:
+    out = LayerWsLayout()
+    _check(lib().tg_upper_layer_ws_layout(ctypes.byref(dims), T, ctypes.byref(out)),
+           "tg_upper_layer_ws_layout")
+    return out
+
+
+class UpperLayerWeights:
+    """Device weights of one upper layer (keys as in tg_layer_weights)."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor]):
+        self.tensors = tensors
+        self.c = LayerWeights(*[_p(tensors[n]) for n, _ in LayerWeights._fields_])
+
+
+def upper_layer_fwd(w: UpperLayerWeights, dims: LayerDims, x_in, pos_c, s_c, cu_kept, max_k: int,
+                    x_out=None, kcache=None, vcache=None, ws=None, events=None):
+    """One upper layer. ``events``: optional ctypes array of LAYER_STAGES + 1
+    hipEvent_t handles; when given, the instrumented entry point records them
+    between the layer's stages."""
+    T = x_in.shape[0]
+    B = cu_kept.numel() - 1
+    dev = x_in.device
+    if x_out is None:
+        x_out = torch.empty_like(x_in)
+    if kcache is None:
+        kcache = torch.empty((T, dims.Hkv, dims.d), dtype=x_in.dtype, device=dev)
+    if vcache is None:
+        vcache = torch.empty((T, dims.Hkv, dims.d), dtype=x_in.dtype, device=dev)
+    need = lib().tg_upper_layer_workspace_size(ctypes.byref(dims), T, B, max_k)
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(need, dev)
+    args = (ctypes.byref(w.c), ctypes.byref(dims), _p(x_in), _p(x_out), _p(pos_c), _p(s_c),
+            _p(cu_kept), B, T, max_k, _p(kcache), _p(vcache), _p(ws), ws.numel(), _stream())
+    if events is None:
+        _check(lib().tg_upper_layer_fwd(*args), "tg_upper_layer_fwd")
+    else:
+        _check(lib().tg_upper_layer_fwd_timed(*args, events), "tg_upper_layer_fwd_timed")
+    return x_out, kcache, vcache, ws

@@ -1,0 +1,55 @@
+// Shared device helpers for the gfx950 kernels of libtokengate.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define TG_LOG2E 1.4426950408889634f
+#define TG_LN2 0.6931471805599453f
+
+namespace tg {
+
+__device__ __forceinline__ float bf2f(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ bf16 f2bf(float x) { return static_cast<bf16>(x); }  // RNE
+
+// 32x32x16 bf16 MFMA, fp32 accumulate (gfx950). Lane l supplies row (l % 32)
+// of A and column (l % 32) of B for the k-slots owned by lane group l / 32;
+// A and B use the same k-slot order, so any fixed k permutation cancels.
+// Result: lane l holds column l % 32, rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = static_cast<bf16>(0.0f);
+  return z;
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+}  // namespace tg

@@ -1,0 +1,63 @@
+// Internal launchers of libtokengate (host side). Every launcher enqueues on
+// `stream`, assumes validated arguments, and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "tg_common.hpp"
+
+namespace tg {
+
+hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
+                              const int32_t* cu_kept, int B, int32_t* kept, int32_t* status,
+                              hipStream_t stream);
+
+hipError_t launch_compact(const void* h, const int32_t* pos, const float* s, const int32_t* kept,
+                          const int32_t* cu_in, const int32_t* cu_kept, int B, int64_t T,
+                          size_t row_bytes, void* h_out, int32_t* pos_out, float* s_out,
+                          hipStream_t stream);
+
+// RMSNorm rows: y = x * rsqrt(mean(x^2) + eps) * w  (is_bf16 selects the storage type)
+hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int D, float eps,
+                          bool is_bf16, hipStream_t stream);
+
+// cos/sin table [T, d] fp32: [.., i] = cos(pos*base^(-2i/d)), [.., d/2 + i] = sin(..)
+hipError_t launch_rope_table(const int32_t* pos, int64_t T, int d, float base, float* table,
+                             hipStream_t stream);
+
+// ---- bf16 MFMA GEMMs: out = f(W x) with W rows as output features ----
+struct QkvOut {
+  bf16* q;        // [M, Hq*d]
+  bf16* kc;       // [M, Hkv*d]
+  bf16* vc;       // [M, Hkv*d]
+  const float* rope;  // [M, d]
+  int Hq, Hkv, d;
+};
+
+hipError_t gemm_bf16_plain(const bf16* X, const bf16* W, const bf16* resid, bf16* out, int M,
+                           int N, int K, hipStream_t stream);
+hipError_t gemm_bf16_qkv(const bf16* X, const bf16* wq, const bf16* wk, const bf16* wv,
+                         const QkvOut& o, int M, int K, hipStream_t stream);
+hipError_t gemm_bf16_swiglu(const bf16* X, const bf16* wg, const bf16* wu, bf16* act, int M,
+                            int I, int K, hipStream_t stream);
+// scorer; partial [nblk, M] fp32 scratch needed when H1 > 256 (nblk = ceil(H1/256))
+hipError_t gemm_bf16_score(const bf16* X, const bf16* W1, const bf16* b1, const bf16* w2,
+                           const bf16* b2, float* s_out, float* partial, int M, int H1, int K,
+                           hipStream_t stream);
+size_t gemm_bf16_score_ws(int64_t M, int H1);
+
+// ---- fp32 SIMT path ----
+hipError_t gemm_f32(const float* X, const float* W, const float* resid, float* out, int M, int N,
+                    int K, int ldo, hipStream_t stream);
+hipError_t score_epilogue_f32(const float* z, const float* b1, const float* w2, const float* b2,
+                              float* s_out, int64_t M, int H1, hipStream_t stream);
+hipError_t qkv_split_rope_f32(const float* qkv, const float* rope, float* q, float* kc, float* vc,
+                              int64_t M, int Hq, int Hkv, int d, hipStream_t stream);
+hipError_t swiglu_f32(const float* gate, const float* up, float* act, int64_t n,
+                      hipStream_t stream);
+
+// ---- attention ----
+hipError_t attn_fwd(const void* q, const void* k, const void* v, const float* s_c, const float* t,
+                    const float* g, const int32_t* cu_kept, int B, int max_k, int Hq, int Hkv,
+                    int d, bool is_bf16, void* o, float* lse, hipStream_t stream);
+
+}  // namespace tg

@@ -1,0 +1,113 @@
+"""The gated prefill above layer L's attention, driven through the C ABI.
+
+Uploads a seeded workload to the GPU once, allocates every buffer once, and
+runs scorer -> Top-K select -> compaction -> the stack of upper layers
+(three-stage forward: Tencent Cloud TokenGate article, early token filtering;
+farwalk.ai summary, the method). All compute happens in libtokengate.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import binding as tg
+from .workloads import Workload, gate_inputs, layer_weights, Tensor
+
+
+def to_device(t: Tensor, device="cuda") -> torch.Tensor:
+    if t.bits is not None:
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(t.value)).to(device)
+
+
+def torch_dtype(w: Workload) -> torch.dtype:
+    return torch.bfloat16 if w.dims.dtype == "bf16" else torch.float32
+
+
+class DeviceWorkload:
+    """Seeded inputs and weights of a workload, resident in HBM."""
+
+    def __init__(self, w: Workload, n_layers: Optional[int] = None, device="cuda", keep_host=False):
+        self.w = w
+        self.device = device
+        gi = gate_inputs(w)
+        self.host_gate = gi if keep_host else None
+        self.h = to_device(gi.h, device)
+        self.W1 = to_device(gi.W1, device)
+        self.b1 = to_device(gi.b1, device)
+        self.w2 = to_device(gi.w2, device)
+        self.b2 = to_device(gi.b2, device)
+        self.keep_mask = torch.from_numpy(gi.keep_mask).to(device)
+        self.cu_in = torch.from_numpy(gi.cu_in).to(device)
+        self.cu_kept = torch.from_numpy(gi.cu_kept).to(device)
+        L = w.layers if n_layers is None else n_layers
+        self.layers: List[tg.UpperLayerWeights] = []
+        self.host_layers = [] if keep_host else None
+        with cf.ThreadPoolExecutor(4) as ex:
+            for lw in ex.map(lambda l: layer_weights(w, l), range(L)):
+                if keep_host:
+                    self.host_layers.append(lw)
+                tens = {
+                    "attn_norm": to_device(lw.attn_norm, device), "wq": to_device(lw.wq, device),
+                    "wk": to_device(lw.wk, device), "wv": to_device(lw.wv, device),
+                    "wo": to_device(lw.wo, device), "ffn_norm": to_device(lw.ffn_norm, device),
+                    "wg": to_device(lw.wg, device), "wu": to_device(lw.wu, device),
+                    "wd": to_device(lw.wd, device),
+                    "t": torch.from_numpy(lw.t).to(device), "g": torch.from_numpy(lw.g).to(device),
+                }
+                self.layers.append(tg.UpperLayerWeights(tens))
+        dm = w.dims
+        self.dims = tg.layer_dims(dm.D, dm.Hq, dm.Hkv, dm.d, dm.I, torch_dtype(w), dm.rope_base, dm.rms_eps)
+
+
+class GatedPrefill:
+    """Preallocated buffers plus one call per step of the path."""
+
+    def __init__(self, dw: DeviceWorkload):
+        self.dw = dw
+        w, dev = dw.w, dw.device
+        dt = torch_dtype(w)
+        T, T_in, D = w.T, w.T_in, w.dims.D
+        self.s = torch.empty(T_in, dtype=torch.float32, device=dev)
+        self.kept = torch.empty(T, dtype=torch.int32, device=dev)
+        self.status = torch.empty(w.B, dtype=torch.int32, device=dev)
+        self.x = torch.empty((T, D), dtype=dt, device=dev)
+        self.pos_c = torch.empty(T, dtype=torch.int32, device=dev)
+        self.s_c = torch.empty(T, dtype=torch.float32, device=dev)
+        n = len(dw.layers)
+        self.kcache = torch.empty((max(n, 1), T, w.dims.Hkv, w.dims.d), dtype=dt, device=dev)
+        self.vcache = torch.empty_like(self.kcache)
+        lib = tg.lib()
+        need = lib.tg_upper_layer_workspace_size(tg.ctypes.byref(dw.dims), T, w.B, w.max_k)
+        need = max(need, lib.tg_gate_score_workspace_size(T_in, D, w.dims.H1, tg.dtype_code(dt)))
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def score(self):
+        d = self.dw
+        tg.gate_score(d.h, d.W1, d.b1, d.w2, d.b2, s_out=self.s, ws=self.ws)
+
+    def select(self):
+        d = self.dw
+        tg.topk_select(self.s, d.keep_mask, d.cu_in, d.cu_kept, d.w.T, d.w.max_n,
+                       kept=self.kept, status=self.status)
+
+    def compact(self):
+        d = self.dw
+        tg.compact(d.h, None, self.s, self.kept, d.cu_in, d.cu_kept,
+                   h_out=self.x, pos_out=self.pos_c, s_out=self.s_c)
+
+    def layer(self, l: int):
+        d = self.dw
+        tg.upper_layer_fwd(d.layers[l], d.dims, self.x, self.pos_c, self.s_c, d.cu_kept, d.w.max_k,
+                           x_out=self.x, kcache=self.kcache[l], vcache=self.vcache[l], ws=self.ws)
+
+    def run(self):
+        self.score()
+        self.select()
+        self.compact()
+        for l in range(len(self.dw.layers)):
+            self.layer(l)
+        return self.x

@@ -7,4 +7,5 @@ from .tokengate_oracle import *  # noqa: F401,F403
 from .tokengate_oracle import (FORCED_GT_BUDGET, BUDGET_GT_LEN, NAN_SCORE,  # noqa: F401
                                gelu, sigmoid, gate_score, select_one, topk_select,
                                compact, rmsnorm, rope, gated_attention, silu,
+                               qkv_rope, o_proj, swiglu_act, down_proj,
                                upper_layer, gated_prefill)

@@ -270,6 +270,40 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
+def qkv_rope(x, pos_c, W: Dict[str, np.ndarray], dims, rows=None):
+    """Pre-attention half of an upper layer: n1 = RMSNorm(x) * attn_norm;
+    q, k, v = n1 Wq^T, n1 Wk^T, n1 Wv^T; RoPE on q and k at pos_c.
+    Returns (n1, q [T,Hq,d], k [T,Hkv,d], v [T,Hkv,d]); with ``rows`` q is
+    filled only there (k and v always for every token)."""
+    x = _f64(x)
+    T = x.shape[0]
+    Hq, Hkv, d = dims.Hq, dims.Hkv, dims.d
+    n1 = rmsnorm(x, W["attn_norm"], dims.rms_eps)
+    k = rope((n1 @ _f64(W["wk"]).T).reshape(T, Hkv, d), pos_c, dims.rope_base)
+    v = (n1 @ _f64(W["wv"]).T).reshape(T, Hkv, d)
+    sel = np.arange(T) if rows is None else np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    q = np.zeros((T, Hq, d))
+    q[sel] = rope((n1[sel] @ _f64(W["wq"]).T).reshape(-1, Hq, d), _f64(pos_c)[sel], dims.rope_base)
+    return n1, q, k, v
+
+
+def o_proj(x, o, Wo):
+    """Attention output projection with the residual: x1 = x + o_flat Wo^T."""
+    o = _f64(o)
+    return _f64(x) + o.reshape(o.shape[0], -1) @ _f64(Wo).T
+
+
+def swiglu_act(x1, W: Dict[str, np.ndarray], eps: float):
+    """n2 = RMSNorm(x1) * ffn_norm; act = silu(n2 Wg^T) * (n2 Wu^T). Returns (n2, act)."""
+    n2 = rmsnorm(x1, W["ffn_norm"], eps)
+    return n2, silu(n2 @ _f64(W["wg"]).T) * (n2 @ _f64(W["wu"]).T)
+
+
+def down_proj(x1, act, Wd):
+    """FFN down projection with the residual: x2 = x1 + act Wd^T."""
+    return _f64(x1) + _f64(act) @ _f64(Wd).T
+
+
 def upper_layer(x, pos_c, s_c, W: Dict[str, np.ndarray], dims, cu_kept,
                 rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """One decoder layer above the gate, run on the kept tokens only.
@@ -285,31 +319,19 @@ def upper_layer(x, pos_c, s_c, W: Dict[str, np.ndarray], dims, cu_kept,
     """
     x = _f64(x)
     T = x.shape[0]
-    Hq, Hkv, d = dims.Hq, dims.Hkv, dims.d
-    eps, base = dims.rms_eps, dims.rope_base
-    n1 = rmsnorm(x, W["attn_norm"], eps)
-    k = (n1 @ _f64(W["wk"]).T).reshape(T, Hkv, d)
-    v = (n1 @ _f64(W["wv"]).T).reshape(T, Hkv, d)
-    k = rope(k, pos_c, base)
-    if rows is None:
-        sel = np.arange(T)
-    else:
-        sel = np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
-    q = np.zeros((T, Hq, d))
-    q[sel] = rope((n1[sel] @ _f64(W["wq"]).T).reshape(-1, Hq, d), _f64(pos_c)[sel], base)
+    n1, q, k, v = qkv_rope(x, pos_c, W, dims, rows)
+    sel = np.arange(T) if rows is None else np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
     o, lse = gated_attention(q, k, v, s_c, W["t"], W["g"], cu_kept,
                              rows=None if rows is None else sel)
-    out = {"n1": n1, "q": q, "k": k, "v": v, "o": o, "lse": lse, "rows": sel}
     x1 = np.zeros_like(x)
-    x1[sel] = x[sel] + o[sel].reshape(-1, Hq * d) @ _f64(W["wo"]).T
+    x1[sel] = o_proj(x[sel], o[sel], W["wo"])
     n2 = np.zeros_like(x)
-    n2[sel] = rmsnorm(x1[sel], W["ffn_norm"], eps)
     act = np.zeros((T, _f64(W["wg"]).shape[0]))
-    act[sel] = silu(n2[sel] @ _f64(W["wg"]).T) * (n2[sel] @ _f64(W["wu"]).T)
+    n2[sel], act[sel] = swiglu_act(x1[sel], W, dims.rms_eps)
     x2 = np.zeros_like(x)
-    x2[sel] = x1[sel] + act[sel] @ _f64(W["wd"]).T
-    out.update({"x1": x1, "n2": n2, "act": act, "x2": x2})
-    return out
+    x2[sel] = down_proj(x1[sel], act[sel], W["wd"])
+    return {"n1": n1, "q": q, "k": k, "v": v, "o": o, "lse": lse, "rows": sel,
+            "x1": x1, "n2": n2, "act": act, "x2": x2}
 
 
 # ----------------------------------------------------------------------------

@@ -1,0 +1,290 @@
+"""GPU parity: every step of the HIP path against the fp64 CPU oracle.
+
+Per-stage comparison on identical inputs: each oracle stage is fed the GPU's
+output of the stage before it. Selection, compaction and positions must match
+bit for bit; scores, attention and layer outputs fall within atol 2e-2 /
+rtol 1e-2 (bf16 storage, fp32 accumulation) or 1e-4 / 1e-4 (fp32).
+Full-size workloads run in the same launch configuration as the benchmark
+(the GatedPrefill driver) and compare sampled rows where the oracle cannot do
+all of them in seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from helpers import TOL, assert_close, bits, f64, layer_dict, sample_rows, say, ws_view
+from learned_token_pruning_post_amd import binding as tg
+from learned_token_pruning_post_amd.pipeline import DeviceWorkload, GatedPrefill, to_device
+from learned_token_pruning_post_amd.workloads import (ModelDims, activations, custom,
+                                                      scores_with_ties, workload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    tg.lib()  # raises loudly if the HIP library is missing
+
+
+def _stage_parity(w, score_rows=None, layer_rows_per_seq=None, seed=0):
+    dt = w.dims.dtype
+    say("workload", w.name, "N", w.N[:3], "K", w.K[:3], "T", w.T)
+    dw = DeviceWorkload(w, n_layers=1, keep_host=True)
+    gi = dw.host_gate
+    gp = GatedPrefill(dw)
+
+    # ---- scorer ----
+    gp.score()
+    torch.cuda.synchronize()
+    s = gp.s.cpu().numpy()
+    rows = np.arange(w.T_in) if score_rows is None else \
+        np.unique(np.concatenate([np.random.default_rng(seed).choice(w.T_in, score_rows, replace=False),
+                                  [0, w.T_in - 1]]))
+    ref = O.gate_score(gi.h.value[rows], gi.W1.value, gi.b1.value, gi.w2.value, gi.b2.value)
+    e = assert_close(s[rows], ref, dt, "scores")
+    say("  scorer max err", e)
+
+    # ---- select: bit exact on the same fp32 scores ----
+    gp.select()
+    torch.cuda.synchronize()
+    kept = gp.kept.cpu().numpy()
+    ref_kept, flags = O.topk_select(s, gi.keep_mask, gi.cu_in, gi.cu_kept)
+    assert np.array_equal(gp.status.cpu().numpy(), flags.astype(np.int32))
+    assert np.array_equal(kept, ref_kept.astype(np.int32))
+    say("  select bit-exact", len(kept))
+
+    # ---- compact: bit exact ----
+    gp.compact()
+    torch.cuda.synchronize()
+    hc_ref, pc_ref, sc_ref = O.compact(gi.h.device_array, None, s, ref_kept, gi.cu_in, gi.cu_kept)
+    assert np.array_equal(bits(gp.x), np.ascontiguousarray(hc_ref).view(bits(gp.x).dtype))
+    assert np.array_equal(gp.pos_c.cpu().numpy(), pc_ref.astype(np.int32))
+    assert np.array_equal(gp.s_c.cpu().numpy().view(np.int32), sc_ref.astype(np.float32).view(np.int32))
+    say("  compact bit-exact")
+
+    # ---- one upper layer, stage by stage ----
+    x_in = f64(gp.x)
+    pos_c = gp.pos_c.cpu().numpy()
+    s_c = gp.s_c.cpu().numpy().astype(np.float64)
+    gp.layer(0)
+    torch.cuda.synchronize()
+    W = layer_dict(dw.host_layers[0])
+    dm = w.dims
+    lay = tg.upper_layer_ws_layout(dw.dims, w.T)
+    tdt = gp.x.dtype
+    T = w.T
+    q_g = f64(ws_view(gp.ws, lay.q, (T, dm.Hq, dm.d), tdt))
+    a_g = f64(ws_view(gp.ws, lay.attn, (T, dm.Hq, dm.d), tdt))
+    x1_g = f64(ws_view(gp.ws, lay.x1, (T, dm.D), tdt))
+    act_g = f64(ws_view(gp.ws, lay.act, (T, dm.I), tdt))
+    k_g, v_g = f64(gp.kcache[0]), f64(gp.vcache[0])
+    x2_g = f64(gp.x)
+    cu = gi.cu_kept
+    lrows = np.arange(T) if layer_rows_per_seq is None else sample_rows(cu, layer_rows_per_seq, seed)
+    n1, q_r, k_r, v_r = O.qkv_rope(x_in, pos_c, W, dm, rows=lrows)
+    errs = {}
+    errs["k"] = assert_close(k_g[lrows], k_r[lrows], dt, "k cache")
+    errs["v"] = assert_close(v_g[lrows], v_r[lrows], dt, "v cache")
+    errs["q"] = assert_close(q_g[lrows], q_r[lrows], dt, "q")
+    o_r, _ = O.gated_attention(q_g, k_g, v_g, s_c, W["t"], W["g"], cu, rows=lrows)
+    errs["attn"] = assert_close(a_g[lrows], o_r[lrows], dt, "attention")
+    errs["x1"] = assert_close(x1_g[lrows], O.o_proj(x_in[lrows], a_g[lrows], W["wo"]), dt, "x1")
+    _, act_r = O.swiglu_act(x1_g[lrows], W, dm.rms_eps)
+    errs["act"] = assert_close(act_g[lrows], act_r, dt, "swiglu act")
+    errs["x2"] = assert_close(x2_g[lrows], O.down_proj(x1_g[lrows], act_g[lrows], W["wd"]), dt, "x out")
+    say("  layer stage max errs", {k: "%.3g" % v for k, v in errs.items()})
+
+
+def test_stages_tiny_fp32():
+    _stage_parity(workload("tiny"))
+
+
+def test_stages_qwen8k():
+    _stage_parity(workload("qwen8k"))
+
+
+@pytest.mark.parametrize("k", [4096, 512, 2048, 8192])
+def test_stages_qwen32k(k):
+    _stage_parity(workload("qwen32k", k=k, layers=1), score_rows=8192,
+                  layer_rows_per_seq=None if k <= 2048 else 384)
+
+
+@pytest.mark.parametrize("n", [65536, 131072])
+def test_stages_long(n):
+    _stage_parity(workload("long", n=n), score_rows=8192, layer_rows_per_seq=384)
+
+
+def test_stages_multibudget():
+    _stage_parity(workload("multibudget"), score_rows=8192, layer_rows_per_seq=96)
+
+
+def test_stages_ragged_small_bf16():
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=96, dtype="bf16")
+    w = custom(21, N=[300, 1, 77, 1000], K=[150, 1, 77, 333], F=1, dims=dims)
+    _stage_parity(w)
+
+
+def test_stages_ragged_gqa4_fp32_d128():
+    dims = ModelDims(D=256, Hq=8, Hkv=2, d=128, I=384, H1=40, dtype="f32")
+    w = custom(22, N=[129, 64, 200], K=[65, 64, 3], F=3, dims=dims)
+    _stage_parity(w)
+
+
+def test_scorer_wide_hidden_uses_partials():
+    dims = ModelDims(D=128, Hq=2, Hkv=1, d=64, I=128, H1=600, dtype="bf16")
+    w = custom(23, N=[777], K=[10], F=2, dims=dims)
+    dw = DeviceWorkload(w, n_layers=0, keep_host=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    torch.cuda.synchronize()
+    gi = dw.host_gate
+    ref = O.gate_score(gi.h.value, gi.W1.value, gi.b1.value, gi.w2.value, gi.b2.value)
+    assert_close(gp.s.cpu().numpy(), ref, "bf16", "scores H1=600")
+
+
+# ---------------------------------------------------------------------------
+# selection edge cases
+# ---------------------------------------------------------------------------
+
+def _select_case(N, K, mask, s):
+    dev = "cuda"
+    cu_in = np.concatenate([[0], np.cumsum(N)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
+    st = torch.from_numpy(s.astype(np.float32)).to(dev)
+    mt = torch.from_numpy(mask.astype(np.uint8)).to(dev)
+    kept, status = tg.topk_select(st, mt, torch.from_numpy(cu_in).to(dev), torch.from_numpy(cu_k).to(dev),
+                                  int(cu_k[-1]), int(max(N) if len(N) else 0))
+    torch.cuda.synchronize()
+    return kept.cpu().numpy(), status.cpu().numpy()[:len(N)], cu_in, cu_k
+
+
+def test_select_ties_specials_ragged():
+    rng = np.random.default_rng(31)
+    N = [1, 7, 1000, 5000, 40000, 3, 2049, 150000]
+    K = [1, 3, 100, 5000, 4096, 0, 2049, 1]
+    T_in = sum(N)
+    s = scores_with_ties(31, T_in, 37)
+    special = rng.choice(T_in, 4000, replace=False)
+    s[special[:1000]] = np.nan
+    s[special[1000:2000]] = -0.0
+    s[special[2000:3000]] = 0.0
+    s[special[3000:3500]] = np.inf
+    s[special[3500:]] = -np.inf
+    mask = np.zeros(T_in, np.uint8)
+    cu = np.concatenate([[0], np.cumsum(N)])
+    for b in range(len(N)):
+        nf = min(K[b], max(0, N[b] // 50))
+        if nf:
+            mask[cu[b] + rng.choice(N[b], nf, replace=False)] = 1
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, flags = O.topk_select(s.astype(np.float32), mask, cu_in, cu_k)
+    assert np.array_equal(status, flags.astype(np.int32))
+    assert np.array_equal(kept, ref.astype(np.int32))
+    # determinism
+    kept2, _, _, _ = _select_case(N, K, mask, s)
+    assert np.array_equal(kept, kept2)
+
+
+def test_select_all_equal_and_budget_extremes():
+    N = [4096, 4096, 4096, 5000]
+    K = [100, 4096, 512, 4999]
+    s = np.full(sum(N), 0.5, np.float32)
+    s[4096 * 3:] = np.linspace(0, 1, 5000, dtype=np.float32)
+    mask = np.zeros(sum(N), np.uint8)
+    mask[4096 * 2 + 4096 - 512:4096 * 3] = 1   # K = F: exactly the forced tail
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, flags = O.topk_select(s, mask, cu_in, cu_k)
+    assert np.array_equal(kept, ref.astype(np.int32)) and not status.any()
+
+
+def test_select_error_flags():
+    N = [10, 10, 10]
+    K = [3, 11, 4]  # seq 0: 5 forced > 3; seq 1: K > N
+    s = np.linspace(0, 1, 30, dtype=np.float32)
+    mask = np.zeros(30, np.uint8)
+    mask[:5] = 1
+    kept, status, _, cu_k = _select_case([10, 10, 10], K, mask, s)
+    assert status.tolist() == [1, 2, 0]
+    assert (kept[:3] == -1).all() and (kept[3:14] == -1).all()
+    ref, _ = O.select_one(s[20:30], mask[20:30].astype(bool), 4)
+    assert kept[14:].tolist() == (ref + 20).tolist()
+
+
+# ---------------------------------------------------------------------------
+# compaction with explicit positions, odd row sizes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 6), ("bf16", 2048), ("f32", 100), ("f32", 3)])
+def test_compact_positions_and_row_sizes(dtype, D):
+    rng = np.random.default_rng(41)
+    N = [50, 1, 300]
+    K = [10, 1, 299]
+    T_in = sum(N)
+    h = activations(41, 7, (T_in, D), dtype)
+    ht = to_device(h)
+    pos = np.concatenate([np.sort(rng.choice(10 ** 6, n, replace=False)) for n in N]).astype(np.int32)
+    s = rng.random(T_in).astype(np.float32)
+    cu_in = np.concatenate([[0], np.cumsum(N)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
+    ref_kept, _ = O.topk_select(s, None, cu_in, cu_k)
+    dev = "cuda"
+    kept_t = torch.from_numpy(ref_kept.astype(np.int32)).to(dev)
+    hc, pc, sc = tg.compact(ht, torch.from_numpy(pos).to(dev), torch.from_numpy(s).to(dev), kept_t,
+                            torch.from_numpy(cu_in).to(dev), torch.from_numpy(cu_k).to(dev))
+    torch.cuda.synchronize()
+    hr, pr, sr = O.compact(h.device_array, pos, s, ref_kept, cu_in, cu_k)
+    assert np.array_equal(bits(hc), np.ascontiguousarray(hr).view(bits(hc).dtype))
+    assert np.array_equal(pc.cpu().numpy(), pr.astype(np.int32))
+    assert np.array_equal(sc.cpu().numpy(), sr)
+
+
+# ---------------------------------------------------------------------------
+# attention kernels on their own
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,G,d", [("bf16", 1, 64), ("bf16", 2, 64), ("bf16", 4, 64),
+                                       ("bf16", 1, 128), ("bf16", 2, 128), ("bf16", 4, 128),
+                                       ("f32", 2, 64), ("f32", 2, 128), ("f32", 4, 128)])
+def test_attention_varlen(dtype, G, d):
+    lens = [1, 31, 64, 65, 200, 129, 0, 3]
+    T = sum(lens)
+    Hkv = 2
+    Hq = Hkv * G
+    q = activations(51, 1, (T, Hq, d), dtype)
+    k = activations(51, 2, (T, Hkv, d), dtype)
+    v = activations(51, 3, (T, Hkv, d), dtype)
+    rng = np.random.default_rng(51)
+    s_c = rng.random(T).astype(np.float32)
+    t = rng.uniform(0.8, 1.2, Hq).astype(np.float32)
+    g = rng.uniform(0.0, 2.0, Hq).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dev = "cuda"
+    o, lse = tg.gated_attn_fwd(to_device(q), to_device(k), to_device(v), torch.from_numpy(s_c).to(dev),
+                               torch.from_numpy(t).to(dev), torch.from_numpy(g).to(dev),
+                               torch.from_numpy(cu).to(dev), max(lens), want_lse=True)
+    torch.cuda.synchronize()
+    o_r, lse_r = O.gated_attention(q.value, k.value, v.value, s_c, t, g, cu)
+    assert_close(f64(o), o_r, dtype, "attention out")
+    assert_close(lse.cpu().numpy(), lse_r, dtype, "lse")
+    o2, _ = tg.gated_attn_fwd(to_device(q), to_device(k), to_device(v), torch.from_numpy(s_c).to(dev),
+                              torch.from_numpy(t).to(dev), torch.from_numpy(g).to(dev),
+                              torch.from_numpy(cu).to(dev), max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)  # deterministic
+
+
+def test_attention_bias_reduces_to_plain_when_gain_zero():
+    """g = 0: the kernel's result must not depend on s_c at all."""
+    lens = [300, 257]
+    T, Hq, Hkv, d = sum(lens), 4, 2, 128
+    q, k, v = (to_device(activations(52, i, (T, H, d), "bf16")) for i, H in ((1, Hq), (2, Hkv), (3, Hkv)))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    t = torch.ones(Hq, device="cuda")
+    g = torch.zeros(Hq, device="cuda")
+    o1, _ = tg.gated_attn_fwd(q, k, v, torch.rand(T, device="cuda"), t, g, cu, 300)
+    o2, _ = tg.gated_attn_fwd(q, k, v, torch.rand(T, device="cuda"), t, g, cu, 300)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
