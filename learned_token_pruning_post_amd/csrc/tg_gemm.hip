@@ -6,24 +6,33 @@
 // token tile the B operand, so every lane ends with 4 consecutive output
 // features of one token and stores 8 bytes at a time.
 //
-// Tiling: BK = 64; each wave owns a 64 (features) x 128 (tokens) tile made of
-// 2 x 4 MFMA 32x32x16 bf16 blocks (128 fp32 accumulators per lane). A
-// workgroup is WN x WM waves. Tiles are staged global -> registers -> LDS
-// (double buffer, one barrier per k-step; the next tile's global loads are in
-// flight while the current one feeds the MFMAs). LDS rows are 128 B with the
-// 16-byte chunk index XOR-swizzled by (row & 7) so the 16-byte fragment reads
-// of 8 consecutive rows hit distinct banks.
+// Tiling: BK = 64 (128-byte LDS rows). A workgroup of WN x WM waves owns a
+// BN (features) x BM (tokens) tile; each wave owns (BN/WN) x (BM/WM) made of
+// 32x32x16 bf16 MFMA blocks with fp32 accumulators. Tiles move global -> LDS
+// with gfx950 direct-to-LDS loads (global_load_lds_dwordx4): no register
+// staging, no per-lane predication, NSTAGE k-tiles in flight in an LDS ring,
+// one barrier per k-tile. Each 1 KB load instruction fills 8 rows; the lane
+// that lands in 16-byte slot (row, c) fetches logical chunk c ^ ((row>>1)&7),
+// so the MFMA fragment reads (16 consecutive rows per 16-lane phase, same
+// logical chunk) hit distinct banks of the 64-bank LDS. Rows past M or N are clamped to the last valid row (their
+// results are never stored).
+//
+// Workgroups are ordered for the 8 XCDs (private L2 each): consecutive
+// hardware workgroup ids rotate over XCDs, so ids are remapped to give each
+// XCD a contiguous run of tiles, token-block fastest, which share weight tiles.
 //
 // Epilogues, fused on the accumulators:
 //   PLAIN  : out = acc (+ residual)                         (O and down proj)
 //   QKV    : rotate-half RoPE of q and k, scatter to q / k-cache / v-cache.
-//            Weight rows are loaded permuted so each lane holds both halves
-//            (i, i + d/2) of its rotary pairs.
+//            A wave's 128 feature rows are whole heads, so each lane holds
+//            both halves (i, i + d/2) of its rotary pairs.
 //   SWIGLU : gate and up rows interleaved per 32 -> silu(g) * u
 //   SCORE  : scorer logit: sum_n GELU(acc + b1[n]) * w2[n], then sigmoid
 //            (the [tokens, H1] activations never reach memory)
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
+
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace tg {
 
@@ -55,29 +64,73 @@ struct GemmParams {
   float* partial;
 };
 
-template <int MODE>
-__device__ __forceinline__ const bf16* weight_row(const GemmParams& p, int n0, int ln) {
-  if (MODE == MODE_PLAIN || MODE == MODE_SCORE) {
-    const int gn = n0 + ln;
-    return gn < p.N ? p.W0 + (size_t)gn * p.K : nullptr;
+// 16-byte direct global -> LDS load for the whole wave: lane l's 16 bytes land
+// at lds_base + 16*l. m0 carries the wave's LDS byte address.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// QKV feature order inside a block. A lane must hold both halves (i, i+d/2)
+// of its rotary pairs, i.e. the wave's feature rows must contain whole half
+// heads in matching subtiles. With 128-row wave tiles, or d = 64, the natural
+// order does this. With 64-row wave tiles and d = 128, rows are permuted
+// inside each 128-row head by swapping bits 5 and 6 of the local row, so wave
+// 2h+w of a head gets dims [32w, 32w+32) and [64+32w, 96+32w).
+template <int TN>
+__device__ __forceinline__ int qkv_colmap(int lc, int hd) {
+  if (TN == 64 && hd == 128) {
+    const int c = lc & 127;
+    return (lc & ~127) | (((c >> 5) & 1) << 6) | (((c >> 6) & 1) << 5) | (c & 31);
+  }
+  return lc;
+}
+
+// Source of load block `blk` (8 consecutive LDS rows; W rows first, then X
+// rows): base pointer, first row and last valid row. Every block lies inside
+// one matrix (head and chunk sizes are multiples of 8), so all three are
+// wave-uniform; only the clamp to the last valid row is per lane.
+template <int MODE, int BN, int TN>
+__device__ __forceinline__ void block_src(const GemmParams& p, int n0, int m0, int blk,
+                                          const bf16*& base, int& r0, int& rmax) {
+  if (blk >= BN / 8) {
+    base = p.X;
+    r0 = m0 + (blk - BN / 8) * 8;
+    rmax = p.M - 1;
+  } else if (MODE == MODE_SWIGLU) {
+    // per wave: subtiles alternate gate (even) / up (odd) over the same 32 features
+    const int ln = blk * 8;
+    const int wv = ln / TN, j = (ln % TN) >> 5;
+    base = (j & 1) ? p.W1 : p.W0;
+    r0 = (n0 >> 1) + wv * (TN >> 1) + (j >> 1) * 32 + (ln & 31);
+    rmax = p.I - 1;
   } else if (MODE == MODE_QKV) {
-    int gn;
-    if (p.hd == 128) {
-      const int c = ln & 127;
-      const int perm = (((c >> 5) & 1) << 6) | (((c >> 6) & 1) << 5) | (c & 31);
-      gn = n0 + (ln & ~127) + perm;
-    } else {
-      gn = n0 + ln;
-    }
+    const int gn0 = n0 + qkv_colmap<TN>(blk * 8, p.hd);
+    const int gn = min(gn0, p.N - 1);
     const int nq = p.Hq * p.hd, nk = p.Hkv * p.hd;
-    if (gn < nq) return p.W0 + (size_t)gn * p.K;
-    if (gn < nq + nk) return p.W1 + (size_t)(gn - nq) * p.K;
-    if (gn < nq + 2 * nk) return p.W2 + (size_t)(gn - nq - nk) * p.K;
-    return nullptr;
-  } else {  // SWIGLU
-    const int idx = (n0 >> 1) + (ln >> 6) * 32 + (ln & 31);
-    if (idx >= p.I) return nullptr;
-    return (((ln >> 5) & 1) ? p.W1 : p.W0) + (size_t)idx * p.K;
+    if (gn < nq) {
+      base = p.W0;
+      r0 = gn0;
+      rmax = nq - 1;
+    } else if (gn < nq + nk) {
+      base = p.W1;
+      r0 = gn0 - nq;
+      rmax = nk - 1;
+    } else {
+      base = p.W2;
+      r0 = gn0 - nq - nk;
+      rmax = nk - 1;
+    }
+  } else {
+    base = p.W0;
+    r0 = n0 + blk * 8;
+    rmax = p.N - 1;
   }
 }
 
@@ -94,149 +147,21 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float 
   *reinterpret_cast<bf16x4*>(dst) = v;
 }
 
-template <int MODE, int WN, int WM>
-__global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int NT = WN * WM * 64;
-  constexpr int BN = WN * 64;
-  constexpr int BM = WM * 128;
-  constexpr int WCH = BN * 8 / NT;  // 16-byte chunks of the W tile per thread
-  constexpr int XCH = BM * 8 / NT;
-  constexpr int STAGE = (BN + BM) * 64;  // bf16 elements per stage
-
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave % WN;
-  const int wm = wave / WN;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int K = p.K;
-
-  // per-thread global source rows (fixed across k-steps)
-  const bf16* wsrc[WCH];
-  const bf16* xsrc[XCH];
-  int wdst[WCH], xdst[XCH];
+// QKV epilogue. Block j pairs with block j + P of the same wave (dims e and
+// e + d/2 of one head, same lane, same register); P = 2 for 128-row wave
+// tiles with d = 128, else 1 (see qkv_colmap for the row order).
+template <int HD, int SN, int SM, int TN, int TM>
+__device__ __forceinline__ void qkv_epilogue(const GemmParams& p, const f32x16 (&acc)[SN][SM],
+                                             int n0, int m0, int wn, int wm, int lane) {
+  constexpr int hd = HD, hh = HD / 2;
+  constexpr int P = (TN == 128 && HD == 128) ? 2 : 1;
+  const int half = lane >> 5, ml = lane & 31;
 #pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int c = tid + i * NT;
-    const int row = c >> 3, kc = c & 7;
-    const bf16* r = weight_row<MODE>(p, n0, row);
-    wsrc[i] = r ? r + kc * 8 : nullptr;
-    wdst[i] = row * 64 + ((kc ^ (row & 7)) << 3);
-  }
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int c = tid + i * NT;
-    const int row = c >> 3, kc = c & 7;
-    const int gm = m0 + row;
-    xsrc[i] = gm < p.M ? p.X + (size_t)gm * K + kc * 8 : nullptr;
-    xdst[i] = BN * 64 + row * 64 + ((kc ^ (row & 7)) << 3);
-  }
-
-  uint4 wreg[WCH], xreg[XCH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < WCH; ++i)
-      wreg[i] = wsrc[i] ? *reinterpret_cast<const uint4*>(wsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < XCH; ++i)
-      xreg[i] = xsrc[i] ? *reinterpret_cast<const uint4*>(xsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto sstore = [&](int stage) {
-    bf16* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) *reinterpret_cast<uint4*>(base + wdst[i]) = wreg[i];
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) *reinterpret_cast<uint4*>(base + xdst[i]) = xreg[i];
-  };
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = zero_f32x16();
-
-  // fragment read offsets (elements) inside a stage
-  const int half = lane >> 5;
-  int woff[2], xoff[4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = wn * 64 + j * 32 + (lane & 31);
-    woff[j] = row * 64;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wm * 128 + i * 32 + (lane & 31);
-    xoff[i] = BN * 64 + row * 64;
-  }
-  const int rsw = lane & 7;  // (row & 7) is lane & 7 for every fragment row
-
-  const int KT = K / 64;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload((kt + 1) * 64);
-    const bf16* base = smem + (kt & 1) * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ((ks * 2 + half) ^ rsw) << 3;
-      bf16x8 wf[2], xf[4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(base + woff[j] + ch);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const bf16x8*>(base + xoff[i] + ch);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = mfma32(wf[j], xf[i], acc[j][i]);
-    }
-    if (kt + 1 < KT) sstore((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // ---------------- epilogues ----------------
-  const int ml = lane & 31;
-  if (MODE == MODE_PLAIN) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + ml;
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int n = n0 + wn * 64 + j * 32 + rq * 8 + half * 4;
-          if (n >= p.N) continue;
-          float v0 = acc[j][i][rq * 4 + 0], v1 = acc[j][i][rq * 4 + 1];
-          float v2 = acc[j][i][rq * 4 + 2], v3 = acc[j][i][rq * 4 + 3];
-          const size_t o = (size_t)m * p.N + n;
-          if (p.resid) {
-            const bf16x4 r = *reinterpret_cast<const bf16x4*>(p.resid + o);
-            v0 += bf2f(r[0]);
-            v1 += bf2f(r[1]);
-            v2 += bf2f(r[2]);
-            v3 += bf2f(r[3]);
-          }
-          store_bf16x4(p.out + o, v0, v1, v2, v3);
-        }
-    }
-  } else if (MODE == MODE_QKV) {
-    const int hd = p.hd, hh = hd >> 1;
+  for (int j = 0; j < SN; ++j) {
+    if ((j / P) & 1) continue;  // second halves are handled with their partner
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      // global column of the j = 0 element (the j = 1 partner is + d/2)
-      const int e = rq * 8 + half * 4;
-      int gn0;
-      if (hd == 128) {
-        const int c = (wn * 64 + e) & 127;  // j = 0 -> bit 5 clear
-        const int perm = (((c >> 6) & 1) << 5) | (c & 31);
-        gn0 = n0 + ((wn * 64) & ~127) + perm;
-      } else {
-        gn0 = n0 + wn * 64 + e;
-      }
+      const int gn0 = n0 + qkv_colmap<TN>(wn * TN + j * 32 + rq * 8 + half * 4, HD);
       const int gh = gn0 / hd;
       const int dim = gn0 - gh * hd;  // < d/2
       if (gh >= p.Hq + 2 * p.Hkv) continue;
@@ -254,24 +179,26 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p) {
         ld = p.Hkv * hd;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + i * 32 + ml;
+      for (int i = 0; i < SM; ++i) {
+        const int m = m0 + wm * TM + i * 32 + ml;
         if (m >= p.M) continue;
+        const f32x16& a0 = acc[j][i];
+        const f32x16& a1 = acc[(j + P) % SN][i];
         float y0[4], y1[4];
         if (rot) {
           const f32x4 cs = *reinterpret_cast<const f32x4*>(p.rope + (size_t)m * hd + dim);
           const f32x4 sn = *reinterpret_cast<const f32x4*>(p.rope + (size_t)m * hd + hh + dim);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float x0 = acc[0][i][rq * 4 + t], x1 = acc[1][i][rq * 4 + t];
+            const float x0 = a0[rq * 4 + t], x1 = a1[rq * 4 + t];
             y0[t] = x0 * cs[t] - x1 * sn[t];
             y1[t] = x1 * cs[t] + x0 * sn[t];
           }
         } else {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            y0[t] = acc[0][i][rq * 4 + t];
-            y1[t] = acc[1][i][rq * 4 + t];
+            y0[t] = a0[rq * 4 + t];
+            y1[t] = a1[rq * 4 + t];
           }
         }
         bf16* row = dst + (size_t)m * ld;
@@ -279,59 +206,192 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p) {
         store_bf16x4(row + hh, y1[0], y1[1], y1[2], y1[3]);
       }
     }
-  } else if (MODE == MODE_SWIGLU) {
+  }
+}
+
+template <int MODE, int BN, int BM, int WN, int WM, int NSTAGE>
+__global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, int NB, int MB) {
+  constexpr int NW = WN * WM;
+  constexpr int TN = BN / WN, TM = BM / WM;   // wave tile
+  constexpr int SN = TN / 32, SM = TM / 32;   // MFMA blocks per wave
+  constexpr int STAGE = (BN + BM) * 128;      // bytes per LDS stage
+  constexpr int NBLK = (BN + BM) / 8;         // 1 KB load blocks per stage
+  constexpr int LPW = NBLK / NW;              // load instructions per wave per stage
+  static_assert(NBLK % NW == 0, "load blocks must split evenly over waves");
+  static_assert(MODE != MODE_QKV || TN == 128 || TN == 64, "QKV wave tiles are 64 or 128 rows");
+  static_assert(MODE != MODE_SWIGLU || SN % 2 == 0, "SwiGLU pairs gate/up subtiles");
+
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+
+  // XCD-aware tile order: hardware id L runs on XCD L % 8
+  const int ntile = NB * MB;
+  int tile = blockIdx.x;
+  if ((ntile & 7) == 0) tile = (blockIdx.x & 7) * (ntile >> 3) + (blockIdx.x >> 3);
+  const int mb = tile % MB, nb = tile / MB;
+  const int n0 = nb * BN, m0 = mb * BM;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN, wm = wave / WN;
+  const int K = p.K;
+
+  // lane l of a load block lands in row l/8, 16-byte slot l%8, and fetches
+  // logical chunk (l%8) ^ swz(row) with swz(row) = (row >> 1) & 7: a 16-lane
+  // ds_read_b128 phase covers 16 consecutive rows, whose 128-byte rows fall
+  // on two halves of the 256-byte bank space, and swz takes 8 distinct values
+  // over the even and over the odd rows of any aligned 16, so the phase hits
+  // 16 distinct 16-byte bank groups. The swizzle of row 8*blk + l/8 depends
+  // on the block's parity only, giving two per-lane offsets.
+  const int rl = lane >> 3;
+  const int kc0 = ((lane & 7) ^ (rl >> 1)) * 8;        // even blocks
+  const int kc1 = ((lane & 7) ^ (4 + (rl >> 1))) * 8;  // odd blocks
+  const uint32_t lane_off0 = (uint32_t)(rl * K + kc0) * (uint32_t)sizeof(bf16);
+  const uint32_t lane_off1 = (uint32_t)(rl * K + kc1) * (uint32_t)sizeof(bf16);
+  auto issue = [&](int kt, int st) {
+    const uint32_t base_lds = lds0 + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + ml;
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wave + NW * i;
+      const bf16* base;
+      int r0, rmax;
+      block_src<MODE, BN, TN>(p, n0, m0, blk, base, r0, rmax);
+      const bf16* g;
+      if (r0 + 7 <= rmax) {
+        g = reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base + (size_t)r0 * K + kt * 64) +
+                                          ((blk & 1) ? lane_off1 : lane_off0));
+      } else {  // edge block: clamp each lane's row
+        const int r = min(r0 + rl, rmax);
+        g = base + (size_t)r * K + kt * 64 + ((blk & 1) ? kc1 : kc0);
+      }
+      lds_dma16(g, __builtin_amdgcn_readfirstlane(base_lds + blk * 1024));
+    }
+  };
+
+  f32x16 acc[SN][SM];
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+#pragma unroll
+    for (int i = 0; i < SM; ++i) acc[j][i] = zero_f32x16();
+
+  const int half = lane >> 5, rsw = (lane >> 1) & 7;  // swz of fragment row (32-aligned base + lane%32)
+  const int KT = K / 64;
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < KT) issue(s, s);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + NSTAGE - 2 < KT)
+      wait_vmcnt<LPW * (NSTAGE - 2)>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
+    const unsigned char* st = smem + (kt % NSTAGE) * STAGE;
+    const unsigned char* wb = st + (wn * TN + (lane & 31)) * 128;
+    const unsigned char* xb = st + (BN + wm * TM + (lane & 31)) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = ((ks * 2 + half) ^ rsw) << 4;
+      bf16x8 wf[SN], xf[SM];
+#pragma unroll
+      for (int j = 0; j < SN; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(wb + j * 32 * 128 + ch);
+#pragma unroll
+      for (int i = 0; i < SM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>(xb + i * 32 * 128 + ch);
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int i = 0; i < SM; ++i) acc[j][i] = mfma32(wf[j], xf[i], acc[j][i]);
+    }
+  }
+
+  // ---------------- epilogues ----------------
+  const int ml = lane & 31;
+  if (MODE == MODE_PLAIN) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int m = m0 + wm * TM + i * 32 + ml;
       if (m >= p.M) continue;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int idx = (n0 >> 1) + wn * 32 + rq * 8 + half * 4;
-        if (idx >= p.I) continue;
-        float y[4];
+      for (int j = 0; j < SN; ++j)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float gt = acc[0][i][rq * 4 + t], up = acc[1][i][rq * 4 + t];
-          y[t] = gt / (1.0f + __expf(-gt)) * up;
+        for (int rq = 0; rq < 4; ++rq) {
+          const int n = n0 + wn * TN + j * 32 + rq * 8 + half * 4;
+          if (n >= p.N) continue;
+          float v0 = acc[j][i][rq * 4 + 0], v1 = acc[j][i][rq * 4 + 1];
+          float v2 = acc[j][i][rq * 4 + 2], v3 = acc[j][i][rq * 4 + 3];
+          const size_t o = (size_t)m * p.N + n;
+          if (p.resid) {
+            const bf16x4 r = *reinterpret_cast<const bf16x4*>(p.resid + o);
+            v0 += bf2f(r[0]);
+            v1 += bf2f(r[1]);
+            v2 += bf2f(r[2]);
+            v3 += bf2f(r[3]);
+          }
+          store_bf16x4(p.out + o, v0, v1, v2, v3);
         }
-        store_bf16x4(p.act + (size_t)m * p.I + idx, y[0], y[1], y[2], y[3]);
-      }
+    }
+  } else if (MODE == MODE_QKV) {
+    if (p.hd == 128)
+      qkv_epilogue<128, SN, SM, TN, TM>(p, acc, n0, m0, wn, wm, lane);
+    else
+      qkv_epilogue<64, SN, SM, TN, TM>(p, acc, n0, m0, wn, wm, lane);
+  } else if (MODE == MODE_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int m = m0 + wm * TM + i * 32 + ml;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int jj = 0; jj < SN / 2; ++jj)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int idx = (n0 >> 1) + wn * (TN >> 1) + jj * 32 + rq * 8 + half * 4;
+          if (idx >= p.I) continue;
+          float y[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float gt = acc[2 * jj][i][rq * 4 + t], up = acc[2 * jj + 1][i][rq * 4 + t];
+            y[t] = gt / (1.0f + __expf(-gt)) * up;
+          }
+          store_bf16x4(p.act + (size_t)m * p.I + idx, y[0], y[1], y[2], y[3]);
+        }
     }
   } else {  // SCORE
-    float part[4];
+    float part[SM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[i] = 0.f;
+    for (int i = 0; i < SM; ++i) part[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < SN; ++j)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int n = n0 + wn * 64 + j * 32 + rq * 8 + half * 4 + t;
+          const int n = n0 + wn * TN + j * 32 + rq * 8 + half * 4 + t;
           if (n < p.N) {
             const float bb = bf2f(p.b1[n]), ww = bf2f(p.w2[n]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part[i] += gelu_erf(acc[j][i][rq * 4 + t] + bb) * ww;
+            for (int i = 0; i < SM; ++i) part[i] += gelu_erf(acc[j][i][rq * 4 + t] + bb) * ww;
           }
         }
-    float* red = reinterpret_cast<float*>(smem);  // pipeline buffers are free now
+    __syncthreads();  // every wave is done with the LDS ring
+    float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < SM; ++i) {
       part[i] += __shfl_xor(part[i], 32, 64);
-      if (half == 0) red[wn * BM + wm * 128 + i * 32 + ml] = part[i];
+      if (half == 0) red[wn * BM + wm * TM + i * 32 + ml] = part[i];
     }
     __syncthreads();
-    for (int r = tid; r < BM; r += NT) {
+    for (int r = tid; r < BM; r += NW * 64) {
       const int m = m0 + r;
       if (m >= p.M) continue;
       float u = 0.f;
 #pragma unroll
       for (int w = 0; w < WN; ++w) u += red[w * BM + r];
-      if (gridDim.x == 1) {
+      if (NB == 1) {
         u += bf2f(p.b2[0]);
         p.s_out[m] = 1.0f / (1.0f + expf(-u));
       } else {
-        p.partial[(size_t)blockIdx.x * p.M + m] = u;
+        p.partial[(size_t)nb * p.M + m] = u;
       }
     }
   }
@@ -347,30 +407,33 @@ __global__ void score_finish_kernel(const float* __restrict__ partial, int nblk,
   s_out[m] = 1.0f / (1.0f + expf(-u));
 }
 
-template <int MODE, int WN, int WM>
+template <int MODE, int BN, int BM, int WN, int WM, int NSTAGE>
 static hipError_t launch_gemm(const GemmParams& p, int Ncols, hipStream_t stream) {
-  constexpr int BN = WN * 64, BM = WM * 128;
-  constexpr size_t lds = (size_t)2 * (BN + BM) * 64 * sizeof(bf16);
+  constexpr size_t lds = (size_t)NSTAGE * (BN + BM) * 128;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MODE, WN, WM>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MODE, BN, BM, WN, WM, NSTAGE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((Ncols + BN - 1) / BN, (p.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WN, WM>), grid, dim3(WN * WM * 64), lds, stream, p);
+  const int NB = (Ncols + BN - 1) / BN, MB = (p.M + BM - 1) / BM;
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BN, BM, WN, WM, NSTAGE>), dim3(NB * MB),
+                     dim3(WN * WM * 64), lds, stream, p, NB, MB);
   return hipGetLastError();
 }
 
-// config choice: the biggest tile that still gives >= 256 workgroups (one per CU)
+// Tile choice (measured on MI355X at M = 4096 tokens): 8 waves per workgroup
+// (two per SIMD, so one wave's MFMAs cover the other's LDS and barrier
+// waits). 256 x 256 tiles (64 x 128 per wave, 2-stage ring) for the wide
+// gate/up projection; 256 x 128 tiles (64 x 64 per wave, 3-stage ring) when
+// 256 x 256 would leave CUs idle.
 template <int MODE>
 static hipError_t launch_auto(const GemmParams& p, int Ncols, hipStream_t stream) {
   const long tA = (long)((Ncols + 255) / 256) * ((p.M + 255) / 256);
-  const long tC = (long)((Ncols + 255) / 256) * ((p.M + 127) / 128);
-  if (tA >= 256) return launch_gemm<MODE, 4, 2>(p, Ncols, stream);
-  if (tC >= 256) return launch_gemm<MODE, 4, 1>(p, Ncols, stream);
-  return launch_gemm<MODE, 2, 1>(p, Ncols, stream);
+  if (tA >= 512) return launch_gemm<MODE, 256, 256, 4, 2, 2>(p, Ncols, stream);
+  return launch_gemm<MODE, 256, 128, 4, 2, 3>(p, Ncols, stream);
 }
 
 hipError_t gemm_bf16_plain(const bf16* X, const bf16* W, const bf16* resid, bf16* out, int M,
@@ -444,11 +507,7 @@ hipError_t gemm_bf16_score(const bf16* X, const bf16* W1, const bf16* b1, const 
   p.s_out = s_out;
   p.partial = partial;
   const int nblk = (H1 + 255) / 256;
-  hipError_t e;
-  if ((long)((M + 255) / 256) * nblk >= 256)
-    e = launch_gemm<MODE_SCORE, 4, 2>(p, H1, stream);
-  else
-    e = launch_gemm<MODE_SCORE, 4, 1>(p, H1, stream);
+  hipError_t e = launch_gemm<MODE_SCORE, 256, 128, 4, 2, 3>(p, H1, stream);
   if (e != hipSuccess || nblk == 1) return e;
   hipLaunchKernelGGL(score_finish_kernel, dim3((M + 255) / 256), dim3(256), 0, stream,
                      (const float*)partial, nblk, (int64_t)M, b2, s_out);
