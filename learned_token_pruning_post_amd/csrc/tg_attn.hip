@@ -14,24 +14,35 @@
 //  * S^T = K Q^T and O^T = V^T P^T: the 32x32 accumulator layout puts one
 //    query per lane (column), so the row max / row sum are per lane plus one
 //    exchange with lane ^ 32, and P goes from the S accumulator straight into
-//    the B operand of the PV product without touching LDS (the k-slot order
-//    of P is matched by a fixed permutation of keys in the transposed V tile);
-//  * log2-domain online softmax: t_h*log2(e)/sqrt(d) is one multiply, the bias
-//    g_h*log2(e)*s_c[j] is precomputed per key and head when the tile is
-//    staged;
-//  * K/V tiles of 64 keys double-buffered through registers -> LDS; K rows
-//    XOR-swizzled, V stored transposed ([d][key]) with a swizzle that keeps
-//    both the transposing writes and the fragment reads spread over banks;
+//    the B operand of the PV product without touching LDS;
+//  * K, V and the tile's gate scores move global -> LDS with direct-to-LDS
+//    loads into a 2-stage ring (one barrier per 64-key tile). V stays
+//    row-major: its V^T fragments come from ds_read_b64_tr_b16, which hands
+//    each lane of a 16-lane group 4 keys of one feature column; the key order
+//    of those fragments matches the k-slot order of P in the accumulator.
+//    LDS rows are XOR-swizzled so that both the K fragment reads and the
+//    transposing V reads of a phase hit distinct banks;
+//  * log2-domain online softmax, t_h*log2(e)/sqrt(d) folded into one
+//    multiply, g_h*log2(e)*s_c[j] added per key; the rescale of the output
+//    accumulator is skipped when no row maximum of the wave grew;
 //  * the heaviest (last) query tiles are dispatched first.
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
 namespace tg {
 
-__device__ __forceinline__ int vperm16(int p) {  // swap bits 2 and 3
-  return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-}
-__device__ __forceinline__ int vswz(int dd) { return (dd ^ (dd >> 3)) & 7; }
+template <int HD>
+struct AttnLayout {
+  static constexpr int RB = HD * 2;          // bytes per K or V row
+  static constexpr int KCH = HD / 8;         // 16-byte chunks per row
+  static constexpr int RPB = 1024 / RB;      // rows per 1 KB load block
+  static constexpr int TILE = 64 * RB;       // bytes of a 64-key K (or V) tile
+  static constexpr int STAGE = 2 * TILE + 256;  // K, V, 64 fp32 scores
+  // K fragment reads: 16 lanes read 16 consecutive keys, same logical chunk
+  __device__ static int kswz(int key) { return HD == 128 ? (key & 15) : ((key >> 1) & 7); }
+  // V transposing reads: 32 lanes read 4 consecutive (4-aligned) keys x 4 chunks
+  __device__ static int vswz(int key) { return HD == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
+};
 
 template <int G, int HD>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
@@ -39,17 +50,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const float* __restrict__ s_c, const float* __restrict__ t, const float* __restrict__ g,
     const int32_t* __restrict__ cu_kept, int B, int Hq, int Hkv, int n_qt, bf16* __restrict__ o,
     float* __restrict__ lse) {
+  using LY = AttnLayout<HD>;
   constexpr int WPH = 4 / G;     // waves per q-head
   constexpr int BQ = 32 * WPH;   // queries per workgroup
-  constexpr int KCH = HD / 8;    // 16-byte chunks per K row
-  constexpr int KSTAGE = 64 * HD;
-  constexpr int VSTAGE = HD * 64;
-  constexpr int NKL = HD / 32;   // K chunks loaded per thread
   constexpr int ND = HD / 32;    // 32-wide d blocks of O^T
-  extern __shared__ __attribute__((aligned(16))) unsigned char attn_smem[];
-  bf16* Ks = reinterpret_cast<bf16*>(attn_smem);
-  bf16* Vs = Ks + 2 * KSTAGE;
-  float* bias = reinterpret_cast<float*>(Vs + 2 * VSTAGE);  // [2][G][64]
+  constexpr int NKB = 64 / LY::RPB;  // load blocks per K (or V) tile
+  constexpr int LPW = NKB / 4;       // of them per wave
+  extern __shared__ __attribute__((aligned(1024))) unsigned char attn_smem[];
+  const uint32_t lds0 = lds_addr(attn_smem);
 
   const int tid = threadIdx.x;
   const int L = blockIdx.x;
@@ -63,7 +71,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   if (q0 >= Kb) return;
   const int Ttot = cu_kept[B];
 
-  const int wave = tid >> 6, lane = tid & 63, l31 = lane & 31, half = lane >> 5;
+  const int lane = tid & 63, l31 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gi = wave / WPH, qs = wave % WPH;
   const int h = hk * G + gi;
   const int qw0 = q0 + qs * 32;
@@ -75,71 +84,34 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
 
   bf16x8 qf[HD / 16];
   {
-    const bf16* qrow = q + ((size_t)(seq0 + qi) * Hq + h) * HD + half * 8;
+    const bf16* qrow = q + ((size_t)(seq0 + min(qi, Kb - 1)) * Hq + h) * HD + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks)
-      qf[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : zero_bf16x8();
+    for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
   const float cscale = t[h] * TG_LOG2E / sqrtf((float)HD);
+  const float gl = g[h] * TG_LOG2E;
 
-  // ---- tile loader state ----
-  uint4 kreg[NKL];
-  bf16x8 vreg[4];
-  float sreg = 0.f;
-  const int vdc = tid % KCH, vkg = tid / KCH;
-  const bool vloader = tid < KCH * 16;
-
-  auto gload = [&](int kt) {
-    const int kb0 = kt * 64;
+  // ---- direct-to-LDS tile loads: lane l of a block lands in row l / KCH,
+  // slot l % KCH and fetches the logical chunk that the swizzle puts there ----
+  const int rib = lane / LY::KCH, slot = lane % LY::KCH;
+  const size_t kv_row = (size_t)Hkv * HD;  // elements between consecutive tokens
+  const bf16* kbase = k + (size_t)seq0 * kv_row + (size_t)hk * HD;
+  const bf16* vbase = v + (size_t)seq0 * kv_row + (size_t)hk * HD;
+  auto issue = [&](int kt, int st) {
+    const uint32_t sb = lds0 + st * LY::STAGE;
 #pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / KCH, kc = c % KCH;
-      const int gk = kb0 + key;
-      kreg[i] = gk < Kb ? *reinterpret_cast<const uint4*>(
-                              k + ((size_t)(seq0 + gk) * Hkv + hk) * HD + kc * 8)
-                        : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wave + 4 * i;
+      const int row = blk * LY::RPB + rib;             // key inside the tile
+      const int key = min(kt * 64 + row, Kb - 1);      // rows past the sequence: clamped, masked later
+      lds_dma16(kbase + (size_t)key * kv_row + ((slot ^ LY::kswz(row)) << 3),
+                __builtin_amdgcn_readfirstlane(sb + blk * 1024));
+      lds_dma16(vbase + (size_t)key * kv_row + ((slot ^ LY::vswz(row)) << 3),
+                __builtin_amdgcn_readfirstlane(sb + LY::TILE + blk * 1024));
     }
-    if (vloader) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gk = kb0 + vkg * 4 + i;
-        vreg[i] = gk < Kb ? *reinterpret_cast<const bf16x8*>(
-                                v + ((size_t)(seq0 + gk) * Hkv + hk) * HD + vdc * 8)
-                          : zero_bf16x8();
-      }
-    }
-    if (tid < 64) {
-      const int gk = kb0 + tid;
-      sreg = gk < Kb ? s_c[seq0 + gk] : 0.f;
-    }
-  };
-  auto sstore = [&](int st) {
-    bf16* kd = Ks + st * KSTAGE;
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / KCH, kc = c % KCH;
-      *reinterpret_cast<uint4*>(kd + key * HD + ((kc ^ (key & (KCH - 1))) << 3)) = kreg[i];
-    }
-    if (vloader) {
-      bf16* vd = Vs + st * VSTAGE;
-      const int p = vperm16((vkg * 4) & 15) | ((vkg * 4) & ~15);
-      const int chunk = p >> 3, off = p & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = vdc * 8 + e;
-        bf16x4 pk;
-        pk[0] = vreg[0][e];
-        pk[1] = vreg[1][e];
-        pk[2] = vreg[2][e];
-        pk[3] = vreg[3][e];
-        *reinterpret_cast<bf16x4*>(vd + dd * 64 + ((chunk ^ vswz(dd)) << 3) + off) = pk;
-      }
-    }
-    if (tid < 64) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) bias[(st * G + j) * 64 + tid] = sreg * g[hk * G + j] * TG_LOG2E;
+    if (wave == 0) {  // one gate score per lane
+      const int key = min(kt * 64 + lane, Kb - 1);
+      lds_dma4(s_c + seq0 + key, __builtin_amdgcn_readfirstlane(sb + 2 * LY::TILE));
     }
   };
 
@@ -148,76 +120,97 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   for (int db = 0; db < ND; ++db) oacc[db] = zero_f32x16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int ksw = l31 & (KCH - 1);
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // V^T fragment source (bytes inside a stage) for key-step kk, d block db:
+  // group G = lane / 16 of the wave: k-slot group G / 2, d half G % 2
+  const int vg = (lane >> 4) & 3, vs = lane & 15;
+  const int vkey_lo = 4 * (vg >> 1) + (vs >> 2);         // + 16*kk (+8 for the high half)
+  const int vd = 16 * (vg & 1) + 4 * (vs & 3);            // + 32*db
+
+  issue(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt) gload(kt + 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < n_kt) issue(kt + 1, (kt + 1) & 1);
     const int st = kt & 1;
-    const int kbase = kt * 64;
-    if (wave_any && kbase <= qw0 + 31) {
-      const bf16* kd = Ks + st * KSTAGE;
+    const int kbase_key = kt * 64;
+    if (wave_any && kbase_key <= qw0 + 31) {
+      const unsigned char* ks_ = attn_smem + st * LY::STAGE;
+      const unsigned char* vs_ = ks_ + LY::TILE;
+      const float* ss_ = reinterpret_cast<const float*>(ks_ + 2 * LY::TILE);
       f32x16 sacc[2];
       sacc[0] = zero_f32x16();
       sacc[1] = zero_f32x16();
+      const int ksw = LY::kswz(l31);  // same for key l31 and 32 + l31
 #pragma unroll
       for (int ks = 0; ks < HD / 16; ++ks) {
-        const int ch = ((ks * 2 + half) ^ ksw) << 3;
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kd + l31 * HD + ch);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kd + (32 + l31) * HD + ch);
+        const int ch = ((ks * 2 + half) ^ ksw) << 4;
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(ks_ + l31 * LY::RB + ch);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(ks_ + (32 + l31) * LY::RB + ch);
         sacc[0] = mfma32(k0, qf[ks], sacc[0]);
         sacc[1] = mfma32(k1, qf[ks], sacc[1]);
       }
-      const float* bs = bias + (st * G + gi) * 64;
-      const bool diag = kbase + 63 > qw0;
+      const bool diag = kbase_key + 63 > qw0;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int kl = kb * 32 + rq * 8 + half * 4;
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(bs + kl);
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(ss_ + kl);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float x = fmaf(sacc[kb][rq * 4 + e], cscale, bv[e]);
-            if (diag && kbase + kl + e > qi) x = -INFINITY;
+            float x = fmaf(sacc[kb][rq * 4 + e], cscale, sv[e] * gl);
+            if (diag && kbase_key + kl + e > qi) x = -INFINITY;
             sacc[kb][rq * 4 + e] = x;
             mx = fmaxf(mx, x);
           }
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      if (__any(m_new > m_run)) {  // some row max grew: rescale (alpha = 1 elsewhere)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+      }
       float rs = 0.f;
       bf16x8 pf[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
           rs += pv;
           pf[kb * 2 + (r >> 3)][r & 7] = f2bf(pv);
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      l_run += rs;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      const bf16* vd = Vs + st * VSTAGE;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key_lo = 16 * kk + vkey_lo, key_hi = key_lo + 8;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const int dd = db * 32 + l31;
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vd + dd * 64 + (((kk * 2 + half) ^ vswz(dd)) << 3));
+          const int d = 32 * db + vd;
+          const unsigned char* a_lo =
+              vs_ + key_lo * LY::RB + (((d >> 3) ^ LY::vswz(key_lo)) << 4) + (d & 7) * 2;
+          const unsigned char* a_hi =
+              vs_ + key_hi * LY::RB + (((d >> 3) ^ LY::vswz(key_hi)) << 4) + (d & 7) * 2;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(a_lo));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(a_hi));
+          bf16x8 vf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vf[e] = lo[e];
+            vf[4 + e] = hi[e];
+          }
           oacc[db] = mfma32(vf, pf[kk], oacc[db]);
         }
+      }
     }
-    if (kt + 1 < n_kt) sstore((kt + 1) & 1);
-    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -306,7 +299,7 @@ static hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, 
                                    int max_k, int Hq, int Hkv, void* o, float* lse,
                                    hipStream_t stream) {
   constexpr int BQ = 32 * (4 / G);
-  constexpr size_t lds = (size_t)2 * 2 * 64 * HD * sizeof(bf16) + (size_t)2 * G * 64 * sizeof(float);
+  constexpr size_t lds = (size_t)2 * AttnLayout<HD>::STAGE;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, HD>,

@@ -14,7 +14,36 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define TG_LOG2E 1.4426950408889634f
 #define TG_LN2 0.6931471805599453f
 
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace tg {
+
+// 16-byte direct global -> LDS load (gfx950 global_load_lds_dwordx4) for the
+// active lanes of a wave: lane l's 16 bytes land at lds_base + 16*l, with m0
+// carrying the wave's LDS byte address. Issued from asm so that the compiler
+// does not add its conservative vmcnt(0) before every later LDS read; the
+// callers order these loads with wait_vmcnt<> and a barrier themselves.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+
+// 4-byte variant: lane l's dword lands at lds_base + 4*l
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
 
 __device__ __forceinline__ float bf2f(bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ bf16 f2bf(float x) { return static_cast<bf16>(x); }  // RNE

@@ -32,8 +32,6 @@
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
-#pragma clang diagnostic ignored "-Winline-asm"
-
 namespace tg {
 
 enum { MODE_PLAIN = 0, MODE_QKV = 1, MODE_SWIGLU = 2, MODE_SCORE = 3 };
@@ -63,19 +61,6 @@ struct GemmParams {
   float* s_out;
   float* partial;
 };
-
-// 16-byte direct global -> LDS load for the whole wave: lane l's 16 bytes land
-// at lds_base + 16*l. m0 carries the wave's LDS byte address.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // QKV feature order inside a block. A lane must hold both halves (i, i+d/2)
 // of its rotary pairs, i.e. the wave's feature rows must contain whole half
