@@ -23,8 +23,8 @@
 //    LDS rows are XOR-swizzled so that both the K fragment reads and the
 //    transposing V reads of a phase hit distinct banks;
 //  * log2-domain online softmax, t_h*log2(e)/sqrt(d) folded into one
-//    multiply, g_h*log2(e)*s_c[j] added per key; the rescale of the output
-//    accumulator is skipped when no row maximum of the wave grew;
+//    multiply, g_h*log2(e)*s_c[j] added per key; the output accumulator is
+//    rescaled only when a row maximum grows by more than 8 (log2 units);
 //  * the heaviest (last) query tiles are dispatched first.
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
@@ -125,6 +125,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int vg = (lane >> 4) & 3, vs = lane & 15;
   const int vkey_lo = 4 * (vg >> 1) + (vs >> 2);         // + 16*kk (+8 for the high half)
   const int vd = 16 * (vg & 1) + 4 * (vs & 3);            // + 32*db
+  // byte offsets of the low-half reads; +16 keys (next kk) and +8 keys (high
+  // half) keep key & 3 and (key >> 1) & 1, hence the swizzle: constant offsets
+  int voff[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    const int d = 32 * db + vd;
+    voff[db] = vkey_lo * LY::RB + (((d >> 3) ^ LY::vswz(vkey_lo)) << 4) + (d & 7) * 2;
+  }
 
   issue(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -149,25 +157,43 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         sacc[0] = mfma32(k0, qf[ks], sacc[0]);
         sacc[1] = mfma32(k1, qf[ks], sacc[1]);
       }
-      const bool diag = kbase_key + 63 > qw0;
+      // logits in the log2 domain; keys past a query (diagonal tiles only) -> -inf
       float mx = -INFINITY;
+      if (kbase_key + 63 > qw0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int kl = kb * 32 + rq * 8 + half * 4;
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(ss_ + kl);
+          for (int rq = 0; rq < 4; ++rq) {
+            const int kl = kb * 32 + rq * 8 + half * 4;
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(ss_ + kl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float x = fmaf(sacc[kb][rq * 4 + e], cscale, sv[e] * gl);
-            if (diag && kbase_key + kl + e > qi) x = -INFINITY;
-            sacc[kb][rq * 4 + e] = x;
-            mx = fmaxf(mx, x);
+            for (int e = 0; e < 4; ++e) {
+              float x = fmaf(sacc[kb][rq * 4 + e], cscale, sv[e] * gl);
+              x = (kbase_key + kl + e > qi) ? -INFINITY : x;
+              sacc[kb][rq * 4 + e] = x;
+              mx = fmaxf(mx, x);
+            }
           }
-        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(ss_ + kb * 32 + rq * 8 + half * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = fmaf(sacc[kb][rq * 4 + e], cscale, sv[e] * gl);
+              sacc[kb][rq * 4 + e] = x;
+              mx = fmaxf(mx, x);
+            }
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {  // some row max grew: rescale (alpha = 1 elsewhere)
+      // Lazy rescale: keep the running max while no row exceeds it by more
+      // than 8 (p <= 2^8, far from fp32/bf16 overflow; exact after the final
+      // division by the row sum, which uses the same reference).
+      if (__any(mx > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -189,24 +215,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       l_run += rs;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int key_lo = 16 * kk + vkey_lo, key_hi = key_lo + 8;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const int d = 32 * db + vd;
-          const unsigned char* a_lo =
-              vs_ + key_lo * LY::RB + (((d >> 3) ^ LY::vswz(key_lo)) << 4) + (d & 7) * 2;
-          const unsigned char* a_hi =
-              vs_ + key_hi * LY::RB + (((d >> 3) ^ LY::vswz(key_hi)) << 4) + (d & 7) * 2;
+          const unsigned char* a_lo = vs_ + voff[db] + kk * 16 * LY::RB;
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
               (__attribute__((address_space(3))) bf16x4*)(a_lo));
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(a_hi));
-          bf16x8 vf;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vf[e] = lo[e];
-            vf[4 + e] = hi[e];
-          }
+              (__attribute__((address_space(3))) bf16x4*)(a_lo + 8 * LY::RB));
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[db] = mfma32(vf, pf[kk], oacc[db]);
         }
       }
