@@ -16,7 +16,7 @@
 //    exchange with lane ^ 32, and P goes from the S accumulator straight into
 //    the B operand of the PV product without touching LDS;
 //  * K, V and the tile's gate scores move global -> LDS with direct-to-LDS
-//    loads into a 2-stage ring (one barrier per 64-key tile). V stays
+//    buffer loads into a 2-stage ring (one barrier per 64-key tile). V stays
 //    row-major: its V^T fragments come from ds_read_b64_tr_b16, which hands
 //    each lane of a 16-lane group 4 keys of one feature column; the key order
 //    of those fragments matches the k-slot order of P in the accumulator.
@@ -91,28 +91,31 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const float cscale = t[h] * TG_LOG2E / sqrtf((float)HD);
   const float gl = g[h] * TG_LOG2E;
 
-  // ---- direct-to-LDS tile loads: lane l of a block lands in row l / KCH,
-  // slot l % KCH and fetches the logical chunk that the swizzle puts there ----
+  // ---- direct-to-LDS tile loads (buffer loads, range = this sequence, so
+  // keys past its end read as zeros and are masked). Lane l of a 1 KB block
+  // lands in row l / KCH, slot l % KCH, and fetches the logical chunk that the
+  // swizzle puts there. A wave's blocks are blk = wave + 4i: for K the
+  // swizzle depends on blk only through blk & 3 (= wave & 3), for V not at
+  // all, so each lane has one fixed byte offset per operand. ----
   const int rib = lane / LY::KCH, slot = lane % LY::KCH;
-  const size_t kv_row = (size_t)Hkv * HD;  // elements between consecutive tokens
-  const bf16* kbase = k + (size_t)seq0 * kv_row + (size_t)hk * HD;
-  const bf16* vbase = v + (size_t)seq0 * kv_row + (size_t)hk * HD;
+  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2u;  // bytes between consecutive tokens
+  const i32x4 rk = make_rsrc(k + (size_t)seq0 * Hkv * HD + (size_t)hk * HD, (uint32_t)Kb * row_bytes);
+  const i32x4 rv = make_rsrc(v + (size_t)seq0 * Hkv * HD + (size_t)hk * HD, (uint32_t)Kb * row_bytes);
+  const i32x4 rsc = make_rsrc(s_c + seq0, (uint32_t)Kb * 4u);
+  const int krow0 = (wave & 3) * LY::RPB + rib;  // row of this lane in the wave's first block
+  const uint32_t koff = rib * row_bytes + ((slot ^ LY::kswz(krow0)) << 4);
+  const uint32_t voff_l = rib * row_bytes + ((slot ^ LY::vswz(krow0)) << 4);
   auto issue = [&](int kt, int st) {
     const uint32_t sb = lds0 + st * LY::STAGE;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int blk = wave + 4 * i;
-      const int row = blk * LY::RPB + rib;             // key inside the tile
-      const int key = min(kt * 64 + row, Kb - 1);      // rows past the sequence: clamped, masked later
-      lds_dma16(kbase + (size_t)key * kv_row + ((slot ^ LY::kswz(row)) << 3),
-                __builtin_amdgcn_readfirstlane(sb + blk * 1024));
-      lds_dma16(vbase + (size_t)key * kv_row + ((slot ^ LY::vswz(row)) << 3),
-                __builtin_amdgcn_readfirstlane(sb + LY::TILE + blk * 1024));
+      const uint32_t rowoff = (uint32_t)(kt * 64 + blk * LY::RPB) * row_bytes;
+      buf_dma16(rk, koff + rowoff, __builtin_amdgcn_readfirstlane(sb + blk * 1024));
+      buf_dma16(rv, voff_l + rowoff, __builtin_amdgcn_readfirstlane(sb + LY::TILE + blk * 1024));
     }
-    if (wave == 0) {  // one gate score per lane
-      const int key = min(kt * 64 + lane, Kb - 1);
-      lds_dma4(s_c + seq0 + key, __builtin_amdgcn_readfirstlane(sb + 2 * LY::TILE));
-    }
+    if (wave == 0)  // one gate score per lane
+      buf_dma4(rsc, (uint32_t)(kt * 64 + lane) * 4u, __builtin_amdgcn_readfirstlane(sb + 2 * LY::TILE));
   };
 
   f32x16 oacc[ND];

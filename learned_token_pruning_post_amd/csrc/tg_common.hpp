@@ -34,6 +34,35 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 family): 48-bit base, stride 0, `bytes` of range.
+// Loads whose byte offset is at or past `bytes` return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16-byte buffer load straight into LDS: lane l reads rsrc at byte offset
+// voff (range-checked, zero past the end) and lands at lds_base + 16*l.
+__device__ __forceinline__ void buf_dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base),
+               "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// 4-byte variant: lane l's dword lands at lds_base + 4*l
+__device__ __forceinline__ void buf_dma4(const i32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base),
+               "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // wait until at most N vector-memory loads of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

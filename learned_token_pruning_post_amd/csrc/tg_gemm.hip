@@ -9,13 +9,14 @@
 // Tiling: BK = 64 (128-byte LDS rows). A workgroup of WN x WM waves owns a
 // BN (features) x BM (tokens) tile; each wave owns (BN/WN) x (BM/WM) made of
 // 32x32x16 bf16 MFMA blocks with fp32 accumulators. Tiles move global -> LDS
-// with gfx950 direct-to-LDS loads (global_load_lds_dwordx4): no register
-// staging, no per-lane predication, NSTAGE k-tiles in flight in an LDS ring,
+// with gfx950 direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no
+// register staging, no per-lane predication (the buffer range check zeroes
+// rows past the end), NSTAGE k-tiles in flight in an LDS ring,
 // one barrier per k-tile. Each 1 KB load instruction fills 8 rows; the lane
 // that lands in 16-byte slot (row, c) fetches logical chunk c ^ ((row>>1)&7),
 // so the MFMA fragment reads (16 consecutive rows per 16-lane phase, same
-// logical chunk) hit distinct banks of the 64-bank LDS. Rows past M or N are clamped to the last valid row (their
-// results are never stored).
+// logical chunk) hit distinct banks of the 64-bank LDS. Rows past M or N
+// read as zeros (their results are never stored).
 //
 // Workgroups are ordered for the 8 XCDs (private L2 each): consecutive
 // hardware workgroup ids rotate over XCDs, so ids are remapped to give each
@@ -77,45 +78,45 @@ __device__ __forceinline__ int qkv_colmap(int lc, int hd) {
   return lc;
 }
 
+// Buffer resources of the operands: W0..W2 (weights; QKV uses all three,
+// SwiGLU two) and X. Each range covers exactly its matrix, so rows past the
+// end read as zeros (their results are never stored).
+struct GemmRsrc {
+  i32x4 w[3];
+  i32x4 x;
+};
+
 // Source of load block `blk` (8 consecutive LDS rows; W rows first, then X
-// rows): base pointer, first row and last valid row. Every block lies inside
-// one matrix (head and chunk sizes are multiples of 8), so all three are
-// wave-uniform; only the clamp to the last valid row is per lane.
+// rows): which resource and its first row. Every block lies inside one
+// matrix (head and chunk sizes are multiples of 8), so both are uniform.
 template <int MODE, int BN, int TN>
-__device__ __forceinline__ void block_src(const GemmParams& p, int n0, int m0, int blk,
-                                          const bf16*& base, int& r0, int& rmax) {
+__device__ __forceinline__ void block_src(const GemmParams& p, int n0, int m0, int blk, int& which,
+                                          int& r0) {
   if (blk >= BN / 8) {
-    base = p.X;
+    which = 3;
     r0 = m0 + (blk - BN / 8) * 8;
-    rmax = p.M - 1;
   } else if (MODE == MODE_SWIGLU) {
     // per wave: subtiles alternate gate (even) / up (odd) over the same 32 features
     const int ln = blk * 8;
     const int wv = ln / TN, j = (ln % TN) >> 5;
-    base = (j & 1) ? p.W1 : p.W0;
+    which = j & 1;
     r0 = (n0 >> 1) + wv * (TN >> 1) + (j >> 1) * 32 + (ln & 31);
-    rmax = p.I - 1;
   } else if (MODE == MODE_QKV) {
-    const int gn0 = n0 + qkv_colmap<TN>(blk * 8, p.hd);
-    const int gn = min(gn0, p.N - 1);
+    const int gn = n0 + qkv_colmap<TN>(blk * 8, p.hd);
     const int nq = p.Hq * p.hd, nk = p.Hkv * p.hd;
     if (gn < nq) {
-      base = p.W0;
-      r0 = gn0;
-      rmax = nq - 1;
+      which = 0;
+      r0 = gn;
     } else if (gn < nq + nk) {
-      base = p.W1;
-      r0 = gn0 - nq;
-      rmax = nk - 1;
+      which = 1;
+      r0 = gn - nq;
     } else {
-      base = p.W2;
-      r0 = gn0 - nq - nk;
-      rmax = nk - 1;
+      which = 2;
+      r0 = gn - nq - nk;  // past the last head: out of range, zeros
     }
   } else {
-    base = p.W0;
+    which = 0;
     r0 = n0 + blk * 8;
-    rmax = p.N - 1;
   }
 }
 
@@ -227,30 +228,40 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   // on two halves of the 256-byte bank space, and swz takes 8 distinct values
   // over the even and over the odd rows of any aligned 16, so the phase hits
   // 16 distinct 16-byte bank groups. The swizzle of row 8*blk + l/8 depends
-  // on the block's parity only, giving two per-lane offsets.
+  // on the block's parity only, giving two per-lane byte offsets.
   const int rl = lane >> 3;
-  const int kc0 = ((lane & 7) ^ (rl >> 1)) * 8;        // even blocks
-  const int kc1 = ((lane & 7) ^ (4 + (rl >> 1))) * 8;  // odd blocks
-  const uint32_t lane_off0 = (uint32_t)(rl * K + kc0) * (uint32_t)sizeof(bf16);
-  const uint32_t lane_off1 = (uint32_t)(rl * K + kc1) * (uint32_t)sizeof(bf16);
+  const uint32_t lane_off0 = (uint32_t)(rl * K + ((lane & 7) ^ (rl >> 1)) * 8) * 2u;
+  const uint32_t lane_off1 = (uint32_t)(rl * K + ((lane & 7) ^ (4 + (rl >> 1))) * 8) * 2u;
+  GemmRsrc rs;
+  {
+    const uint32_t kb = (uint32_t)K * 2u;
+    if (MODE == MODE_SWIGLU) {
+      rs.w[0] = make_rsrc(p.W0, (uint32_t)p.I * kb);
+      rs.w[1] = make_rsrc(p.W1, (uint32_t)p.I * kb);
+      rs.w[2] = rs.w[1];
+    } else if (MODE == MODE_QKV) {
+      rs.w[0] = make_rsrc(p.W0, (uint32_t)(p.Hq * p.hd) * kb);
+      rs.w[1] = make_rsrc(p.W1, (uint32_t)(p.Hkv * p.hd) * kb);
+      rs.w[2] = make_rsrc(p.W2, (uint32_t)(p.Hkv * p.hd) * kb);
+    } else {
+      rs.w[0] = make_rsrc(p.W0, (uint32_t)p.N * kb);
+      rs.w[1] = rs.w[0];
+      rs.w[2] = rs.w[0];
+    }
+    rs.x = make_rsrc(p.X, (uint32_t)p.M * kb);
+  }
+  // one 1 KB block: 8 rows of 128 bytes of k-tile kt
+  auto dma_block = [&](int blk, int kt, uint32_t base_lds) {
+    int which, r0;
+    block_src<MODE, BN, TN>(p, n0, m0, blk, which, r0);
+    const uint32_t voff = ((blk & 1) ? lane_off1 : lane_off0) + ((uint32_t)r0 * (uint32_t)K + kt * 64) * 2u;
+    const i32x4& r = which == 3 ? rs.x : (which == 2 ? rs.w[2] : (which == 1 ? rs.w[1] : rs.w[0]));
+    buf_dma16(r, voff, __builtin_amdgcn_readfirstlane(base_lds + blk * 1024));
+  };
   auto issue = [&](int kt, int st) {
     const uint32_t base_lds = lds0 + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int blk = wave + NW * i;
-      const bf16* base;
-      int r0, rmax;
-      block_src<MODE, BN, TN>(p, n0, m0, blk, base, r0, rmax);
-      const bf16* g;
-      if (r0 + 7 <= rmax) {
-        g = reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base + (size_t)r0 * K + kt * 64) +
-                                          ((blk & 1) ? lane_off1 : lane_off0));
-      } else {  // edge block: clamp each lane's row
-        const int r = min(r0 + rl, rmax);
-        g = base + (size_t)r * K + kt * 64 + ((blk & 1) ? kc1 : kc0);
-      }
-      lds_dma16(g, __builtin_amdgcn_readfirstlane(base_lds + blk * 1024));
-    }
+    for (int i = 0; i < LPW; ++i) dma_block(wave + NW * i, kt, base_lds);
   };
 
   f32x16 acc[SN][SM];
@@ -264,7 +275,6 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KT) issue(s, s);
-
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + NSTAGE - 2 < KT)
       wait_vmcnt<LPW * (NSTAGE - 2)>();
