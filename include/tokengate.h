@@ -74,7 +74,8 @@ int tg_abi_version(void);
  *  W1  [H1, D]    dtype   (nn.Linear layout), b1 [H1] dtype
  *  w2  [H1]       dtype,  b2 [1] dtype (biases may be zeros, never NULL)
  *  s_out [T_in]   fp32
- * bf16 needs D % 64 == 0 and H1 % 32 == 0; fp32 needs D % 4 == 0.
+ * bf16 needs D % 64 == 0 and H1 % 4 == 0 (H1 > 256 needs a workspace for
+ * the partial row sums); fp32 accepts any D and H1 (workspace T_in*H1 fp32).
  * T_in == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 size_t tg_gate_score_workspace_size(int64_t T_in, int D, int H1, tg_dtype dtype);
