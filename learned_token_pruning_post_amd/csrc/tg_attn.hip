@@ -25,7 +25,7 @@
 //  * log2-domain online softmax, t_h*log2(e)/sqrt(d) folded into one
 //    multiply, g_h*log2(e)*s_c[j] added per key; the output accumulator is
 //    rescaled only when a row maximum grows by more than 8 (log2 units);
-//  * the heaviest (last) query tiles are dispatched first.
+//  * heavy (late) and light (early) query tiles are dispatched in pairs.
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
@@ -60,10 +60,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const uint32_t lds0 = lds_addr(attn_smem);
 
   const int tid = threadIdx.x;
+  // Work order: the first half of the grid takes query tiles from the last
+  // (heaviest: most keys under the causal mask) down, the second half from
+  // the first up. Workgroups L and L + grid/2 land on the same XCD and, with
+  // breadth-first dispatch, on the same CU, so every CU gets about n_qt + 1
+  // key tiles of work.
   const int L = blockIdx.x;
   const int per = Hkv * B;
-  const int qt = n_qt - 1 - L / per;
-  const int rem = L - (L / per) * per;
+  const int rank = L / per;
+  const int hn = (n_qt + 1) >> 1;
+  const int qt = rank < hn ? n_qt - 1 - rank : rank - hn;
+  const int rem = L - rank * per;
   const int hk = rem % Hkv, b = rem / Hkv;
   const int seq0 = cu_kept[b];
   const int Kb = cu_kept[b + 1] - seq0;

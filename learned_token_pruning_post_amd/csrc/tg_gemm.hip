@@ -303,28 +303,53 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   // ---------------- epilogues ----------------
   const int ml = lane & 31;
   if (MODE == MODE_PLAIN) {
+    // Stage the wave's fp32 tile in LDS ([token][feature], rows padded by 16
+    // bytes so the 16 rows of a write phase hit distinct banks), then each
+    // lane adds the residual and stores 8 consecutive features (16 bytes):
+    // full 128-byte row segments instead of 32 scattered 16-byte pieces.
+    constexpr int PADW = TN + 4;                    // floats per staged row
+    constexpr int CH = NW * 64 * PADW * 4 <= STAGE * NSTAGE ? 64 : 32;  // tokens per round
+    static_assert(NW * CH * PADW * 4 <= STAGE * NSTAGE, "staging fits in the LDS ring");
+    float* stg = reinterpret_cast<float*>(smem) + wave * CH * PADW;
+    __syncthreads();  // every wave is done with the LDS ring
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int m = m0 + wm * TM + i * 32 + ml;
-      if (m >= p.M) continue;
+    for (int c0 = 0; c0 < SM; c0 += CH / 32) {
 #pragma unroll
-      for (int j = 0; j < SN; ++j)
+      for (int ii = 0; ii < CH / 32; ++ii)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int n = n0 + wn * TN + j * 32 + rq * 8 + half * 4;
-          if (n >= p.N) continue;
-          float v0 = acc[j][i][rq * 4 + 0], v1 = acc[j][i][rq * 4 + 1];
-          float v2 = acc[j][i][rq * 4 + 2], v3 = acc[j][i][rq * 4 + 3];
+        for (int j = 0; j < SN; ++j)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            f32x4 v;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = acc[j][c0 + ii][rq * 4 + t];
+            *reinterpret_cast<f32x4*>(stg + (ii * 32 + ml) * PADW + j * 32 + rq * 8 + half * 4) = v;
+          }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      constexpr int LPR = TN / 8;          // lanes per staged row
+      constexpr int RPI = 64 / LPR;        // rows per pass
+#pragma unroll
+      for (int r0 = 0; r0 < CH; r0 += RPI) {
+        const int r = r0 + lane / LPR, c = (lane % LPR) * 8;
+        const int m = m0 + wm * TM + c0 * 32 + r;
+        const int n = n0 + wn * TN + c;
+        if (m < p.M && n < p.N) {
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + r * PADW + c);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + r * PADW + c + 4);
+          float y[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
           const size_t o = (size_t)m * p.N + n;
           if (p.resid) {
-            const bf16x4 r = *reinterpret_cast<const bf16x4*>(p.resid + o);
-            v0 += bf2f(r[0]);
-            v1 += bf2f(r[1]);
-            v2 += bf2f(r[2]);
-            v3 += bf2f(r[3]);
+            const bf16x8 rr = *reinterpret_cast<const bf16x8*>(p.resid + o);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) y[t] += bf2f(rr[t]);
           }
-          store_bf16x4(p.out + o, v0, v1, v2, v3);
+          bf16x8 w;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) w[t] = f2bf(y[t]);
+          *reinterpret_cast<bf16x8*>(p.out + o) = w;
         }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next round overwrites
     }
   } else if (MODE == MODE_QKV) {
     if (p.hd == 128)
