@@ -24,10 +24,9 @@
 //
 // Epilogues, fused on the accumulators:
 //   PLAIN  : out = acc (+ residual)                         (O and down proj)
-//   QKV    : rotate-half RoPE of q and k, scatter to q / k-cache / v-cache.
-//            A wave's 128 feature rows are whole heads, so each lane holds
-//            both halves (i, i + d/2) of its rotary pairs.
-//   SWIGLU : gate and up rows interleaved per 32 -> silu(g) * u
+//   QKV    : rotate-half RoPE of q and k, scatter to q / k-cache / v-cache
+//            (staged through LDS so rotary pairs and stores are row-wise).
+//   SWIGLU : gate and up rows interleaved per 32 -> silu(g) * u (staged).
 //   SCORE  : scorer logit: sum_n GELU(acc + b1[n]) * w2[n], then sigmoid
 //            (the [tokens, H1] activations never reach memory)
 #include "tg_common.hpp"
@@ -63,21 +62,6 @@ struct GemmParams {
   float* partial;
 };
 
-// QKV feature order inside a block. A lane must hold both halves (i, i+d/2)
-// of its rotary pairs, i.e. the wave's feature rows must contain whole half
-// heads in matching subtiles. With 128-row wave tiles, or d = 64, the natural
-// order does this. With 64-row wave tiles and d = 128, rows are permuted
-// inside each 128-row head by swapping bits 5 and 6 of the local row, so wave
-// 2h+w of a head gets dims [32w, 32w+32) and [64+32w, 96+32w).
-template <int TN>
-__device__ __forceinline__ int qkv_colmap(int lc, int hd) {
-  if (TN == 64 && hd == 128) {
-    const int c = lc & 127;
-    return (lc & ~127) | (((c >> 5) & 1) << 6) | (((c >> 6) & 1) << 5) | (c & 31);
-  }
-  return lc;
-}
-
 // Buffer resources of the operands: W0..W2 (weights; QKV uses all three,
 // SwiGLU two) and X. Each range covers exactly its matrix, so rows past the
 // end read as zeros (their results are never stored).
@@ -102,7 +86,7 @@ __device__ __forceinline__ void block_src(const GemmParams& p, int n0, int m0, i
     which = j & 1;
     r0 = (n0 >> 1) + wv * (TN >> 1) + (j >> 1) * 32 + (ln & 31);
   } else if (MODE == MODE_QKV) {
-    const int gn = n0 + qkv_colmap<TN>(blk * 8, p.hd);
+    const int gn = n0 + blk * 8;
     const int nq = p.Hq * p.hd, nk = p.Hkv * p.hd;
     if (gn < nq) {
       which = 0;
@@ -124,77 +108,6 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
-__device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float c, float d) {
-  bf16x4 v;
-  v[0] = f2bf(a);
-  v[1] = f2bf(b);
-  v[2] = f2bf(c);
-  v[3] = f2bf(d);
-  *reinterpret_cast<bf16x4*>(dst) = v;
-}
-
-// QKV epilogue. Block j pairs with block j + P of the same wave (dims e and
-// e + d/2 of one head, same lane, same register); P = 2 for 128-row wave
-// tiles with d = 128, else 1 (see qkv_colmap for the row order).
-template <int HD, int SN, int SM, int TN, int TM>
-__device__ __forceinline__ void qkv_epilogue(const GemmParams& p, const f32x16 (&acc)[SN][SM],
-                                             int n0, int m0, int wn, int wm, int lane) {
-  constexpr int hd = HD, hh = HD / 2;
-  constexpr int P = (TN == 128 && HD == 128) ? 2 : 1;
-  const int half = lane >> 5, ml = lane & 31;
-#pragma unroll
-  for (int j = 0; j < SN; ++j) {
-    if ((j / P) & 1) continue;  // second halves are handled with their partner
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int gn0 = n0 + qkv_colmap<TN>(wn * TN + j * 32 + rq * 8 + half * 4, HD);
-      const int gh = gn0 / hd;
-      const int dim = gn0 - gh * hd;  // < d/2
-      if (gh >= p.Hq + 2 * p.Hkv) continue;
-      const bool rot = gh < p.Hq + p.Hkv;
-      bf16* dst;
-      int ld;
-      if (gh < p.Hq) {
-        dst = p.q + gh * hd + dim;
-        ld = p.Hq * hd;
-      } else if (gh < p.Hq + p.Hkv) {
-        dst = p.kc + (gh - p.Hq) * hd + dim;
-        ld = p.Hkv * hd;
-      } else {
-        dst = p.vc + (gh - p.Hq - p.Hkv) * hd + dim;
-        ld = p.Hkv * hd;
-      }
-#pragma unroll
-      for (int i = 0; i < SM; ++i) {
-        const int m = m0 + wm * TM + i * 32 + ml;
-        if (m >= p.M) continue;
-        const f32x16& a0 = acc[j][i];
-        const f32x16& a1 = acc[(j + P) % SN][i];
-        float y0[4], y1[4];
-        if (rot) {
-          const f32x4 cs = *reinterpret_cast<const f32x4*>(p.rope + (size_t)m * hd + dim);
-          const f32x4 sn = *reinterpret_cast<const f32x4*>(p.rope + (size_t)m * hd + hh + dim);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float x0 = a0[rq * 4 + t], x1 = a1[rq * 4 + t];
-            y0[t] = x0 * cs[t] - x1 * sn[t];
-            y1[t] = x1 * cs[t] + x0 * sn[t];
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            y0[t] = a0[rq * 4 + t];
-            y1[t] = a1[rq * 4 + t];
-          }
-        }
-        bf16* row = dst + (size_t)m * ld;
-        store_bf16x4(row, y0[0], y0[1], y0[2], y0[3]);
-        store_bf16x4(row + hh, y1[0], y1[1], y1[2], y1[3]);
-      }
-    }
-  }
-}
-
 template <int MODE, int BN, int BM, int WN, int WM, int NSTAGE>
 __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, int NB, int MB) {
   constexpr int NW = WN * WM;
@@ -204,7 +117,6 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   constexpr int NBLK = (BN + BM) / 8;         // 1 KB load blocks per stage
   constexpr int LPW = NBLK / NW;              // load instructions per wave per stage
   static_assert(NBLK % NW == 0, "load blocks must split evenly over waves");
-  static_assert(MODE != MODE_QKV || TN == 128 || TN == 64, "QKV wave tiles are 64 or 128 rows");
   static_assert(MODE != MODE_SWIGLU || SN % 2 == 0, "SwiGLU pairs gate/up subtiles");
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -351,30 +263,102 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next round overwrites
     }
-  } else if (MODE == MODE_QKV) {
-    if (p.hd == 128)
-      qkv_epilogue<128, SN, SM, TN, TM>(p, acc, n0, m0, wn, wm, lane);
-    else
-      qkv_epilogue<64, SN, SM, TN, TM>(p, acc, n0, m0, wn, wm, lane);
-  } else if (MODE == MODE_SWIGLU) {
+  } else if (MODE == MODE_QKV || MODE == MODE_SWIGLU) {
+    // Stage 64 tokens at a time in LDS as fp32 [token][feature] over the
+    // whole workgroup tile, then let every thread finish 8-feature chunks of
+    // a token row: RoPE pairs (i, i + d/2) are both in the tile (heads never
+    // straddle a 256-feature tile), the RoPE table is read in 32-byte pieces
+    // along the row, and every store is 16 bytes of a contiguous row segment.
+    // Inside a staged row the 4-feature halves of each 8-feature chunk are
+    // split into two runs, so both the f32x4 writes (one token per lane) and
+    // the f32x4 reads (consecutive chunks per lane) are conflict-free.
+    constexpr int W = MODE == MODE_QKV ? BN : BN / 2;  // staged features per token
+    constexpr int RW = W + 4;                           // floats per staged row
+    constexpr int CHT = 64;                             // tokens per round
+    static_assert(CHT * RW * 4 <= STAGE * NSTAGE, "staging fits in the LDS ring");
+    static_assert(BM % CHT == 0 && TM % 32 == 0, "token rounds cover whole MFMA blocks");
+    float* stg = reinterpret_cast<float*>(smem);
+    auto fpos = [](int f) { return ((f >> 2) & 1) * (W / 2) + (f >> 3) * 4 + (f & 3); };
+    constexpr int CPR = W / 8;  // chunks per staged row
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int m = m0 + wm * TM + i * 32 + ml;
-      if (m >= p.M) continue;
+    for (int c0 = 0; c0 < BM; c0 += CHT) {
+      __syncthreads();  // the LDS ring (or the previous round) is no longer read
 #pragma unroll
-      for (int jj = 0; jj < SN / 2; ++jj)
+      for (int i = 0; i < SM; ++i) {
+        const int tl = wm * TM + i * 32;  // first tile-local token of block i
+        if (tl < c0 || tl >= c0 + CHT) continue;
+        float* row = stg + (tl - c0 + ml) * RW;
+        if (MODE == MODE_QKV) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int idx = (n0 >> 1) + wn * (TN >> 1) + jj * 32 + rq * 8 + half * 4;
-          if (idx >= p.I) continue;
-          float y[4];
+          for (int j = 0; j < SN; ++j)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float gt = acc[2 * jj][i][rq * 4 + t], up = acc[2 * jj + 1][i][rq * 4 + t];
-            y[t] = gt / (1.0f + __expf(-gt)) * up;
-          }
-          store_bf16x4(p.act + (size_t)m * p.I + idx, y[0], y[1], y[2], y[3]);
+            for (int rq = 0; rq < 4; ++rq) {
+              const int f = wn * TN + j * 32 + rq * 8 + half * 4;
+              *reinterpret_cast<f32x4*>(row + fpos(f)) =
+                  f32x4{acc[j][i][rq * 4], acc[j][i][rq * 4 + 1], acc[j][i][rq * 4 + 2], acc[j][i][rq * 4 + 3]};
+            }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < SN / 2; ++jj)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              f32x4 y;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float gt = acc[2 * jj][i][rq * 4 + t], up = acc[2 * jj + 1][i][rq * 4 + t];
+                y[t] = gt / (1.0f + __expf(-gt)) * up;
+              }
+              *reinterpret_cast<f32x4*>(row + fpos(wn * (TN / 2) + jj * 32 + rq * 8 + half * 4)) = y;
+            }
         }
+      }
+      __syncthreads();
+      for (int task = tid; task < CHT * CPR; task += NW * 64) {
+        const int r = task / CPR, f = (task % CPR) * 8;
+        const int m = m0 + c0 + r;
+        if (m >= p.M) continue;
+        const float* row = stg + r * RW;
+        const f32x4 xa = *reinterpret_cast<const f32x4*>(row + fpos(f));
+        const f32x4 xb = *reinterpret_cast<const f32x4*>(row + fpos(f + 4));
+        float y[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+        bf16* dst;
+        if (MODE == MODE_QKV) {
+          const int hd = p.hd, hh = hd >> 1;
+          const int gn = n0 + f;
+          const int gh = gn / hd, dim = gn - gh * hd;
+          if (gh >= p.Hq + 2 * p.Hkv) continue;
+          if (gh < p.Hq + p.Hkv) {
+            const bool lo = dim < hh;
+            const int fp = lo ? f + hh : f - hh;  // partner chunk, same head
+            const f32x4 pa = *reinterpret_cast<const f32x4*>(row + fpos(fp));
+            const f32x4 pb = *reinterpret_cast<const f32x4*>(row + fpos(fp + 4));
+            const float z[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+            const float* cs = p.rope + (size_t)m * hd + (lo ? dim : dim - hh);
+            const f32x4 c0v = *reinterpret_cast<const f32x4*>(cs);
+            const f32x4 c1v = *reinterpret_cast<const f32x4*>(cs + 4);
+            const f32x4 s0v = *reinterpret_cast<const f32x4*>(cs + hh);
+            const f32x4 s1v = *reinterpret_cast<const f32x4*>(cs + hh + 4);
+            const float c[8] = {c0v[0], c0v[1], c0v[2], c0v[3], c1v[0], c1v[1], c1v[2], c1v[3]};
+            const float sn[8] = {s0v[0], s0v[1], s0v[2], s0v[3], s1v[0], s1v[1], s1v[2], s1v[3]};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) y[t] = lo ? y[t] * c[t] - z[t] * sn[t] : y[t] * c[t] + z[t] * sn[t];
+          }
+          if (gh < p.Hq)
+            dst = p.q + (size_t)m * p.Hq * hd + gh * hd + dim;
+          else if (gh < p.Hq + p.Hkv)
+            dst = p.kc + (size_t)m * p.Hkv * hd + (gh - p.Hq) * hd + dim;
+          else
+            dst = p.vc + (size_t)m * p.Hkv * hd + (gh - p.Hq - p.Hkv) * hd + dim;
+        } else {
+          const int idx = (n0 >> 1) + f;
+          if (idx >= p.I) continue;
+          dst = p.act + (size_t)m * p.I + idx;
+        }
+        bf16x8 w;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w[t] = f2bf(y[t]);
+        *reinterpret_cast<bf16x8*>(dst) = w;
+      }
     }
   } else {  // SCORE
     float part[SM];
