@@ -430,13 +430,14 @@ static hipError_t launch_gemm(const GemmParams& p, int Ncols, hipStream_t stream
 
 // Tile choice (measured on MI355X at M = 4096 tokens): 8 waves per workgroup
 // (two per SIMD, so one wave's MFMAs cover the other's LDS and barrier
-// waits). 256 x 256 tiles (64 x 128 per wave, 2-stage ring) for the wide
-// gate/up projection; 256 x 128 tiles (64 x 64 per wave, 3-stage ring) when
-// 256 x 256 would leave CUs idle.
+// waits). 256 x 256 tiles (64 x 128 per wave, 2-stage ring) whenever they
+// give every CU at least one tile (gate/up, QKV); 256 x 128 tiles (64 x 64
+// per wave, 3-stage ring) when 256 x 256 would leave CUs idle (O, down).
+// A 32-wide k-tile with a deeper ring measured slower for every shape.
 template <int MODE>
 static hipError_t launch_auto(const GemmParams& p, int Ncols, hipStream_t stream) {
   const long tA = (long)((Ncols + 255) / 256) * ((p.M + 255) / 256);
-  if (tA >= 512) return launch_gemm<MODE, 256, 256, 4, 2, 2>(p, Ncols, stream);
+  if (tA >= 256) return launch_gemm<MODE, 256, 256, 4, 2, 2>(p, Ncols, stream);
   return launch_gemm<MODE, 256, 128, 4, 2, 3>(p, Ncols, stream);
 }
 
