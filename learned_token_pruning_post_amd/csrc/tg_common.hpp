@@ -56,6 +56,15 @@ __device__ __forceinline__ void buf_dma16(const i32x4& rsrc, uint32_t voff, uint
                : "memory", "m0");
 }
 
+// Same with a wave-uniform byte offset in the instruction's scalar offset
+// (added to the address; the range check sees the per-lane offset).
+__device__ __forceinline__ void buf_dma16_soff(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                               uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_base),
+               "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // 4-byte variant: lane l's dword lands at lds_base + 4*l
 __device__ __forceinline__ void buf_dma4(const i32x4& rsrc, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base),

@@ -162,18 +162,25 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     }
     rs.x = make_rsrc(p.X, (uint32_t)p.M * kb);
   }
-  // one 1 KB block: 8 rows of 128 bytes of k-tile kt
-  auto dma_block = [&](int blk, int kt, uint32_t base_lds) {
+  // This wave's load blocks are blk = wave + NW*i. Their source (resource and
+  // first row) does not depend on the k-tile, so it is resolved once; the
+  // k-tile's byte offset goes in the instruction's scalar offset.
+  i32x4 brs[LPW];
+  uint32_t bvoff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int blk = wave + NW * i;
     int which, r0;
     block_src<MODE, BN, TN>(p, n0, m0, blk, which, r0);
-    const uint32_t voff = ((blk & 1) ? lane_off1 : lane_off0) + ((uint32_t)r0 * (uint32_t)K + kt * 64) * 2u;
-    const i32x4& r = which == 3 ? rs.x : (which == 2 ? rs.w[2] : (which == 1 ? rs.w[1] : rs.w[0]));
-    buf_dma16(r, voff, __builtin_amdgcn_readfirstlane(base_lds + blk * 1024));
-  };
+    brs[i] = which == 3 ? rs.x : (which == 2 ? rs.w[2] : (which == 1 ? rs.w[1] : rs.w[0]));
+    bvoff[i] = ((blk & 1) ? lane_off1 : lane_off0) + (uint32_t)r0 * (uint32_t)K * 2u;
+  }
   auto issue = [&](int kt, int st) {
-    const uint32_t base_lds = lds0 + st * STAGE;
+    const uint32_t base_lds = lds0 + st * STAGE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_block(wave + NW * i, kt, base_lds);
+    for (int i = 0; i < LPW; ++i)
+      buf_dma16_soff(brs[i], bvoff[i], (uint32_t)kt * 128u,
+                     __builtin_amdgcn_readfirstlane(base_lds + NW * i * 1024));
   };
 
   f32x16 acc[SN][SM];
@@ -197,19 +204,40 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     const unsigned char* st = smem + (kt % NSTAGE) * STAGE;
     const unsigned char* wb = st + (wn * TN + (lane & 31)) * 128;
     const unsigned char* xb = st + (BN + wm * TM + (lane & 31)) * 128;
+    // fragments of k-step ks+1 are read while the MFMAs of ks run
+    bf16x8 wf[2][SN], xf[2][SM];
+    auto frag = [&](int ks, int b) {
+      const int ch = ((ks * 2 + half) ^ rsw) << 4;
+#pragma unroll
+      for (int j = 0; j < SN; ++j) wf[b][j] = *reinterpret_cast<const bf16x8*>(wb + j * 32 * 128 + ch);
+#pragma unroll
+      for (int i = 0; i < SM; ++i) xf[b][i] = *reinterpret_cast<const bf16x8*>(xb + i * 32 * 128 + ch);
+    };
+    frag(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ((ks * 2 + half) ^ rsw) << 4;
-      bf16x8 wf[SN], xf[SM];
-#pragma unroll
-      for (int j = 0; j < SN; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(wb + j * 32 * 128 + ch);
-#pragma unroll
-      for (int i = 0; i < SM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>(xb + i * 32 * 128 + ch);
+      if (ks < 3) frag(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int j = 0; j < SN; ++j)
 #pragma unroll
-        for (int i = 0; i < SM; ++i) acc[j][i] = mfma32(wf[j], xf[i], acc[j][i]);
+        for (int i = 0; i < SM; ++i) acc[j][i] = mfma32(wf[ks & 1][j], xf[ks & 1][i], acc[j][i]);
     }
+    // Issue order (the scheduler would otherwise put each step's reads after
+    // the previous step's MFMAs): k-step 0 reads, then each later read
+    // between the MFMAs of the step before, so LDS latency hides under them.
+    constexpr int NR = SN + SM, NMF = SN * SM;
+    static_assert(NR <= NMF, "one read per MFMA slot");
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
   }
 
   // ---------------- epilogues ----------------
