@@ -7,21 +7,14 @@
 //
 // Algorithm: scores map to order-preserving uint32 keys. A range search
 // narrows [kmin, kmax] to the threshold key T with histogram passes whose bin
-// width is a power of two sized so at most 2048 bins span the live range
-// (the range, not the fixed top byte: sigmoid scores share their top bits, a
-// fixed-digit radix would pile every key into one or two bins). Each pass
-// shrinks the range by >= 2^10, so three passes resolve any 32-bit key. A
-// final pass keeps forced tokens, keys > T, and the first `need` keys == T in
-// index order (block-wide exclusive scans give each thread its share and its
-// output offset).
+// width is a power of two sized so the bins span the live range (the range,
+// not the fixed top byte: sigmoid scores share their top bits, a fixed-digit
+// radix would pile every key into one or two bins). A final pass keeps forced
+// tokens, keys > T, and the first `need` keys == T in index order.
 //
-// Sequences of up to SEL_LDS_MAX tokens keep their keys in LDS after one load
-// pass (forced tokens carry a flag bit in a separate bitmap), so the
-// histogram and emit passes never touch global memory. The key array is
-// padded by one word per 32 so that the blocked per-thread reads of the emit
-// pass (thread t reads 32t..32t+31) fall on distinct banks. Longer sequences
-// stream their scores from global memory with 16 independent loads in flight
-// per thread.
+// Sequences of up to SEL_LDS_MAX tokens keep their keys in LDS (select_lds).
+// Longer sequences stream their scores from global memory on every pass
+// (select_sequence) with 16 independent loads in flight per thread.
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
@@ -182,7 +175,7 @@ struct KeySrc {
 };
 
 template <bool IN_LDS>
-__device__ void select_sequence(const float* __restrict__ sp, const uint8_t* __restrict__ mp,
+__device__ __forceinline__ void select_sequence(const float* __restrict__ sp, const uint8_t* __restrict__ mp,
                                 int n, int K, int in0, int32_t* __restrict__ kp,
                                 int32_t* __restrict__ status_b, uint32_t* keys, uint32_t* fbits,
                                 uint32_t* hist, int* shi, uint32_t* shu, int* found) {
@@ -349,16 +342,350 @@ __device__ void select_sequence(const float* __restrict__ sp, const uint8_t* __r
   });
 }
 
+// ---------------------------------------------------------------------------
+// LDS path (n <= SEL_LDS_MAX): keys stay in LDS after one vectorised load.
+//  * load: every thread issues all of its 16-byte score loads and 4-byte
+//    mask loads before using any; the forced bitmap words are assembled
+//    with lane shuffles (8 lanes = 32 tokens), no atomics;
+//  * one fused reduction of (forced count, NaN flag, candidate min, max);
+//  * range passes with SEL_LDS_BINS = 4096 power-of-two bins (the span
+//    shrinks by 2^12 per pass). Once the live range holds at most SEL_LIST
+//    candidates, the pass that scans all keys also gathers those into a
+//    list, and the remaining passes read only the list;
+//  * emit: wave w owns tokens [w*2048, w*2048 + 2048), 4 per lane per round;
+//    wave scans give each lane its output slot (and, when only part of the
+//    threshold ties is kept, its tie rank), so kept indices are written in
+//    ascending order without a block-wide scan over tokens.
+// ---------------------------------------------------------------------------
+constexpr int SEL_LDS_BINS = 4096;
+constexpr int SEL_LIST = 2048;
+constexpr int SEL_SPAN = SEL_LDS_MAX / SEL_WAVES;  // tokens per wave in the emit pass
+
+// Wave-wide inclusive scans on DPP lane moves (plain VALU: no LDS round trip
+// as with ds_bpermute): row_shr 1, 2, 4, 8 scan each 16-lane row, then
+// row_bcast 15 and 31 carry the row totals upward. `id` is the identity: it
+// fills lanes whose source is outside the row or whose row is masked off.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x, uint32_t id, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  return (int)wave_scan_u32((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
+__device__ __forceinline__ void select_lds(const float* __restrict__ sp, const uint8_t* __restrict__ mp, int n,
+                           int K, int in0, int32_t* __restrict__ kp, int32_t* __restrict__ status_b,
+                           uint32_t* keys, uint32_t* fbits, uint32_t* hist, int* red,
+                           uint32_t* list) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  constexpr int NG = SEL_LDS_MAX / 4 / SEL_THREADS;  // 4-token groups per thread
+
+  // ---- load ----
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  int nf = 0, nan_seen = 0;
+  auto take_key = [&](float x, bool f) -> uint32_t {
+    bool isn;
+    const uint32_t k = score_key(x, isn);
+    nan_seen |= isn;
+    if (f) {
+      ++nf;
+    } else {
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+    return k;
+  };
+  const bool vec = (reinterpret_cast<uintptr_t>(sp) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(mp) & 3u) == 0;
+  if (vec) {
+    // group g = u*1024 + tid holds tokens 4g..4g+3; lanes 8c..8c+7 of a wave
+    // cover one bitmap word. Every thread runs all NG rounds so that all
+    // lanes take part in the shuffles.
+    f32x4 xv[NG];
+    uint32_t mv[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int i = 4 * (u * SEL_THREADS + tid);
+      mv[u] = 0u;
+      if (i + 3 < n) {
+        xv[u] = *reinterpret_cast<const f32x4*>(sp + i);
+        if (mp) mv[u] = *reinterpret_cast<const uint32_t*>(mp + i);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[u][e] = i + e < n ? sp[i + e] : 0.f;
+          if (mp && i + e < n && mp[i + e]) mv[u] |= 1u << (8 * e);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int i = 4 * (u * SEL_THREADS + tid);
+      uint32_t nib = 0u;
+      u32x4 kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool f = ((mv[u] >> (8 * e)) & 0xffu) != 0;
+        kv[e] = 0u;
+        if (i + e < n) {
+          kv[e] = take_key(xv[u][e], f);
+          nib |= (uint32_t)f << e;
+        }
+      }
+      if (i < n) *reinterpret_cast<u32x4*>(keys + i) = kv;
+      // OR of the 8 lanes of a word lands in lane 8c+7 (row shifts 1, 2, 4
+      // reach exactly lanes 8c..8c+7 from there)
+      uint32_t word = nib << (4 * (lane & 7));
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x111, 0xf, 0xf, false);
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x112, 0xf, 0xf, false);
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x114, 0xf, 0xf, false);
+      const int iw = i - 28;  // first token of the word
+      if ((lane & 7) == 7 && iw < n) fbits[iw >> 5] = word;
+    }
+  } else {
+    for (int i = tid; i < ((n + 63) & ~63); i += SEL_THREADS) {
+      bool f = false;
+      if (i < n) {
+        f = mp && mp[i];
+        keys[i] = take_key(sp[i], f);
+      }
+      const uint64_t bal = __ballot(f);
+      if (lane == 0) {
+        fbits[i >> 5] = (uint32_t)bal;
+        fbits[(i >> 5) + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+  }
+  // ---- fused reduction ----
+  nf = lane63(wave_incl_scan(nf));
+  nan_seen = lane63(wave_incl_scan(nan_seen));
+  kmin = (uint32_t)lane63((int)wave_scan_u32(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
+  kmax = (uint32_t)lane63((int)wave_scan_u32(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }));
+  if (lane == 0) {
+    red[4 * w + 0] = nf;
+    red[4 * w + 1] = nan_seen;
+    red[4 * w + 2] = (int)kmin;
+    red[4 * w + 3] = (int)kmax;
+  }
+  __syncthreads();
+  nf = 0;
+  nan_seen = 0;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int v = 0; v < SEL_WAVES; ++v) {
+    nf += red[4 * v];
+    nan_seen |= red[4 * v + 1];
+    kmin = min(kmin, (uint32_t)red[4 * v + 2]);
+    kmax = max(kmax, (uint32_t)red[4 * v + 3]);
+  }
+  const int flags = (nan_seen ? 4 : 0) | (K > n ? 2 : 0) | (nf > K ? 1 : 0);
+  if (tid == 0 && status_b) *status_b = flags;
+  if (flags & 3) {
+    for (int i = tid; i < K; i += SEL_THREADS) kp[i] = -1;
+    return;
+  }
+  const int C = n - nf;  // candidates
+  const int r = K - nf;  // slots for candidates
+  uint32_t T;
+  int needT;
+  if (r == 0) {
+    T = 0xffffffffu;  // no key reaches it (largest real key is +inf's)
+    needT = 0;
+  } else if (r == C) {
+    T = 0u;
+    needT = C;
+  } else {
+    uint32_t lo = kmin, hi = kmax;
+    int need = r;
+    int in_range = C;       // candidates with lo <= key <= hi
+    bool use_list = false;  // candidates in range are all in list[0, nlist)
+    int nlist = 0;
+    T = lo;
+    needT = need;
+    for (int iter = 0; iter < 4; ++iter) {
+      if (lo == hi) {
+        T = lo;
+        needT = need;
+        break;
+      }
+      const uint32_t span = hi - lo;
+      const int bits = 32 - __clz(span);
+      const int shift = bits > 12 ? bits - 12 : 0;
+      const int nb = (int)(span >> shift) + 1;
+      const bool build = !use_list && in_range <= SEL_LIST;
+      __syncthreads();  // the previous pass's readers of hist / red are done
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hist[4 * tid + e] = 0u;
+      if (tid == 0) red[130] = 0;
+      __syncthreads();
+      if (use_list) {
+        for (int j = tid; j < nlist; j += SEL_THREADS) {
+          const uint32_t k = list[j];
+          if (k - lo <= span) atomicAdd(&hist[(k - lo) >> shift], 1u);
+        }
+      } else {
+        for (int g = tid; g < (n + 3) / 4; g += SEL_THREADS) {
+          const int i = 4 * g;
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(keys + i);
+          const uint32_t nib = fbits[i >> 5] >> (i & 31);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t k = kv[e];
+            const bool inr = i + e < n && !((nib >> e) & 1u) && k - lo <= span;
+            if (inr) atomicAdd(&hist[(k - lo) >> shift], 1u);
+            if (build) {  // wave-aggregated append
+              const uint64_t m = __ballot(inr);
+              int base = 0;
+              if (lane == 0 && m) base = atomicAdd(&red[130], __popcll(m));
+              base = __builtin_amdgcn_readlane(base, 0);
+              if (inr) list[base + __popcll(m & below)] = k;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (build) {
+        nlist = red[130];
+        use_list = true;
+      }
+      // thread t owns bins 4t'..4t'+3, t' = 1023 - t: an inclusive scan in
+      // thread order counts the keys in every bin >= 4t'
+      const int tb = 4 * (SEL_THREADS - 1 - tid);
+      int h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = tb + e < nb ? (int)hist[tb + e] : 0;
+      const int mine = h[0] + h[1] + h[2] + h[3];
+      int incl = wave_incl_scan(mine);
+      if (lane == 63) red[64 + w] = incl;
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < SEL_WAVES; ++v) incl += v < w ? red[64 + v] : 0;
+      int above = incl - mine;  // keys in bins above tb + 3
+      if (above < need && incl >= need) {
+        int bstar = tb, cnt = h[0];
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          if (above + h[e] >= need) {
+            bstar = tb + e;
+            cnt = h[e];
+            break;
+          }
+          above += h[e];
+        }
+        red[128] = bstar;
+        red[129] = above;
+        red[131] = cnt;
+      }
+      __syncthreads();
+      const int bstar = red[128];
+      need -= red[129];
+      in_range = red[131];
+      const uint64_t nlo = (uint64_t)lo + ((uint64_t)bstar << shift);
+      const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+      lo = (uint32_t)nlo;
+      hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+      if (shift == 0) {
+        T = lo;
+        needT = need;
+        break;
+      }
+    }
+  }
+
+  // ---- emit ----
+  // lane l of round q covers tokens w0 + 256q + 4l .. +3
+  const int w0 = w * SEL_SPAN;
+  auto flags4 = [&](int i, uint32_t& sure, uint32_t& tie) {
+    sure = 0u;
+    tie = 0u;
+    if (i >= n) return;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(keys + i);
+    const uint32_t nib = fbits[i >> 5] >> (i & 31);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = i + e < n, f = (nib >> e) & 1u;
+      sure |= (uint32_t)(in && (f || kv[e] > T)) << e;
+      tie |= (uint32_t)(in && !f && kv[e] == T) << e;
+    }
+  };
+  int sure_w = 0, ties_w = 0;
+  for (int q = 0; q < SEL_SPAN / 256; ++q) {
+    uint32_t su, ti;
+    flags4(w0 + 256 * q + 4 * lane, su, ti);
+    sure_w += __popc(su);
+    ties_w += __popc(ti);
+  }
+  sure_w = lane63(wave_incl_scan(sure_w));
+  ties_w = lane63(wave_incl_scan(ties_w));
+  __syncthreads();  // red is free
+  if (lane == 0) {
+    red[2 * w] = sure_w;
+    red[2 * w + 1] = ties_w;
+  }
+  __syncthreads();
+  int off = 0, tie_before = 0;
+#pragma unroll
+  for (int v = 0; v < SEL_WAVES; ++v) {
+    if (v < w) {
+      const int s_v = red[2 * v], t_v = red[2 * v + 1];
+      off += s_v + min(max(needT - tie_before, 0), t_v);
+      tie_before += t_v;
+    }
+  }
+  const int take_w = min(max(needT - tie_before, 0), ties_w);
+  const bool all_ties = take_w == ties_w;  // else a prefix of this wave's ties (in index order)
+  int tie_run = 0;
+  for (int q = 0; q < SEL_SPAN / 256; ++q) {
+    const int i = w0 + 256 * q + 4 * lane;
+    uint32_t su, ti;
+    flags4(i, su, ti);
+    uint32_t keep = su | (all_ties ? ti : 0u);
+    if (!all_ties) {
+      const int tc = __popc(ti);
+      const int t_incl = wave_incl_scan(tc);
+      int rank = tie_run + t_incl - tc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((ti >> e) & 1u) {
+          if (rank < take_w) keep |= 1u << e;
+          ++rank;
+        }
+      tie_run += lane63(t_incl);
+    }
+    const int kc = __popc(keep);
+    const int k_incl = wave_incl_scan(kc);
+    int pos = off + k_incl - kc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((keep >> e) & 1u) {
+        if (pos < K) kp[pos] = in0 + i + e;  // pos < K always holds; the guard keeps a logic slip in bounds
+        ++pos;
+      }
+    off += lane63(k_incl);
+  }
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
     const float* __restrict__ s, const uint8_t* __restrict__ mask,
     const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
     int32_t* __restrict__ kept, int32_t* __restrict__ status) {
   extern __shared__ __attribute__((aligned(16))) uint32_t sel_smem[];
-  __shared__ uint32_t hist[SEL_BINS];
+  __shared__ uint32_t hist[SEL_LDS_BINS];
   __shared__ int shi[SEL_WAVES];
   __shared__ uint32_t shu[SEL_WAVES];
   __shared__ int found[2];
-  __shared__ uint32_t fbits[SEL_LDS_MAX / 32];
+  __shared__ int red[132];
+  __shared__ uint32_t list[SEL_LIST];
+  __shared__ uint32_t fbits[SEL_LDS_MAX / 32 + 2];
 
   const int b = blockIdx.x;
   const int in0 = cu_in[b];
@@ -369,8 +696,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
   const uint8_t* mp = mask ? mask + in0 : nullptr;
   int32_t* st = status ? status + b : nullptr;
   if (n <= SEL_LDS_MAX)
-    select_sequence<true>(sp, mp, n, K, in0, kept + out0, st, sel_smem, fbits, hist, shi, shu,
-                          found);
+    select_lds(sp, mp, n, K, in0, kept + out0, st, sel_smem, fbits, hist, red, list);
   else
     select_sequence<false>(sp, mp, n, K, in0, kept + out0, st, sel_smem, fbits, hist, shi, shu,
                            found);
@@ -380,7 +706,7 @@ hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t
                               const int32_t* cu_kept, int B, int32_t* kept, int32_t* status,
                               hipStream_t stream) {
   if (B <= 0) return hipSuccess;
-  constexpr size_t lds = (size_t)SEL_KEY_WORDS * sizeof(uint32_t);
+  constexpr size_t lds = (size_t)SEL_LDS_MAX * sizeof(uint32_t);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
