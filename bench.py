@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--n", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device-to-device copy of BYTES (counter calibration "
+                         "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only the whole step (no per-kernel events)")
     return ap.parse_args()
@@ -119,6 +122,21 @@ def cpu_baseline(w, dw_host_gate, host_layer):
     }
 
 
+def measured_traffic(stage, workload_name):
+    """HBM bytes per launch of `stage` from the committed FETCH_SIZE / WRITE_SIZE summary
+    (profiles/traffic_<stage>_<workload>.json), or None when there is none or the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (stage, workload_name))
+    if not os.path.exists(path):
+        return None
+    from learned_token_pruning_post_amd.rocprof_summary import source_hash
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return rec["traffic_bytes"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -165,6 +183,13 @@ def main():
                                x_out=gp.x, kcache=gp.kcache[l], vcache=gp.vcache[l], ws=gp.ws,
                                events=ev.sub(base + 4 + l * (tg.LAYER_STAGES + 1), tg.LAYER_STAGES + 1))
 
+    if args.calib_copy > 0:
+        src = torch.empty(args.calib_copy, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -265,15 +290,16 @@ def main():
                                  "frac_hbm": round(sc_bytes / (sc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         dom = max(kern, key=lambda n: kern[n]["ms_per_step"])
         de = kern[dom]
+        traffic = measured_traffic(dom, w.name)
         if dom in kflop:
             out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": de["tflops"],
                                "peak": PEAK_BF16_TFLOPS if dm.dtype == "bf16" else PEAK_F32_TFLOPS,
-                               "unit": "TFLOP/s", "frac": de["frac_mfma_peak"], "traffic": None,
+                               "unit": "TFLOP/s", "frac": de["frac_mfma_peak"], "traffic": traffic,
                                "work_per_launch": kflop[dom]}
         else:
             out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": de["gbs"],
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": de["frac_hbm"],
-                               "traffic": None, "work_per_launch": kbytes[dom]}
+                               "traffic": traffic, "work_per_launch": kbytes[dom]}
         out["kernels"] = kern
     if want_cpu:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

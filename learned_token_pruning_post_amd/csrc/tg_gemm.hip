@@ -18,9 +18,13 @@
 // logical chunk) hit distinct banks of the 64-bank LDS. Rows past M or N
 // read as zeros (their results are never stored).
 //
-// Workgroups are ordered for the 8 XCDs (private L2 each): consecutive
-// hardware workgroup ids rotate over XCDs, so ids are remapped to give each
-// XCD a contiguous run of tiles, token-block fastest, which share weight tiles.
+// Workgroups are ordered for the 8 XCDs (private L2 each): hardware id L
+// runs on XCD L % 8, in order of L / 8. The token-block x weight-block tile
+// grid is cut into 8 rectangles, one per XCD, and each XCD walks its
+// rectangle in groups of 4 token blocks, so the ~32 tiles an XCD runs at
+// once cover about 4 token blocks x 8 weight blocks: 12 row blocks of operand
+// data per round through its L2 instead of 2 + 16 (token-block-fastest
+// order).
 //
 // Epilogues, fused on the accumulators:
 //   PLAIN  : out = acc (+ residual)                         (O and down proj)
@@ -122,11 +126,29 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
-  // XCD-aware tile order: hardware id L runs on XCD L % 8
-  const int ntile = NB * MB;
-  int tile = blockIdx.x;
-  if ((ntile & 7) == 0) tile = (blockIdx.x & 7) * (ntile >> 3) + (blockIdx.x >> 3);
-  const int mb = tile % MB, nb = tile / MB;
+  // XCD-aware tile order (see the file header)
+  int mb, nb;
+  {
+    const int L = blockIdx.x;
+    int RX = 0;  // XCD rectangles along the token blocks (8 / RX along weight blocks)
+    if (((NB * MB) & 7) == 0) {
+      if (MB % 4 == 0 && NB % 2 == 0) RX = 4;
+      else if (MB % 2 == 0 && NB % 4 == 0) RX = 2;
+      else if (MB % 8 == 0) RX = 8;
+      else if (NB % 8 == 0) RX = 1;
+    }
+    if (RX) {
+      const int xcd = L & 7, j = L >> 3;
+      const int mbr = MB / RX, nbr = NB / (8 / RX);
+      const int G = (mbr & 3) == 0 ? 4 : ((mbr & 1) == 0 ? 2 : 1);
+      const int gi = j / (G * nbr), jj = j - gi * (G * nbr);
+      mb = (xcd % RX) * mbr + gi * G + jj % G;
+      nb = (xcd / RX) * nbr + jj / G;
+    } else {
+      mb = L % MB;
+      nb = L / MB;
+    }
+  }
   const int n0 = nb * BN, m0 = mb * BM;
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -1,0 +1,144 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    python -m learned_token_pruning_post_amd.rocprof_summary stats STATS_CSV --cmd "..." > out.md
+        kernel table (calls, average / total duration) from a --kernel-trace --stats run
+
+    python -m learned_token_pruning_post_amd.rocprof_summary traffic \\
+        --fetch FETCH_CSV --write WRITE_CSV --kernel SUBSTR --copy-bytes N --cmd "..." --out PREFIX
+        HBM traffic of one kernel from two --pmc runs (FETCH_SIZE, then WRITE_SIZE), each
+        scaled by what the same counter reads for the plain device copy of N bytes that
+        `bench.py --calib-copy` issues in the same process; writes PREFIX.json (read by
+        bench.py) and PREFIX.md
+
+The JSON carries a hash of the kernel sources (csrc/ and include/); bench.py reports the
+traffic only while the sources still hash the same, i.e. while the counters describe the
+kernels being timed.
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources and the C header, in a fixed order."""
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "tokengate.h")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find_csv(path, suffix):
+    if os.path.isdir(path):
+        hits = glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True)
+        if not hits:
+            raise SystemExit("no *%s under %s" % (suffix, path))
+        return hits[0]
+    return path
+
+
+def stats_table(stats_csv: str, top: int = 20) -> str:
+    rows = _rows(_find_csv(stats_csv, "kernel_stats.csv"))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = ["| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows[:top]:
+        name = r["Name"].replace("|", "\\|")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        out.append("| `%s` | %s | %.2f | %.1f | %.1f |" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3,
+            100.0 * float(r["TotalDurationNs"]) / tot))
+    return "\n".join(out)
+
+
+def _per_dispatch(pmc_csv, counter, match, largest=False):
+    """Average over dispatches of kernels whose name contains `match` (KiB per dispatch);
+    with `largest`, the largest single dispatch instead (the calibration copy among the
+    runtime's smaller copies)."""
+    per = collections.defaultdict(float)
+    names = {}
+    for r in _rows(_find_csv(pmc_csv, "counter_collection.csv")):
+        if r["Counter_Name"] != counter or match not in r["Kernel_Name"]:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(per))
+        per[key] += float(r["Counter_Value"])  # summed over XCD/SE instances
+        names[key] = r["Kernel_Name"]
+    if not per:
+        raise SystemExit("no %s rows for kernels matching %r" % (counter, match))
+    vals = list(per.values())
+    if largest:
+        return max(vals), 1, sorted(set(names.values()))[0]
+    return sum(vals) / len(vals), len(vals), sorted(set(names.values()))[0]
+
+
+def traffic(fetch_csv, write_csv, kernel, copy_bytes):
+    f_kib, f_n, name = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
+    w_kib, w_n, _ = _per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    cf_kib, _, _ = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL, largest=True)
+    cw_kib, _, _ = _per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL, largest=True)
+    f_factor = cf_kib * 1024.0 / copy_bytes   # counter KiB per true KiB
+    w_factor = cw_kib * 1024.0 / copy_bytes
+    fetch_b = f_kib * 1024.0 / f_factor
+    write_b = w_kib * 1024.0 / w_factor
+    return {
+        "kernel_match": kernel, "kernel_name": name, "dispatches": [f_n, w_n],
+        "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+        "copy_bytes": copy_bytes, "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
+        "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+        "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+        "traffic_bytes": round(fetch_b + write_b), "source_sha256": source_hash(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True, help="the command that produced the csv")
+    s.add_argument("--title", default="Kernel durations")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--stage", required=True, help="bench.py stage name of the kernel")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--cmd", required=True, help="the two commands, separated by ' ; '")
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd_name == "stats":
+        print("# %s\n\nCommand:\n\n```\n%s\n```\n\n%s" % (a.title, a.cmd, stats_table(a.csv)))
+        return
+    res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
+    res["stage"] = a.stage
+    res["command"] = a.cmd
+    with open(a.out + ".json", "w") as fh:
+        json.dump(res, fh, indent=1)
+    with open(a.out + ".md", "w") as fh:
+        fh.write("# HBM traffic of `%s` (%s)\n\nCommands:\n\n```\n%s\n```\n\n" % (a.stage, res["kernel_name"], a.cmd.replace(" ; ", "\n")))
+        fh.write("| counter | kernel KiB/dispatch | copy KiB (of %d B) | factor | bytes/dispatch |\n|---|---:|---:|---:|---:|\n" % a.copy_bytes)
+        fh.write("| FETCH_SIZE | %.1f | %.1f | %.4f | %d |\n" % (res["fetch_kib_per_dispatch"], res["copy_fetch_kib"], res["fetch_factor"], res["fetch_bytes"]))
+        fh.write("| WRITE_SIZE | %.1f | %.1f | %.4f | %d |\n" % (res["write_kib_per_dispatch"], res["copy_write_kib"], res["write_factor"], res["write_bytes"]))
+        fh.write("\nTraffic per dispatch: %.1f MB (source hash %s).\n" % (res["traffic_bytes"] / 1e6, res["source_sha256"][:16]))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
