@@ -33,6 +33,8 @@
 //   SWIGLU : gate and up rows interleaved per 32 -> silu(g) * u (staged).
 //   SCORE  : scorer logit: sum_n GELU(acc + b1[n]) * w2[n], then sigmoid
 //            (the [tokens, H1] activations never reach memory)
+#include <type_traits>
+
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
@@ -216,13 +218,24 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KT) issue(s, s);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One k-tile. Its wave's share of the loads for k-tile kt+NSTAGE-1 (ISSUE)
+  // is spread over the four k-steps, after each step's MFMAs: issuing them
+  // back to back right after the barrier stalls the wave for ~500-1000 cycles
+  // (64 KB per CU per k-tile through the vector-memory path) before its first
+  // MFMA. The last NSTAGE-1 k-tiles (no loads) use a separate copy of the
+  // loop so the body has no branch.
+  constexpr int NR = SN + SM, NMF = SN * SM;
+  static_assert(NR <= NMF, "one read per MFMA slot");
+  constexpr int LPK = (LPW + 3) / 4;  // loads per k-step
+  auto ktile = [&](int kt, auto issue_c) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
     if (kt + NSTAGE - 2 < KT)
       wait_vmcnt<LPW * (NSTAGE - 2)>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
+    const int kn = kt + NSTAGE - 1, sn = kn % NSTAGE;
+    const uint32_t base_lds = lds0 + sn * STAGE + wave * 1024;
     const unsigned char* st = smem + (kt % NSTAGE) * STAGE;
     const unsigned char* wb = st + (wn * TN + (lane & 31)) * 128;
     const unsigned char* xb = st + (BN + wm * TM + (lane & 31)) * 128;
@@ -243,12 +256,18 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
       for (int j = 0; j < SN; ++j)
 #pragma unroll
         for (int i = 0; i < SM; ++i) acc[j][i] = mfma32(wf[ks & 1][j], xf[ks & 1][i], acc[j][i]);
+      if (ISSUE) {
+#pragma unroll
+        for (int i = ks * LPK; i < (ks + 1) * LPK; ++i)
+          if (i < LPW)
+            buf_dma16_soff(brs[i], bvoff[i], (uint32_t)kn * 128u,
+                           __builtin_amdgcn_readfirstlane(base_lds + NW * i * 1024));
+      }
     }
-    // Issue order (the scheduler would otherwise put each step's reads after
-    // the previous step's MFMAs): k-step 0 reads, then each later read
-    // between the MFMAs of the step before, so LDS latency hides under them.
-    constexpr int NR = SN + SM, NMF = SN * SM;
-    static_assert(NR <= NMF, "one read per MFMA slot");
+    // Issue order of reads and MFMAs (the scheduler would otherwise put each
+    // step's reads after the previous step's MFMAs): k-step 0 reads, then
+    // each later read between the MFMAs of the step before, so LDS latency
+    // hides under them.
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
@@ -260,7 +279,10 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
       __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
-  }
+  };
+  int kt = 0;
+  for (; kt + NSTAGE - 1 < KT; ++kt) ktile(kt, std::true_type());
+  for (; kt < KT; ++kt) ktile(kt, std::false_type());
 
   // ---------------- epilogues ----------------
   const int ml = lane & 31;
@@ -356,7 +378,7 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
                 const float gt = acc[2 * jj][i][rq * 4 + t], up = acc[2 * jj + 1][i][rq * 4 + t];
-                y[t] = gt / (1.0f + __expf(-gt)) * up;
+                y[t] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // v_rcp_f32: 1 ulp
               }
               *reinterpret_cast<f32x4*>(row + fpos(wn * (TN / 2) + jj * 32 + rq * 8 + half * 4)) = y;
             }
