@@ -219,14 +219,15 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KT) issue(s, s);
   // One k-tile. Its wave's share of the loads for k-tile kt+NSTAGE-1 (ISSUE)
-  // is spread over the four k-steps, after each step's MFMAs: issuing them
-  // back to back right after the barrier stalls the wave for ~500-1000 cycles
-  // (64 KB per CU per k-tile through the vector-memory path) before its first
-  // MFMA. The last NSTAGE-1 k-tiles (no loads) use a separate copy of the
-  // loop so the body has no branch.
+  // goes out after the MFMAs of k-steps 0 and 1: issuing them back to back
+  // right after the barrier stalls the wave for ~500-1000 cycles (64 KB per
+  // CU per k-tile through the vector-memory path) before its first MFMA, and
+  // issuing them as late as k-step 3 leaves them in flight at the next wait.
+  // The last NSTAGE-1 k-tiles (no loads) use a separate copy of the loop so
+  // the body has no branch.
   constexpr int NR = SN + SM, NMF = SN * SM;
   static_assert(NR <= NMF, "one read per MFMA slot");
-  constexpr int LPK = (LPW + 3) / 4;  // loads per k-step
+  constexpr int LPK = (LPW + 1) / 2;  // loads after each of k-steps 0 and 1
   auto ktile = [&](int kt, auto issue_c) {
     constexpr bool ISSUE = decltype(issue_c)::value;
     if (kt + NSTAGE - 2 < KT)
