@@ -184,7 +184,16 @@ typedef struct tg_layer_dims {
   float rope_base;        /* e.g. 1e6 */
   float rms_eps;          /* e.g. 1e-6 */
   tg_dtype dtype;
+  int flags;              /* TG_LAYER_* below; 0 by default */
 } tg_layer_dims;
+
+/* tg_layer_dims.flags: the workspace's RoPE table region (layout.rope)
+ * already holds the table for this call's pos_c, T, d and rope_base,
+ * written by an earlier tg_upper_layer_fwd on the same workspace and stream
+ * (the layers of one stack share positions), so the call does not rebuild
+ * it. With any other content the layer's RoPE is wrong: the flag is the
+ * caller's promise, the library does not check it. */
+#define TG_LAYER_ROPE_READY 1
 
 /* Byte offsets of the layer's intermediates inside its workspace (valid
  * after the call returns and the stream has run): RMSNorm output n2 (n1 is

@@ -52,7 +52,9 @@ class LayerWeights(ctypes.Structure):
 class LayerDims(ctypes.Structure):
     _fields_ = [("D", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
                 ("d", ctypes.c_int), ("I", ctypes.c_int), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int), ("flags", ctypes.c_int)]
+
+LAYER_ROPE_READY = 1  # tg_layer_dims.flags: the workspace already holds this RoPE table
 
 
 class LayerWsLayout(ctypes.Structure):
@@ -197,7 +199,7 @@ def gated_attn_fwd(q, k, v, s_c, t, g, cu_kept, max_k: int, o=None, lse=None, wa
 
 
 def layer_dims(D, Hq, Hkv, d, I, dtype: torch.dtype, rope_base=1.0e6, rms_eps=1.0e-6) -> LayerDims:
-    return LayerDims(D, Hq, Hkv, d, I, rope_base, rms_eps, dtype_code(dtype))
+    return LayerDims(D, Hq, Hkv, d, I, rope_base, rms_eps, dtype_code(dtype), 0)
 
 
 def upper_layer_ws_layout(dims: LayerDims, T: int) -> LayerWsLayout:
@@ -216,10 +218,16 @@ class UpperLayerWeights:
 
 
 def upper_layer_fwd(w: UpperLayerWeights, dims: LayerDims, x_in, pos_c, s_c, cu_kept, max_k: int,
-                    x_out=None, kcache=None, vcache=None, ws=None, events=None):
+                    x_out=None, kcache=None, vcache=None, ws=None, events=None, rope_ready=False):
     """One upper layer. ``events``: optional ctypes array of LAYER_STAGES + 1
     hipEvent_t handles; when given, the instrumented entry point records them
-    between the layer's stages."""
+    between the layer's stages. ``rope_ready``: ``ws`` already holds the RoPE
+    table of these positions (an earlier layer of the same stack ran on it)."""
+    if rope_ready:
+        if ws is None:
+            raise ValueError("rope_ready needs the workspace that holds the table")
+        dims = LayerDims(*[getattr(dims, n) for n, _ in LayerDims._fields_])
+        dims.flags |= LAYER_ROPE_READY
     T = x_in.shape[0]
     B = cu_kept.numel() - 1
     dev = x_in.device

@@ -47,7 +47,8 @@ inline tg_status launched(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ER
 
 bool layer_dims_ok(const tg_layer_dims* dm) {
   return dm->D > 0 && dm->Hq > 0 && dm->Hkv > 0 && dm->d > 0 && dm->I > 0 &&
-         dm->Hq % dm->Hkv == 0 && dm->rms_eps >= 0.f && dm->rope_base > 0.f;
+         dm->Hq % dm->Hkv == 0 && dm->rms_eps >= 0.f && dm->rope_base > 0.f &&
+         (dm->flags & ~TG_LAYER_ROPE_READY) == 0;
 }
 
 tg_status layer_dims_supported(const tg_layer_dims* dm) {
@@ -76,7 +77,7 @@ const char* tg_status_string(tg_status s) {
   }
 }
 
-int tg_abi_version(void) { return (1 << 16) | 0; }
+int tg_abi_version(void) { return (2 << 16) | 0; }
 
 // ---------------------------------------------------------------------------
 size_t tg_gate_score_workspace_size(int64_t T_in, int D, int H1, tg_dtype dtype) {
@@ -265,7 +266,8 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
 
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   TG_LAUNCH(mark(0));
-  TG_LAUNCH(tg::launch_rope_table(pos_c, T, d, dm->rope_base, rope, stream));
+  if (!(dm->flags & TG_LAYER_ROPE_READY))
+    TG_LAUNCH(tg::launch_rope_table(pos_c, T, d, dm->rope_base, rope, stream));
   TG_LAUNCH(mark(1));
   TG_LAUNCH(tg::launch_rmsnorm(x_in, w->attn_norm, norm, T, D, dm->rms_eps, bf, stream));
   TG_LAUNCH(mark(2));

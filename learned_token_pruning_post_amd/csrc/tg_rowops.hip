@@ -99,10 +99,71 @@ hipError_t launch_compact(const void* h, const int32_t* pos, const float* s, con
 // RMSNorm (pre-norm of the Qwen3-shaped layer): y = x * rsqrt(mean x^2 + eps) * w,
 // one wave per row, fp32 statistics.
 // ---------------------------------------------------------------------------
+// Wave-wide float sum on DPP lane moves (VALU; no LDS round trip): row_shr
+// 1, 2, 4, 8 sum each 16-lane row, row_bcast 15 / 31 carry the row totals,
+// lane 63 ends with the total.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+#define TG_DPP_ADD(ctrl, rmask)                                                                 \
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xf, false))
+  TG_DPP_ADD(0x111, 0xf);
+  TG_DPP_ADD(0x112, 0xf);
+  TG_DPP_ADD(0x114, 0xf);
+  TG_DPP_ADD(0x118, 0xf);
+  TG_DPP_ADD(0x142, 0xa);
+  TG_DPP_ADD(0x143, 0xc);
+#undef TG_DPP_ADD
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// One wave per row; the row (NVL 16-byte vectors per lane) stays in
+// registers between the sum of squares and the scaling, so x is read once.
+template <int NVL>
 __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const bf16* __restrict__ x,
                                                            const bf16* __restrict__ w,
                                                            bf16* __restrict__ y, int64_t rows,
                                                            int D, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const bf16x8* xr = reinterpret_cast<const bf16x8*>(x + row * D);
+  const bf16x8* wr = reinterpret_cast<const bf16x8*>(w);
+  bf16x8* yr = reinterpret_cast<bf16x8*>(y + row * D);
+  const int nv = D >> 3;
+  bf16x8 v[NVL];
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nv) v[i] = xr[c];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NVL; ++i)
+    if (lane + 64 * i < nv)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = bf2f(v[i][e]);
+        ss += f * f;
+      }
+  ss = wave_sum_dpp(ss);
+  const float r = rsqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nv) {
+      const bf16x8 ww = wr[c];
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f2bf(bf2f(v[i][e]) * r * bf2f(ww[e]));
+      yr[c] = o;
+    }
+  }
+}
+
+// rows wider than the register budget: two passes over the row
+__global__ __launch_bounds__(256) void rmsnorm_bf16_wide_kernel(const bf16* __restrict__ x,
+                                                                const bf16* __restrict__ w,
+                                                                bf16* __restrict__ y, int64_t rows,
+                                                                int D, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -119,7 +180,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const bf16* __restric
       ss += f * f;
     }
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_dpp(ss);
   const float r = rsqrtf(ss / (float)D + eps);
   for (int c = lane; c < nv; c += 64) {
     bf16x8 v = xr[c], ww = wr[c], o;
@@ -149,8 +210,15 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
                           bool is_bf16, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 3) / 4));
-  if (is_bf16)
-    hipLaunchKernelGGL(rmsnorm_bf16_kernel, grid, dim3(256), 0, stream, (const bf16*)x,
+  const int nvl = ((D >> 3) + 63) / 64;  // 16-byte vectors per lane
+  if (is_bf16 && nvl <= 4)
+    hipLaunchKernelGGL(rmsnorm_bf16_kernel<4>, grid, dim3(256), 0, stream, (const bf16*)x,
+                       (const bf16*)w, (bf16*)y, rows, D, eps);
+  else if (is_bf16 && nvl <= 8)
+    hipLaunchKernelGGL(rmsnorm_bf16_kernel<8>, grid, dim3(256), 0, stream, (const bf16*)x,
+                       (const bf16*)w, (bf16*)y, rows, D, eps);
+  else if (is_bf16)
+    hipLaunchKernelGGL(rmsnorm_bf16_wide_kernel, grid, dim3(256), 0, stream, (const bf16*)x,
                        (const bf16*)w, (bf16*)y, rows, D, eps);
   else
     hipLaunchKernelGGL(rmsnorm_f32_kernel, grid, dim3(256), 0, stream, (const float*)x,

@@ -101,8 +101,10 @@ class GatedPrefill:
 
     def layer(self, l: int):
         d = self.dw
+        # layers after the first reuse the RoPE table the first one left in the workspace
         tg.upper_layer_fwd(d.layers[l], d.dims, self.x, self.pos_c, self.s_c, d.cu_kept, d.w.max_k,
-                           x_out=self.x, kcache=self.kcache[l], vcache=self.vcache[l], ws=self.ws)
+                           x_out=self.x, kcache=self.kcache[l], vcache=self.vcache[l], ws=self.ws,
+                           rope_ready=l > 0)
 
     def run(self):
         self.score()

@@ -44,7 +44,7 @@ def test_status_strings_and_version(L):
     for code in range(5):
         assert tg.status_string(code)
     assert tg.status_string(99) == "unknown status"
-    assert L.tg_abi_version() >> 16 == 1
+    assert L.tg_abi_version() >> 16 == 2
 
 
 def test_gate_score_argument_errors(L):
@@ -115,6 +115,10 @@ def test_layer_layout_and_errors(L):
     assert f(*args(_dims(d=96), 1 << 40)) == UNSUP
     assert f(*args(_dims(Hq=6, Hkv=4), 1 << 40)) == INVALID
     assert f(*args(_dims(D=200), 1 << 40)) == UNSUP  # bf16 needs D % 64 == 0
+    bad_flags = _dims()
+    bad_flags.flags = 2  # only TG_LAYER_ROPE_READY is defined
+    assert f(*args(bad_flags, 1 << 40)) == INVALID
+    assert L.tg_upper_layer_ws_layout(ctypes.byref(bad_flags), 1000, ctypes.byref(lay)) == INVALID
     assert f(None, ctypes.byref(dm), *([FAKE] * 5), 1, 1000, 1000, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
     # fp32 layout carries the raw projections too
     lay32 = tg.LayerWsLayout()
