@@ -133,6 +133,34 @@ def test_stages_ragged_gqa4_fp32_d128():
     _stage_parity(w)
 
 
+def test_layer_stack_reuses_rope_table():
+    """Layer 1 of a stack runs on the RoPE table layer 0 left in the workspace
+    (TG_LAYER_ROPE_READY): its outputs equal a run that rebuilds the table, and
+    its post-RoPE K cache matches the oracle."""
+    w = workload("qwen8k", layers=2)
+    dw = DeviceWorkload(w, n_layers=2, keep_host=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    gp.select()
+    gp.compact()
+    gp.layer(0)
+    x_in = gp.x.clone()
+    gp.layer(1)
+    torch.cuda.synchronize()
+    reuse = (gp.x.clone(), gp.kcache[1].clone(), gp.vcache[1].clone())
+    fresh_ws = torch.zeros_like(gp.ws)
+    x2, k2, v2, _ = tg.upper_layer_fwd(dw.layers[1], dw.dims, x_in, gp.pos_c, gp.s_c, dw.cu_kept,
+                                       w.max_k, ws=fresh_ws)
+    torch.cuda.synchronize()
+    for a, b, name in zip(reuse, (x2, k2, v2), ("x out", "k cache", "v cache")):
+        assert torch.equal(a, b), name
+    W = layer_dict(dw.host_layers[1])
+    rows = sample_rows(dw.host_gate.cu_kept, 256, 1)
+    _, q_r, k_r, v_r = O.qkv_rope(f64(x_in), gp.pos_c.cpu().numpy(), W, w.dims, rows=rows)
+    e = assert_close(f64(reuse[1])[rows], k_r[rows], w.dims.dtype, "layer-1 k cache")
+    say("  layer 1 on the reused RoPE table: bit-identical to a rebuilt one; k err %.3g" % e)
+
+
 def test_scorer_wide_hidden_uses_partials():
     dims = ModelDims(D=128, Hq=2, Hkv=1, d=64, I=128, H1=600, dtype="bf16")
     w = custom(23, N=[777], K=[10], F=2, dims=dims)

@@ -1,0 +1,72 @@
+"""CPU checks of the rocprofv3 summary tool that fills bench.py's roofline traffic."""
+import csv
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from learned_token_pruning_post_amd import rocprof_summary as R  # noqa: E402
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _pmc(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "p_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            # two counter instances per dispatch (summed by the tool)
+            for part in (0.25, 0.75):
+                w.writerow({"Correlation_Id": i, "Dispatch_Id": i, "Kernel_Name": name,
+                            "Counter_Name": counter, "Counter_Value": value * part})
+
+
+def test_traffic_scales_by_the_calibration_copy(tmp_path):
+    copy = 1 << 20  # bytes
+    # the counter reads half of the true bytes for fetches, all of them for writes
+    fetch = [("__amd_rocclr_copyBuffer", 4.0), ("__amd_rocclr_copyBuffer", copy / 1024 * 0.5),
+             ("void k<2>(P)", 300.0), ("void k<2>(P)", 500.0), ("other", 9.0)]
+    write = [("__amd_rocclr_copyBuffer", 8.0), ("__amd_rocclr_copyBuffer", copy / 1024 * 1.0),
+             ("void k<2>(P)", 100.0), ("void k<2>(P)", 100.0)]
+    _pmc(str(tmp_path / "f"), "FETCH_SIZE", fetch)
+    _pmc(str(tmp_path / "w"), "WRITE_SIZE", write)
+    res = R.traffic(str(tmp_path / "f"), str(tmp_path / "w"), "k<2>", copy)
+    assert res["fetch_factor"] == pytest.approx(0.5)
+    assert res["write_factor"] == pytest.approx(1.0)
+    assert res["fetch_kib_per_dispatch"] == pytest.approx(400.0)
+    assert res["fetch_bytes"] == round(400.0 * 1024 / 0.5)
+    assert res["write_bytes"] == round(100.0 * 1024)
+    assert res["traffic_bytes"] == res["fetch_bytes"] + res["write_bytes"]
+    assert res["source_sha256"] == R.source_hash()
+
+
+def test_stats_table_orders_by_total(tmp_path):
+    p = tmp_path / "run_kernel_stats.csv"
+    with open(p, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow(["small", 10, 1000, 100, 1, 90, 110, 1])
+        w.writerow(["big", 2, 9000, 4500, 9, 4000, 5000, 1])
+    lines = R.stats_table(str(p)).splitlines()
+    assert "`big`" in lines[2] and "`small`" in lines[3]
+    assert "4.50" in lines[2]
+
+
+def test_bench_reports_traffic_only_for_unchanged_sources(tmp_path, monkeypatch):
+    import bench
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    rec = {"traffic_bytes": 123, "source_sha256": R.source_hash()}
+    with open(tmp_path / "profiles" / "traffic_gate_up_swiglu_w.json", "w") as fh:
+        json.dump(rec, fh)
+    assert bench.measured_traffic("gate_up_swiglu", "w") == 123
+    assert bench.measured_traffic("gated_attn", "w") is None
+    rec["source_sha256"] = "0" * 64
+    with open(tmp_path / "profiles" / "traffic_gate_up_swiglu_w.json", "w") as fh:
+        json.dump(rec, fh)
+    assert bench.measured_traffic("gate_up_swiglu", "w") is None
