@@ -131,6 +131,37 @@ def cpu_baseline(w, dw_host_gate, host_layers):
     }
 
 
+def attention_bias_ratio(tg, torch, w, dw, gp, stream, reps=20):
+    """The gated attention of the last layer's q/k/v with its gains g, and with g = 0
+    (plain causal attention, same shape and kernel), each timed over `reps` calls."""
+    L = len(dw.layers)
+    dm = dw.dims
+    lay = tg.upper_layer_ws_layout(dm, w.T)
+    dt = gp.x.dtype
+    nq = w.T * dm.Hq * dm.d
+    q = gp.ws[lay.q:lay.q + nq * gp.x.element_size()].view(dt).view(w.T, dm.Hq, dm.d)
+    k, v = gp.kcache[L - 1], gp.vcache[L - 1]
+    t = dw.layers[L - 1].tensors["t"]
+    g = dw.layers[L - 1].tensors["g"]
+    o = torch.empty_like(q)
+    ev = HipEvents(4)
+    res = {}
+    g0 = torch.zeros_like(g)
+    for _ in range(3):  # alternate the two, keep the best of each (clock drift)
+        for name, gg in (("bias", g), ("g0", g0)):
+            tg.gated_attn_fwd(q, k, v, gp.s_c, t, gg, dw.cu_kept, w.max_k, o=o)
+            ev.record(0, stream)
+            for _ in range(reps):
+                tg.gated_attn_fwd(q, k, v, gp.s_c, t, gg, dw.cu_kept, w.max_k, o=o)
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            us = ev.ms(0, 1) * 1e3 / reps
+            res[name] = min(res.get(name, us), us)
+    ev.close()
+    return {"us_bias": round(res["bias"], 2), "us_g0": round(res["g0"], 2),
+            "ratio": round(res["bias"] / res["g0"], 3)}
+
+
 def measured_traffic(stage, workload_name):
     """HBM bytes per launch of `stage` from the committed FETCH_SIZE / WRITE_SIZE summary
     (profiles/traffic_<stage>_<workload>.json), or None when there is none or the kernel
@@ -227,6 +258,7 @@ def main():
         ev.record(3, stream)
         torch.cuda.synchronize()
         ms_instr = ev.ms(2, 3) / args.steps
+        attn_bias = attention_bias_ratio(tg, torch, w, dw, gp, stream)
     ms_per_step = total_ms / args.steps
     tokens_per_s = w.T_in / (ms_per_step / 1e3)
     peak_mem = torch.cuda.max_memory_allocated()
@@ -301,12 +333,14 @@ def main():
         },
         "host_wall_s_timed": round(t_host1 - t_host0, 3),
         "ms_per_step_with_kernel_events": round(ms_instr, 4) if ms_instr else None,
+        "kept_tokens_per_s": round(w.T / (ms_per_step / 1e3), 1),
         "peak_device_mem_gb": round(peak_mem / 1e9, 3),
     }
     if use_ev:
         a = kern["gated_attn"]
         out["attn_tflops"] = a["tflops"]
         out["attn_frac_mfma_peak"] = a["frac_mfma_peak"]
+        out["attn_bias_vs_g0"] = attn_bias
         sc_us = kern["topk_select"]["avg_us"] + kern["compact"]["avg_us"]
         sc_bytes = kbytes["topk_select"] + kbytes["compact"]
         out["select_compact"] = {"us": round(sc_us, 2), "bytes": sc_bytes,
