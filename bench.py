@@ -172,7 +172,7 @@ def measured_traffic(stage, workload_name):
     from learned_token_pruning_post_amd.rocprof_summary import source_hash
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha256") != source_hash():
+    if rec.get("source_sha256") != source_hash(stage):
         return None
     return rec["traffic_bytes"]
 

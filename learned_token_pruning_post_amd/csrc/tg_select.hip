@@ -14,7 +14,7 @@
 //
 // Sequences of up to SEL_LDS_MAX tokens keep their keys in LDS (select_lds).
 // Longer sequences stream their scores from global memory on every pass
-// (select_sequence) with 16 independent loads in flight per thread.
+// (select_global) with 16 independent loads in flight per thread.
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
@@ -24,7 +24,6 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_BINS = 2048;
 constexpr int SEL_LDS_MAX = 32768;                       // keys held in LDS
-constexpr int SEL_KEY_WORDS = SEL_LDS_MAX + SEL_LDS_MAX / 32;  // padded
 constexpr int SEL_BATCH = 16;                            // loads in flight (global path)
 
 __device__ __forceinline__ uint32_t score_key(float x, bool& is_nan) {
@@ -34,8 +33,6 @@ __device__ __forceinline__ uint32_t score_key(float x, bool& is_nan) {
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ int pidx(int i) { return i + (i >> 5); }
 
 // Block-wide inclusive scan of one int per thread (1024 threads).
 __device__ __forceinline__ int block_incl_scan(int v, int* sh /*[SEL_WAVES]*/) {
@@ -101,144 +98,90 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
   return r;
 }
 
-// Key source of one sequence: LDS-resident (IN_LDS) or streamed from global.
-template <bool IN_LDS>
-struct KeySrc {
+// Scores of one sequence streamed from global memory (sequences longer than
+// SEL_LDS_MAX tokens), SEL_BATCH independent loads in flight per thread.
+struct GlobalKeys {
   const float* sp;
   const uint8_t* mp;
-  const uint32_t* keys;   // LDS, padded
-  const uint32_t* fbits;  // LDS bitmap of forced tokens
 
-  __device__ __forceinline__ bool forced(int i) const {
-    if (IN_LDS) return (fbits[i >> 5] >> (i & 31)) & 1u;
-    return mp && mp[i];
-  }
-  __device__ __forceinline__ uint32_t key(int i) const {
-    if (IN_LDS) return keys[pidx(i)];
-    bool isn;
-    return score_key(sp[i], isn);
-  }
   // visit (index, key, forced) of the contiguous span [i0, i1) in order
   template <class F>
   __device__ __forceinline__ void blocked(int i0, int i1, F&& f) const {
-    if (IN_LDS) {
-      for (int i = i0; i < i1; ++i) f(i, keys[pidx(i)], forced(i));
-    } else {
-      for (int b0 = i0; b0 < i1; b0 += SEL_BATCH) {
-        float x[SEL_BATCH];
-        uint8_t fm[SEL_BATCH];
+    for (int b0 = i0; b0 < i1; b0 += SEL_BATCH) {
+      float x[SEL_BATCH];
+      uint8_t fm[SEL_BATCH];
 #pragma unroll
-        for (int u = 0; u < SEL_BATCH; ++u) {
-          const int i = b0 + u;
-          x[u] = i < i1 ? sp[i] : 0.f;
-          fm[u] = (i < i1 && mp) ? mp[i] : 0;
-        }
+      for (int u = 0; u < SEL_BATCH; ++u) {
+        const int i = b0 + u;
+        x[u] = i < i1 ? sp[i] : 0.f;
+        fm[u] = (i < i1 && mp) ? mp[i] : 0;
+      }
 #pragma unroll
-        for (int u = 0; u < SEL_BATCH; ++u) {
-          const int i = b0 + u;
-          if (i < i1) {
-            bool isn;
-            f(i, score_key(x[u], isn), fm[u] != 0);
-          }
+      for (int u = 0; u < SEL_BATCH; ++u) {
+        const int i = b0 + u;
+        if (i < i1) {
+          bool isn;
+          f(i, score_key(x[u], isn), fm[u] != 0);
         }
       }
     }
   }
-  // visit (index, key, forced) of the strided set tid, tid+1024, ... (< n);
-  // the global variant keeps SEL_BATCH independent loads in flight
+  // visit (index, key, forced) of the strided set tid, tid+1024, ... (< n)
   template <class F>
   __device__ __forceinline__ void strided(int n, F&& f) const {
     const int tid = threadIdx.x;
-    if (IN_LDS) {
-      for (int i = tid; i < n; i += SEL_THREADS) f(i, keys[pidx(i)], forced(i));
-    } else {
-      for (int i0 = tid; i0 < n; i0 += SEL_THREADS * SEL_BATCH) {
-        float x[SEL_BATCH];
-        uint8_t fm[SEL_BATCH];
+    for (int i0 = tid; i0 < n; i0 += SEL_THREADS * SEL_BATCH) {
+      float x[SEL_BATCH];
+      uint8_t fm[SEL_BATCH];
 #pragma unroll
-        for (int u = 0; u < SEL_BATCH; ++u) {
-          const int i = i0 + u * SEL_THREADS;
-          x[u] = i < n ? sp[i] : 0.f;
-          fm[u] = (i < n && mp) ? mp[i] : 0;
-        }
+      for (int u = 0; u < SEL_BATCH; ++u) {
+        const int i = i0 + u * SEL_THREADS;
+        x[u] = i < n ? sp[i] : 0.f;
+        fm[u] = (i < n && mp) ? mp[i] : 0;
+      }
 #pragma unroll
-        for (int u = 0; u < SEL_BATCH; ++u) {
-          const int i = i0 + u * SEL_THREADS;
-          if (i < n) {
-            bool isn;
-            f(i, score_key(x[u], isn), fm[u] != 0);
-          }
+      for (int u = 0; u < SEL_BATCH; ++u) {
+        const int i = i0 + u * SEL_THREADS;
+        if (i < n) {
+          bool isn;
+          f(i, score_key(x[u], isn), fm[u] != 0);
         }
       }
     }
   }
 };
 
-template <bool IN_LDS>
-__device__ __forceinline__ void select_sequence(const float* __restrict__ sp, const uint8_t* __restrict__ mp,
-                                int n, int K, int in0, int32_t* __restrict__ kp,
-                                int32_t* __restrict__ status_b, uint32_t* keys, uint32_t* fbits,
-                                uint32_t* hist, int* shi, uint32_t* shu, int* found) {
+__device__ __forceinline__ void select_global(const float* __restrict__ sp,
+                                              const uint8_t* __restrict__ mp, int n, int K, int in0,
+                                              int32_t* __restrict__ kp, int32_t* __restrict__ status_b,
+                                              uint32_t* hist, int* shi, uint32_t* shu, int* found) {
   const int tid = threadIdx.x;
-  KeySrc<IN_LDS> src{sp, mp, keys, fbits};
+  GlobalKeys src{sp, mp};
 
-  // pass 0: (LDS variant) load keys and forced bits; forced count, NaN flag,
-  // live key range of the candidates
+  // pass 0: forced count, NaN flag, live key range of the candidates
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   int nf = 0, nan_seen = 0;
-  if (IN_LDS) {
-    for (int w = tid; w < (n + 31) / 32; w += SEL_THREADS) fbits[w] = 0u;
-    __syncthreads();
-    for (int i0 = tid; i0 < n; i0 += SEL_THREADS * SEL_BATCH) {
-      float x[SEL_BATCH];
-      uint8_t fm[SEL_BATCH];
+  for (int i0 = tid; i0 < n; i0 += SEL_THREADS * SEL_BATCH) {
+    float x[SEL_BATCH];
+    uint8_t fm[SEL_BATCH];
 #pragma unroll
-      for (int u = 0; u < SEL_BATCH; ++u) {
-        const int i = i0 + u * SEL_THREADS;
-        x[u] = i < n ? sp[i] : 0.f;
-        fm[u] = (i < n && mp) ? mp[i] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < SEL_BATCH; ++u) {
-        const int i = i0 + u * SEL_THREADS;
-        if (i < n) {
-          bool isn;
-          const uint32_t k = score_key(x[u], isn);
-          nan_seen |= isn;
-          keys[pidx(i)] = k;
-          if (fm[u]) {
-            ++nf;
-            atomicOr(&fbits[i >> 5], 1u << (i & 31));
-          } else {
-            kmin = min(kmin, k);
-            kmax = max(kmax, k);
-          }
-        }
-      }
+    for (int u = 0; u < SEL_BATCH; ++u) {
+      const int i = i0 + u * SEL_THREADS;
+      x[u] = i < n ? sp[i] : 0.f;
+      fm[u] = (i < n && mp) ? mp[i] : 0;
     }
-  } else {
-    for (int i0 = tid; i0 < n; i0 += SEL_THREADS * SEL_BATCH) {
-      float x[SEL_BATCH];
-      uint8_t fm[SEL_BATCH];
 #pragma unroll
-      for (int u = 0; u < SEL_BATCH; ++u) {
-        const int i = i0 + u * SEL_THREADS;
-        x[u] = i < n ? sp[i] : 0.f;
-        fm[u] = (i < n && mp) ? mp[i] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < SEL_BATCH; ++u) {
-        const int i = i0 + u * SEL_THREADS;
-        if (i < n) {
-          bool isn;
-          const uint32_t k = score_key(x[u], isn);
-          nan_seen |= isn;
-          if (fm[u]) {
-            ++nf;
-          } else {
-            kmin = min(kmin, k);
-            kmax = max(kmax, k);
-          }
+    for (int u = 0; u < SEL_BATCH; ++u) {
+      const int i = i0 + u * SEL_THREADS;
+      if (i < n) {
+        bool isn;
+        const uint32_t k = score_key(x[u], isn);
+        nan_seen |= isn;
+        if (fm[u]) {
+          ++nf;
+        } else {
+          kmin = min(kmin, k);
+          kmax = max(kmax, k);
         }
       }
     }
@@ -698,8 +641,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
   if (n <= SEL_LDS_MAX)
     select_lds(sp, mp, n, K, in0, kept + out0, st, sel_smem, fbits, hist, red, list);
   else
-    select_sequence<false>(sp, mp, n, K, in0, kept + out0, st, sel_smem, fbits, hist, shi, shu,
-                           found);
+    select_global(sp, mp, n, K, in0, kept + out0, st, hist, shi, shu, found);
 }
 
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,

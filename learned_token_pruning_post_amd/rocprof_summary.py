@@ -10,9 +10,9 @@
         `bench.py --calib-copy` issues in the same process; writes PREFIX.json (read by
         bench.py) and PREFIX.md
 
-The JSON carries a hash of the kernel sources (csrc/ and include/); bench.py reports the
-traffic only while the sources still hash the same, i.e. while the counters describe the
-kernels being timed.
+The JSON carries a hash of the measured kernel's sources (its own .hip file and the shared
+device headers); bench.py reports the traffic only while those still hash the same, i.e.
+while the counters describe the kernel being timed.
 """
 import argparse
 import collections
@@ -28,9 +28,30 @@ ROOT = os.path.dirname(PKG)
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 
 
-def source_hash() -> str:
-    """sha256 over the kernel sources and the C header, in a fixed order."""
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "tokengate.h")]
+# the files that define each stage's kernel: its own source plus the shared device headers
+_SHARED = ["tg_common.hpp", "tg_internal.hpp"]
+STAGE_SOURCES = {
+    "gate_score": ["tg_gemm.hip"] + _SHARED,
+    "topk_select": ["tg_select.hip"] + _SHARED,
+    "compact": ["tg_rowops.hip"] + _SHARED,
+    "rmsnorm_attn": ["tg_rowops.hip"] + _SHARED,
+    "rmsnorm_ffn": ["tg_rowops.hip"] + _SHARED,
+    "rope_table": ["tg_rowops.hip"] + _SHARED,
+    "qkv_rope_kv": ["tg_gemm.hip"] + _SHARED,
+    "gated_attn": ["tg_attn.hip"] + _SHARED,
+    "o_proj_resid": ["tg_gemm.hip"] + _SHARED,
+    "gate_up_swiglu": ["tg_gemm.hip"] + _SHARED,
+    "down_proj_resid": ["tg_gemm.hip"] + _SHARED,
+}
+
+
+def source_hash(stage=None) -> str:
+    """sha256 over the sources of `stage`'s kernel (every kernel source and the C header
+    when `stage` is None or unknown), in a fixed order."""
+    if stage in STAGE_SOURCES:
+        files = [os.path.join(PKG, "csrc", f) for f in STAGE_SOURCES[stage]]
+    else:
+        files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "tokengate.h")]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -88,7 +109,7 @@ def _per_dispatch(pmc_csv, counter, match, largest=False):
     return sum(vals) / len(vals), len(vals), sorted(set(names.values()))[0]
 
 
-def traffic(fetch_csv, write_csv, kernel, copy_bytes):
+def traffic(fetch_csv, write_csv, kernel, copy_bytes, stage=None):
     f_kib, f_n, name = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
     w_kib, w_n, _ = _per_dispatch(write_csv, "WRITE_SIZE", kernel)
     cf_kib, _, _ = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL, largest=True)
@@ -103,7 +124,7 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes):
         "copy_bytes": copy_bytes, "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
         "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
         "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
-        "traffic_bytes": round(fetch_b + write_b), "source_sha256": source_hash(),
+        "traffic_bytes": round(fetch_b + write_b), "source_sha256": source_hash(stage),
     }
 
 
@@ -126,7 +147,7 @@ def main(argv=None):
     if a.cmd_name == "stats":
         print("# %s\n\nCommand:\n\n```\n%s\n```\n\n%s" % (a.title, a.cmd, stats_table(a.csv)))
         return
-    res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
+    res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes, a.stage)
     res["stage"] = a.stage
     res["command"] = a.cmd
     with open(a.out + ".json", "w") as fh:

@@ -35,14 +35,15 @@ def test_traffic_scales_by_the_calibration_copy(tmp_path):
              ("void k<2>(P)", 100.0), ("void k<2>(P)", 100.0)]
     _pmc(str(tmp_path / "f"), "FETCH_SIZE", fetch)
     _pmc(str(tmp_path / "w"), "WRITE_SIZE", write)
-    res = R.traffic(str(tmp_path / "f"), str(tmp_path / "w"), "k<2>", copy)
+    res = R.traffic(str(tmp_path / "f"), str(tmp_path / "w"), "k<2>", copy, "gated_attn")
     assert res["fetch_factor"] == pytest.approx(0.5)
     assert res["write_factor"] == pytest.approx(1.0)
     assert res["fetch_kib_per_dispatch"] == pytest.approx(400.0)
     assert res["fetch_bytes"] == round(400.0 * 1024 / 0.5)
     assert res["write_bytes"] == round(100.0 * 1024)
     assert res["traffic_bytes"] == res["fetch_bytes"] + res["write_bytes"]
-    assert res["source_sha256"] == R.source_hash()
+    assert res["source_sha256"] == R.source_hash("gated_attn")
+    assert R.source_hash("gated_attn") != R.source_hash("gate_up_swiglu") != R.source_hash()
 
 
 def test_stats_table_orders_by_total(tmp_path):
@@ -61,10 +62,14 @@ def test_bench_reports_traffic_only_for_unchanged_sources(tmp_path, monkeypatch)
     import bench
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     os.makedirs(tmp_path / "profiles")
-    rec = {"traffic_bytes": 123, "source_sha256": R.source_hash()}
+    rec = {"traffic_bytes": 123, "source_sha256": R.source_hash("gate_up_swiglu")}
     with open(tmp_path / "profiles" / "traffic_gate_up_swiglu_w.json", "w") as fh:
         json.dump(rec, fh)
     assert bench.measured_traffic("gate_up_swiglu", "w") == 123
+    assert bench.measured_traffic("gated_attn", "w") is None
+    # a record taken for one kernel does not stand for another
+    with open(tmp_path / "profiles" / "traffic_gated_attn_w.json", "w") as fh:
+        json.dump(rec, fh)
     assert bench.measured_traffic("gated_attn", "w") is None
     rec["source_sha256"] = "0" * 64
     with open(tmp_path / "profiles" / "traffic_gate_up_swiglu_w.json", "w") as fh:
