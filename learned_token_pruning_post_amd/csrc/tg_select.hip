@@ -288,21 +288,28 @@ __device__ __forceinline__ void select_global(const float* __restrict__ sp,
 // ---------------------------------------------------------------------------
 // LDS path (n <= SEL_LDS_MAX): keys stay in LDS after one vectorised load.
 //  * load: every thread issues all of its 16-byte score loads and 4-byte
-//    mask loads before using any; the forced bitmap words are assembled
-//    with lane shuffles (8 lanes = 32 tokens), no atomics;
+//    mask loads before using any; forced tokens are stored as key 0 and NaN
+//    candidates as key 1, below every number's key, so no separate forced
+//    bitmap is kept;
 //  * one fused reduction of (forced count, NaN flag, candidate min, max);
 //  * range passes with SEL_LDS_BINS = 4096 power-of-two bins (the span
 //    shrinks by 2^12 per pass). Once the live range holds at most SEL_LIST
 //    candidates, the pass that scans all keys also gathers those into a
 //    list, and the remaining passes read only the list;
-//  * emit: wave w owns tokens [w*2048, w*2048 + 2048), 4 per lane per round;
-//    wave scans give each lane its output slot (and, when only part of the
-//    threshold ties is kept, its tie rank), so kept indices are written in
-//    ascending order without a block-wide scan over tokens.
+//  * emit: thread t owns tokens 32t..32t+31; one block scan of
+//    packed (sure, tie) counts gives every thread its output slot and the
+//    tie rank of its first tie, so kept indices are written in ascending
+//    order.
 // ---------------------------------------------------------------------------
 constexpr int SEL_LDS_BINS = 4096;
+
+// LDS position of 4-token chunk g: chunks are XOR-swizzled inside each
+// aligned block of 16 (256 bytes, the 64-bank width), so both the strided
+// chunk walks (16 consecutive chunks per 16 lanes) and the emit's
+// thread-contiguous walk (chunks 8t + q for 16 consecutive t) hit 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int kchunk(int g) { return g ^ ((g >> 3) & 15); }
 constexpr int SEL_LIST = 2048;
-constexpr int SEL_SPAN = SEL_LDS_MAX / SEL_WAVES;  // tokens per wave in the emit pass
 
 // Wave-wide inclusive scans on DPP lane moves (plain VALU: no LDS round trip
 // as with ds_bpermute): row_shr 1, 2, 4, 8 scan each 16-lane row, then
@@ -325,33 +332,33 @@ __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(
 
 __device__ __forceinline__ void select_lds(const float* __restrict__ sp, const uint8_t* __restrict__ mp, int n,
                            int K, int in0, int32_t* __restrict__ kp, int32_t* __restrict__ status_b,
-                           uint32_t* keys, uint32_t* fbits, uint32_t* hist, int* red,
-                           uint32_t* list) {
+                           uint32_t* keys, uint32_t* hist, int* red, uint32_t* list) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint64_t below = (1ull << lane) - 1ull;
   constexpr int NG = SEL_LDS_MAX / 4 / SEL_THREADS;  // 4-token groups per thread
 
   // ---- load ----
+  // LDS key of a token: 0 if forced, 1 if a NaN candidate, else its order
+  // key (>= 0x007fffff, the key of -inf), so range tests skip forced tokens
+  // by value and the tail of a partial 4-token chunk (0) is never in range.
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   int nf = 0, nan_seen = 0;
   auto take_key = [&](float x, bool f) -> uint32_t {
     bool isn;
-    const uint32_t k = score_key(x, isn);
+    uint32_t k = score_key(x, isn);
     nan_seen |= isn;
     if (f) {
       ++nf;
-    } else {
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
+      return 0u;
     }
+    k = isn ? 1u : k;
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
     return k;
   };
   const bool vec = (reinterpret_cast<uintptr_t>(sp) & 15u) == 0 &&
                    (reinterpret_cast<uintptr_t>(mp) & 3u) == 0;
   if (vec) {
-    // group g = u*1024 + tid holds tokens 4g..4g+3; lanes 8c..8c+7 of a wave
-    // cover one bitmap word. Every thread runs all NG rounds so that all
-    // lanes take part in the shuffles.
+    // chunk g = u*1024 + tid holds tokens 4g..4g+3: all loads first
     f32x4 xv[NG];
     uint32_t mv[NG];
 #pragma unroll
@@ -371,41 +378,16 @@ __device__ __forceinline__ void select_lds(const float* __restrict__ sp, const u
     }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int i = 4 * (u * SEL_THREADS + tid);
-      uint32_t nib = 0u;
+      const int g = u * SEL_THREADS + tid, i = 4 * g;
       u32x4 kv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool f = ((mv[u] >> (8 * e)) & 0xffu) != 0;
-        kv[e] = 0u;
-        if (i + e < n) {
-          kv[e] = take_key(xv[u][e], f);
-          nib |= (uint32_t)f << e;
-        }
-      }
-      if (i < n) *reinterpret_cast<u32x4*>(keys + i) = kv;
-      // OR of the 8 lanes of a word lands in lane 8c+7 (row shifts 1, 2, 4
-      // reach exactly lanes 8c..8c+7 from there)
-      uint32_t word = nib << (4 * (lane & 7));
-      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x111, 0xf, 0xf, false);
-      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x112, 0xf, 0xf, false);
-      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x114, 0xf, 0xf, false);
-      const int iw = i - 28;  // first token of the word
-      if ((lane & 7) == 7 && iw < n) fbits[iw >> 5] = word;
+      for (int e = 0; e < 4; ++e)
+        kv[e] = i + e < n ? take_key(xv[u][e], ((mv[u] >> (8 * e)) & 0xffu) != 0) : 0u;
+      if (i < n) *reinterpret_cast<u32x4*>(keys + 4 * kchunk(g)) = kv;
     }
   } else {
-    for (int i = tid; i < ((n + 63) & ~63); i += SEL_THREADS) {
-      bool f = false;
-      if (i < n) {
-        f = mp && mp[i];
-        keys[i] = take_key(sp[i], f);
-      }
-      const uint64_t bal = __ballot(f);
-      if (lane == 0) {
-        fbits[i >> 5] = (uint32_t)bal;
-        fbits[(i >> 5) + 1] = (uint32_t)(bal >> 32);
-      }
-    }
+    for (int i = tid; i < ((n + 3) & ~3); i += SEL_THREADS)
+      keys[4 * kchunk(i >> 2) + (i & 3)] = i < n ? take_key(sp[i], mp && mp[i]) : 0u;
   }
   // ---- fused reduction ----
   nf = lane63(wave_incl_scan(nf));
@@ -476,22 +458,36 @@ __device__ __forceinline__ void select_lds(const float* __restrict__ sp, const u
           if (k - lo <= span) atomicAdd(&hist[(k - lo) >> shift], 1u);
         }
       } else {
-        for (int g = tid; g < (n + 3) / 4; g += SEL_THREADS) {
-          const int i = 4 * g;
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(keys + i);
-          const uint32_t nib = fbits[i >> 5] >> (i & 31);
+        // candidates of chunk g (tokens 4g..4g+3) inside [lo, hi]; forced
+        // tokens and the tail of a partial chunk hold key 0 < lo
+        auto in_range4 = [&](int g, u32x4& kv) -> uint32_t {
+          kv = *reinterpret_cast<const u32x4*>(keys + 4 * kchunk(g));
+          uint32_t m = 0u;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t k = kv[e];
-            const bool inr = i + e < n && !((nib >> e) & 1u) && k - lo <= span;
-            if (inr) atomicAdd(&hist[(k - lo) >> shift], 1u);
-            if (build) {  // wave-aggregated append
-              const uint64_t m = __ballot(inr);
-              int base = 0;
-              if (lane == 0 && m) base = atomicAdd(&red[130], __popcll(m));
-              base = __builtin_amdgcn_readlane(base, 0);
-              if (inr) list[base + __popcll(m & below)] = k;
-            }
+          for (int e = 0; e < 4; ++e) m |= (uint32_t)(kv[e] - lo <= span) << e;
+          return m;
+        };
+        int cnt = 0;
+        for (int g = tid; g < (n + 3) / 4; g += SEL_THREADS) {
+          u32x4 kv;
+          const uint32_t m = in_range4(g, kv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((m >> e) & 1u) atomicAdd(&hist[(kv[e] - lo) >> shift], 1u);
+          cnt += __popc(m);
+        }
+        if (build) {
+          // one list reservation per wave, then a second read writes the keys
+          const int incl = wave_incl_scan(cnt);
+          int base = 0;
+          if (lane == 63) base = atomicAdd(&red[130], incl);
+          int pos = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
+          for (int g = tid; g < (n + 3) / 4; g += SEL_THREADS) {
+            u32x4 kv;
+            const uint32_t m = in_range4(g, kv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if ((m >> e) & 1u) list[pos++] = kv[e];
           }
         }
       }
@@ -545,75 +541,47 @@ __device__ __forceinline__ void select_lds(const float* __restrict__ sp, const u
   }
 
   // ---- emit ----
-  // lane l of round q covers tokens w0 + 256q + 4l .. +3
-  const int w0 = w * SEL_SPAN;
-  auto flags4 = [&](int i, uint32_t& sure, uint32_t& tie) {
-    sure = 0u;
-    tie = 0u;
-    if (i >= n) return;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(keys + i);
-    const uint32_t nib = fbits[i >> 5] >> (i & 31);
+  // thread t owns tokens [32t, 32t + 32): 32-bit masks of sure keeps (forced,
+  // key 0, or key > T) and of ties (candidate key == T), one block scan of
+  // the packed (sure, tie) counts, the first needT ties in index order are
+  // kept, and each thread writes its kept indices in order. T = 0 keeps
+  // every token; T = 0xffffffff (no candidate slot) keeps the forced ones.
+  uint32_t sure = 0u, tie = 0u;
+  const int i0 = 32 * tid;
+  if (i0 < n) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool in = i + e < n, f = (nib >> e) & 1u;
-      sure |= (uint32_t)(in && (f || kv[e] > T)) << e;
-      tie |= (uint32_t)(in && !f && kv[e] == T) << e;
-    }
-  };
-  int sure_w = 0, ties_w = 0;
-  for (int q = 0; q < SEL_SPAN / 256; ++q) {
-    uint32_t su, ti;
-    flags4(w0 + 256 * q + 4 * lane, su, ti);
-    sure_w += __popc(su);
-    ties_w += __popc(ti);
-  }
-  sure_w = lane63(wave_incl_scan(sure_w));
-  ties_w = lane63(wave_incl_scan(ties_w));
-  __syncthreads();  // red is free
-  if (lane == 0) {
-    red[2 * w] = sure_w;
-    red[2 * w + 1] = ties_w;
-  }
-  __syncthreads();
-  int off = 0, tie_before = 0;
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(keys + 4 * kchunk(8 * tid + q));
 #pragma unroll
-  for (int v = 0; v < SEL_WAVES; ++v) {
-    if (v < w) {
-      const int s_v = red[2 * v], t_v = red[2 * v + 1];
-      off += s_v + min(max(needT - tie_before, 0), t_v);
-      tie_before += t_v;
-    }
-  }
-  const int take_w = min(max(needT - tie_before, 0), ties_w);
-  const bool all_ties = take_w == ties_w;  // else a prefix of this wave's ties (in index order)
-  int tie_run = 0;
-  for (int q = 0; q < SEL_SPAN / 256; ++q) {
-    const int i = w0 + 256 * q + 4 * lane;
-    uint32_t su, ti;
-    flags4(i, su, ti);
-    uint32_t keep = su | (all_ties ? ti : 0u);
-    if (!all_ties) {
-      const int tc = __popc(ti);
-      const int t_incl = wave_incl_scan(tc);
-      int rank = tie_run + t_incl - tc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((ti >> e) & 1u) {
-          if (rank < take_w) keep |= 1u << e;
-          ++rank;
-        }
-      tie_run += lane63(t_incl);
-    }
-    const int kc = __popc(keep);
-    const int k_incl = wave_incl_scan(kc);
-    int pos = off + k_incl - kc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if ((keep >> e) & 1u) {
-        if (pos < K) kp[pos] = in0 + i + e;  // pos < K always holds; the guard keeps a logic slip in bounds
-        ++pos;
+      for (int e = 0; e < 4; ++e) {
+        const int bit = 4 * q + e;
+        const bool in = i0 + bit < n;
+        const uint32_t k = kv[e];
+        sure |= (uint32_t)(in && (k == 0u || k > T)) << bit;
+        tie |= (uint32_t)(in && k != 0u && k == T) << bit;
       }
-    off += lane63(k_incl);
+    }
+  }
+  // sure and tie totals are <= 32768, so the packed halves never carry
+  const uint32_t packed = (uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16);
+  const uint32_t incl = (uint32_t)wave_incl_scan((int)packed);
+  __syncthreads();  // red is free
+  if (lane == 63) red[w] = (int)incl;
+  __syncthreads();
+  uint32_t excl = incl - packed;
+#pragma unroll
+  for (int v = 0; v < SEL_WAVES; ++v) excl += v < w ? (uint32_t)red[v] : 0u;
+  const int sure_before = (int)(excl & 0xffffu), tie_before = (int)(excl >> 16);
+  const int take = min(max(needT - tie_before, 0), __popc(tie));
+  uint32_t rest = tie;  // drop the lowest `take` tie bits from rest: they are kept
+  for (int c = 0; c < take; ++c) rest &= rest - 1u;
+  uint32_t keep = sure | (tie ^ rest);
+  int pos = sure_before + min(tie_before, needT);
+  while (keep) {
+    const int bit = __builtin_ctz(keep);
+    if (pos < K) kp[pos] = in0 + i0 + bit;  // pos < K always holds; the guard keeps a logic slip in bounds
+    ++pos;
+    keep &= keep - 1u;
   }
 }
 
@@ -628,7 +596,6 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
   __shared__ int found[2];
   __shared__ int red[132];
   __shared__ uint32_t list[SEL_LIST];
-  __shared__ uint32_t fbits[SEL_LDS_MAX / 32 + 2];
 
   const int b = blockIdx.x;
   const int in0 = cu_in[b];
@@ -639,7 +606,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
   const uint8_t* mp = mask ? mask + in0 : nullptr;
   int32_t* st = status ? status + b : nullptr;
   if (n <= SEL_LDS_MAX)
-    select_lds(sp, mp, n, K, in0, kept + out0, st, sel_smem, fbits, hist, red, list);
+    select_lds(sp, mp, n, K, in0, kept + out0, st, sel_smem, hist, red, list);
   else
     select_global(sp, mp, n, K, in0, kept + out0, st, hist, shi, shu, found);
 }
