@@ -339,12 +339,16 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   } else if (MODE == MODE_QKV || MODE == MODE_SWIGLU) {
     // Stage 64 tokens at a time in LDS as fp32 [token][feature] over the
     // whole workgroup tile, then let every thread finish 8-feature chunks of
-    // a token row: RoPE pairs (i, i + d/2) are both in the tile (heads never
-    // straddle a 256-feature tile), the RoPE table is read in 32-byte pieces
-    // along the row, and every store is 16 bytes of a contiguous row segment.
-    // Inside a staged row the 4-feature halves of each 8-feature chunk are
-    // split into two runs, so both the f32x4 writes (one token per lane) and
-    // the f32x4 reads (consecutive chunks per lane) are conflict-free.
+    // token rows with 16-byte stores of contiguous row segments. Inside a
+    // staged row the 4-feature halves of each 8-feature chunk are split into
+    // two runs, so the f32x4 writes (one token per lane) and the f32x4 reads
+    // (16 lanes on 16 consecutive rows, or on 16 consecutive chunks of a row)
+    // are conflict-free. QKV: RoPE pairs (i, i + d/2) are both in the tile
+    // (heads never straddle a 256-feature tile, and a tile holds an even
+    // number of heads); a thread takes one token and one 8-dim slice j of a
+    // head pair, i.e. the chunks at dims 8j and d/2 + 8j of both heads, so
+    // each cos/sin value read from the RoPE table serves four outputs and
+    // the two chunks of a pair are each other's partner.
     constexpr int W = MODE == MODE_QKV ? BN : BN / 2;  // staged features per token
     constexpr int RW = W + 4;                           // floats per staged row
     constexpr int CHT = 64;                             // tokens per round
@@ -353,8 +357,28 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     float* stg = reinterpret_cast<float*>(smem);
     auto fpos = [](int f) { return ((f >> 2) & 1) * (W / 2) + (f >> 3) * 4 + (f & 3); };
     constexpr int CPR = W / 8;  // chunks per staged row
+    static_assert(MODE != MODE_QKV || (BN == 256 && NW * 64 == CHT * 8),
+                  "QKV: one (token, head pair, 8-dim slice) task per thread and round");
+    // QKV task of this thread: token row qr of the round, head pair qhp, slice qj
+    const int qlane = tid & 63, qwv = tid >> 6;
+    const int qr = (qlane & 15) + 16 * (qwv >> 1), qu = (qlane >> 4) + 4 * (qwv & 1);
+    const int qnpc = MODE == MODE_QKV ? (p.hd >> 4) : 1;  // slices per head
+    const int qhp = qu / qnpc, qj = qu - qhp * qnpc;
 #pragma unroll
     for (int c0 = 0; c0 < BM; c0 += CHT) {
+      // QKV: cos and sin of the task's 8 dims, requested before the staging
+      // barriers so that their latency overlaps the staging
+      f32x4 tab[4];
+      if (MODE == MODE_QKV) {
+        const int m = m0 + c0 + qr, gh0 = n0 / p.hd + 2 * qhp;
+        if (m < p.M && gh0 < p.Hq + p.Hkv) {
+          const float* cs = p.rope + (size_t)m * p.hd + 8 * qj;
+          tab[0] = *reinterpret_cast<const f32x4*>(cs);
+          tab[1] = *reinterpret_cast<const f32x4*>(cs + 4);
+          tab[2] = *reinterpret_cast<const f32x4*>(cs + (p.hd >> 1));
+          tab[3] = *reinterpret_cast<const f32x4*>(cs + (p.hd >> 1) + 4);
+        }
+      }
       __syncthreads();  // the LDS ring (or the previous round) is no longer read
 #pragma unroll
       for (int i = 0; i < SM; ++i) {
@@ -386,51 +410,69 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
         }
       }
       __syncthreads();
-      for (int task = tid; task < CHT * CPR; task += NW * 64) {
-        const int r = task / CPR, f = (task % CPR) * 8;
-        const int m = m0 + c0 + r;
-        if (m >= p.M) continue;
-        const float* row = stg + r * RW;
-        const f32x4 xa = *reinterpret_cast<const f32x4*>(row + fpos(f));
-        const f32x4 xb = *reinterpret_cast<const f32x4*>(row + fpos(f + 4));
-        float y[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
-        bf16* dst;
-        if (MODE == MODE_QKV) {
-          const int hd = p.hd, hh = hd >> 1;
-          const int gn = n0 + f;
-          const int gh = gn / hd, dim = gn - gh * hd;
-          if (gh >= p.Hq + 2 * p.Hkv) continue;
-          if (gh < p.Hq + p.Hkv) {
-            const bool lo = dim < hh;
-            const int fp = lo ? f + hh : f - hh;  // partner chunk, same head
-            const f32x4 pa = *reinterpret_cast<const f32x4*>(row + fpos(fp));
-            const f32x4 pb = *reinterpret_cast<const f32x4*>(row + fpos(fp + 4));
-            const float z[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-            const float* cs = p.rope + (size_t)m * hd + (lo ? dim : dim - hh);
-            const f32x4 c0v = *reinterpret_cast<const f32x4*>(cs);
-            const f32x4 c1v = *reinterpret_cast<const f32x4*>(cs + 4);
-            const f32x4 s0v = *reinterpret_cast<const f32x4*>(cs + hh);
-            const f32x4 s1v = *reinterpret_cast<const f32x4*>(cs + hh + 4);
-            const float c[8] = {c0v[0], c0v[1], c0v[2], c0v[3], c1v[0], c1v[1], c1v[2], c1v[3]};
-            const float sn[8] = {s0v[0], s0v[1], s0v[2], s0v[3], s1v[0], s1v[1], s1v[2], s1v[3]};
+      if (MODE == MODE_QKV) {
+        const int m = m0 + c0 + qr;
+        const int hd = p.hd, hh = hd >> 1;
+        const float* row = stg + qr * RW;
+        const float c[8] = {tab[0][0], tab[0][1], tab[0][2], tab[0][3], tab[1][0], tab[1][1], tab[1][2], tab[1][3]};
+        const float sn[8] = {tab[2][0], tab[2][1], tab[2][2], tab[2][3], tab[3][0], tab[3][1], tab[3][2], tab[3][3]};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) y[t] = lo ? y[t] * c[t] - z[t] * sn[t] : y[t] * c[t] + z[t] * sn[t];
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int h = 2 * qhp + e2;  // head inside the tile
+          const int gh = n0 / hd + h;
+          if (m >= p.M || gh >= p.Hq + 2 * p.Hkv) continue;
+          const int flo = h * hd + 8 * qj, fhi = flo + hh;
+          const f32x4 la = *reinterpret_cast<const f32x4*>(row + fpos(flo));
+          const f32x4 lb = *reinterpret_cast<const f32x4*>(row + fpos(flo + 4));
+          const f32x4 ha = *reinterpret_cast<const f32x4*>(row + fpos(fhi));
+          const f32x4 hb = *reinterpret_cast<const f32x4*>(row + fpos(fhi + 4));
+          float ylo[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+          float yhi[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+          if (gh < p.Hq + p.Hkv) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const float xl = ylo[t], xh = yhi[t];
+              ylo[t] = xl * c[t] - xh * sn[t];
+              yhi[t] = xh * c[t] + xl * sn[t];
+            }
           }
+          bf16* dst;
           if (gh < p.Hq)
-            dst = p.q + (size_t)m * p.Hq * hd + gh * hd + dim;
+            dst = p.q + (size_t)m * p.Hq * hd + gh * hd;
           else if (gh < p.Hq + p.Hkv)
-            dst = p.kc + (size_t)m * p.Hkv * hd + (gh - p.Hq) * hd + dim;
+            dst = p.kc + (size_t)m * p.Hkv * hd + (gh - p.Hq) * hd;
           else
-            dst = p.vc + (size_t)m * p.Hkv * hd + (gh - p.Hq - p.Hkv) * hd + dim;
-        } else {
+            dst = p.vc + (size_t)m * p.Hkv * hd + (gh - p.Hq - p.Hkv) * hd;
+          bf16x8 wl, wh;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            wl[t] = f2bf(ylo[t]);
+            wh[t] = f2bf(yhi[t]);
+          }
+          *reinterpret_cast<bf16x8*>(dst + 8 * qj) = wl;
+          *reinterpret_cast<bf16x8*>(dst + hh + 8 * qj) = wh;
+        }
+      } else {
+        for (int task = tid; task < CHT * CPR; task += NW * 64) {
+          const int r = task / CPR, f = (task % CPR) * 8;
+          const int m = m0 + c0 + r;
+          if (m >= p.M) continue;
+          const float* row = stg + r * RW;
+          const f32x4 xa = *reinterpret_cast<const f32x4*>(row + fpos(f));
+          const f32x4 xb = *reinterpret_cast<const f32x4*>(row + fpos(f + 4));
           const int idx = (n0 >> 1) + f;
           if (idx >= p.I) continue;
-          dst = p.act + (size_t)m * p.I + idx;
+          bf16x8 w;
+          w[0] = f2bf(xa[0]);
+          w[1] = f2bf(xa[1]);
+          w[2] = f2bf(xa[2]);
+          w[3] = f2bf(xa[3]);
+          w[4] = f2bf(xb[0]);
+          w[5] = f2bf(xb[1]);
+          w[6] = f2bf(xb[2]);
+          w[7] = f2bf(xb[3]);
+          *reinterpret_cast<bf16x8*>(p.act + (size_t)m * p.I + idx) = w;
         }
-        bf16x8 w;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) w[t] = f2bf(y[t]);
-        *reinterpret_cast<bf16x8*>(dst) = w;
       }
     }
   } else {  // SCORE

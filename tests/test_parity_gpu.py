@@ -127,6 +127,14 @@ def test_stages_ragged_small_bf16():
     _stage_parity(w)
 
 
+def test_stages_ragged_bf16_k_and_v_head_in_one_pair():
+    # Hq + Hkv odd: the QKV epilogue's head pair (2, 3) of the only 256-feature
+    # tile holds the k head (rotated) and the v head (not rotated)
+    dims = ModelDims(D=128, Hq=2, Hkv=1, d=64, I=256, H1=64, dtype="bf16")
+    w = custom(23, N=[97, 260], K=[40, 130], F=2, dims=dims)
+    _stage_parity(w)
+
+
 def test_stages_ragged_gqa4_fp32_d128():
     dims = ModelDims(D=256, Hq=8, Hkv=2, d=128, I=384, H1=40, dtype="f32")
     w = custom(22, N=[129, 64, 200], K=[65, 64, 3], F=3, dims=dims)
