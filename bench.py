@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--n", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused-norms", action="store_true",
+                    help="run the two RMSNorms of each layer as kernels of their own instead of "
+                         "fused into the QKV and gate/up GEMMs (norm weights folded at setup)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device-to-device copy of BYTES (counter calibration "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -196,7 +199,7 @@ def main():
     print("[bench] generating %s: B=%d N=%s K=%s layers=%d" % (w.name, w.B, w.N[:4], w.K[:4], w.layers),
           file=sys.stderr, flush=True)
     want_cpu = not args.no_cpu_baseline
-    dw = DeviceWorkload(w, keep_host=False)
+    dw = DeviceWorkload(w, keep_host=False, norms_folded=not args.unfused_norms)
     gp = GatedPrefill(dw)
     L = len(dw.layers)
     stream = torch.cuda.current_stream().cuda_stream
@@ -222,7 +225,8 @@ def main():
             tg.upper_layer_fwd(dw.layers[l], dw.dims, gp.x, gp.pos_c, gp.s_c, dw.cu_kept, w.max_k,
                                x_out=gp.x, kcache=gp.kcache[l], vcache=gp.vcache[l], ws=gp.ws,
                                events=ev.sub(base + 4 + l * (tg.LAYER_STAGES + 1), tg.LAYER_STAGES + 1),
-                               rope_ready=l > 0)
+                               rope_ready=l > 0, norms_folded=dw.norms_folded,
+                               input_ssq=dw.norms_folded and l > 0)
 
     if args.calib_copy > 0:
         src = torch.empty(args.calib_copy, dtype=torch.uint8, device="cuda").fill_(1)
@@ -279,10 +283,11 @@ def main():
         "gate_score": w.T_in * D * elt + 4.0 * w.T_in + H1 * D * elt,
         "topk_select": 5.0 * w.T_in + 4.0 * T,
         "compact": 4.0 * T + 2.0 * T * D * elt + 4.0 * T + 8.0 * T,
-        "rmsnorm_attn": 2.0 * T * D * elt,
-        "rmsnorm_ffn": 2.0 * T * D * elt,
         "rope_table": 4.0 * T + 4.0 * T * d,
     }
+    if not dw.norms_folded:  # fused: stage 1 is x_in's sums of squares (first layer), stage 5 empty
+        kbytes["rmsnorm_attn"] = 2.0 * T * D * elt
+        kbytes["rmsnorm_ffn"] = 2.0 * T * D * elt
     kern = {}
     if use_ev:
         acc = {}
@@ -330,6 +335,8 @@ def main():
                            "/".join(map(str, w.K[:2])) + ("..." if w.B > 2 else ""), w.F, L,
                            D, Hq, Hkv, d, I, D, H1),
             "batch": w.B, "n_prompt_tokens": w.T_in, "n_kept_tokens": T, "upper_layers": L,
+            "rms_norm": "fused into the QKV and gate/up GEMMs (norm weights folded at setup)"
+                        if dw.norms_folded else "separate kernels",
         },
         "host_wall_s_timed": round(t_host1 - t_host0, 3),
         "ms_per_step_with_kernel_events": round(ms_instr, 4) if ms_instr else None,

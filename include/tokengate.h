@@ -195,13 +195,46 @@ typedef struct tg_layer_dims {
  * caller's promise, the library does not check it. */
 #define TG_LAYER_ROPE_READY 1
 
+/* tg_layer_dims.flags, bf16 only: both RMSNorms are fused into the
+ * projections that consume them. The caller has folded the norm weights
+ * into the input columns of those projections (tg_fold_norm_weights: wq, wk
+ * and wv by attn_norm, wg and wu by ffn_norm); attn_norm and ffn_norm are
+ * then ignored and may be NULL. The QKV and gate/up GEMMs read the raw x and
+ * x1 and scale each token row of their products by
+ * 1 / sqrt(mean(row^2) + rms_eps), formed from per-64-feature sums of
+ * squares: the O and down projections write those of x1 and x_out in their
+ * epilogues (layout.ssq), x_in's come from a small kernel unless
+ * TG_LAYER_INPUT_SSQ is set. Same layer up to rounding: the normalised
+ * activations are never rounded to the dtype. fp32 layers return
+ * TG_ERR_UNSUPPORTED with this flag. */
+#define TG_LAYER_NORMS_FOLDED 2
+
+/* tg_layer_dims.flags, with TG_LAYER_NORMS_FOLDED: the first half of the
+ * workspace's ssq region already holds x_in's sums of squares, written by
+ * the previous NORMS_FOLDED call on the same workspace and stream whose
+ * x_out is this call's x_in (consecutive layers of a stack), so the call
+ * does not recompute them. The caller's promise, unchecked; without
+ * TG_LAYER_NORMS_FOLDED the call returns TG_ERR_INVALID_ARG. */
+#define TG_LAYER_INPUT_SSQ 4
+
+/* Fold an RMSNorm weight into a projection for TG_LAYER_NORMS_FOLDED, in
+ * place on the stream: W[r, c] = W[r, c] * norm_w[c], the product taken in
+ * fp32 and rounded to the dtype (nearest even). W [rows, cols] and
+ * norm_w [cols] are device pointers of `dtype`. Errors: TG_ERR_INVALID_ARG
+ * for NULL pointers or negative sizes; rows or cols == 0 is a no-op. */
+tg_status tg_fold_norm_weights(const void* norm_w, void* W, int64_t rows, int cols,
+                               tg_dtype dtype, hipStream_t stream);
+
 /* Byte offsets of the layer's intermediates inside its workspace (valid
  * after the call returns and the stream has run): RMSNorm output n2 (n1 is
- * overwritten), q after RoPE [T,Hq,d], attention output o [T,Hq,d],
- * x1 [T,D], SwiGLU activation [T,I] (all dtype), RoPE table [T, d] fp32
- * (cos for i < d/2, then sin). */
+ * overwritten; unused with TG_LAYER_NORMS_FOLDED), q after RoPE [T,Hq,d],
+ * attention output o [T,Hq,d], x1 [T,D], SwiGLU activation [T,I] (all
+ * dtype), RoPE table [T, d] fp32 (cos for i < d/2, then sin), and with
+ * TG_LAYER_NORMS_FOLDED the row sums of squares [2][T][D/64] fp32 (sum over
+ * features 64s..64s+63 of row t at [., t, s]): x_out's in the first half
+ * (x_in's until the down projection overwrites them), x1's in the second. */
 typedef struct tg_layer_ws_layout {
-  size_t norm, q, attn, x1, act, rope, total;
+  size_t norm, q, attn, x1, act, rope, ssq, total;
 } tg_layer_ws_layout;
 
 tg_status tg_upper_layer_ws_layout(const tg_layer_dims* dims, int64_t T, tg_layer_ws_layout* out);
@@ -219,7 +252,8 @@ tg_status tg_upper_layer_fwd(const tg_layer_weights* w, const tg_layer_dims* dim
  * stage's GPU time. Stages: 0 RoPE table, 1 RMSNorm, 2 QKV projection (+RoPE,
  * KV-cache write), 3 gated attention, 4 O projection (+residual), 5 RMSNorm,
  * 6 gate/up projection (+SwiGLU), 7 down projection (+residual). In bf16 each
- * stage is one kernel. events: TG_LAYER_STAGES + 1 handles created by the
+ * stage is one kernel; with TG_LAYER_NORMS_FOLDED stage 1 is the sums of
+ * squares of x_in (empty with TG_LAYER_INPUT_SSQ) and stage 5 is empty. events: TG_LAYER_STAGES + 1 handles created by the
  * caller with hipEventCreate (none may be NULL). */
 #define TG_LAYER_STAGES 8
 tg_status tg_upper_layer_fwd_timed(const tg_layer_weights* w, const tg_layer_dims* dims,

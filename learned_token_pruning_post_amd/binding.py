@@ -31,7 +31,7 @@ ABI_FUNCTIONS = (
     "tg_compact",
     "tg_gated_attn_workspace_size", "tg_gated_attn_fwd",
     "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
-    "tg_upper_layer_fwd_timed",
+    "tg_upper_layer_fwd_timed", "tg_fold_norm_weights",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -55,10 +55,12 @@ class LayerDims(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int), ("flags", ctypes.c_int)]
 
 LAYER_ROPE_READY = 1  # tg_layer_dims.flags: the workspace already holds this RoPE table
+LAYER_NORMS_FOLDED = 2  # norm weights folded into wq/wk/wv and wg/wu: RMSNorms fused into the GEMMs
+LAYER_INPUT_SSQ = 4  # with NORMS_FOLDED: the workspace holds x_in's row sums of squares
 
 
 class LayerWsLayout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("norm", "q", "attn", "x1", "act", "rope", "total")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("norm", "q", "attn", "x1", "act", "rope", "ssq", "total")]
 
 
 _lib = None
@@ -102,6 +104,8 @@ def lib() -> ctypes.CDLL:
     L.tg_upper_layer_fwd.restype = i32
     L.tg_upper_layer_fwd_timed.argtypes = L.tg_upper_layer_fwd.argtypes + [vp]
     L.tg_upper_layer_fwd_timed.restype = i32
+    L.tg_fold_norm_weights.argtypes = [vp, vp, i64, i32, i32, vp]
+    L.tg_fold_norm_weights.restype = i32
     _lib = L
     return L
 
@@ -217,17 +221,32 @@ class UpperLayerWeights:
         self.c = LayerWeights(*[_p(tensors[n]) for n, _ in LayerWeights._fields_])
 
 
+def fold_norm_weights(norm_w: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
+    """W[r, c] *= norm_w[c] in place (fp32 product rounded to W's dtype); returns W."""
+    if W.dim() != 2 or norm_w.numel() != W.shape[1] or norm_w.dtype != W.dtype:
+        raise ValueError("fold_norm_weights: W [rows, cols] and norm_w [cols] of one dtype")
+    _check(lib().tg_fold_norm_weights(_p(norm_w.contiguous()), _p(W), W.shape[0], W.shape[1],
+                                      dtype_code(W.dtype), _stream()), "tg_fold_norm_weights")
+    return W
+
+
 def upper_layer_fwd(w: UpperLayerWeights, dims: LayerDims, x_in, pos_c, s_c, cu_kept, max_k: int,
-                    x_out=None, kcache=None, vcache=None, ws=None, events=None, rope_ready=False):
+                    x_out=None, kcache=None, vcache=None, ws=None, events=None, rope_ready=False,
+                    norms_folded=False, input_ssq=False):
     """One upper layer. ``events``: optional ctypes array of LAYER_STAGES + 1
     hipEvent_t handles; when given, the instrumented entry point records them
     between the layer's stages. ``rope_ready``: ``ws`` already holds the RoPE
-    table of these positions (an earlier layer of the same stack ran on it)."""
-    if rope_ready:
-        if ws is None:
-            raise ValueError("rope_ready needs the workspace that holds the table")
+    table of these positions (an earlier layer of the same stack ran on it).
+    ``norms_folded``: the weights went through fold_norm_weights and the RMSNorms
+    run fused into the GEMMs; ``input_ssq``: ``ws`` holds x_in's row sums of
+    squares from the previous folded layer of the stack."""
+    flags = (LAYER_ROPE_READY if rope_ready else 0) | (LAYER_NORMS_FOLDED if norms_folded else 0) | \
+        (LAYER_INPUT_SSQ if input_ssq else 0)
+    if (rope_ready or input_ssq) and ws is None:
+        raise ValueError("rope_ready / input_ssq need the workspace that holds the table / sums")
+    if flags:
         dims = LayerDims(*[getattr(dims, n) for n, _ in LayerDims._fields_])
-        dims.flags |= LAYER_ROPE_READY
+        dims.flags |= flags
     T = x_in.shape[0]
     B = cu_kept.numel() - 1
     dev = x_in.device

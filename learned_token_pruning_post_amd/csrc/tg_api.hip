@@ -48,12 +48,14 @@ inline tg_status launched(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ER
 bool layer_dims_ok(const tg_layer_dims* dm) {
   return dm->D > 0 && dm->Hq > 0 && dm->Hkv > 0 && dm->d > 0 && dm->I > 0 &&
          dm->Hq % dm->Hkv == 0 && dm->rms_eps >= 0.f && dm->rope_base > 0.f &&
-         (dm->flags & ~TG_LAYER_ROPE_READY) == 0;
+         (dm->flags & ~(TG_LAYER_ROPE_READY | TG_LAYER_NORMS_FOLDED | TG_LAYER_INPUT_SSQ)) == 0 &&
+         (!(dm->flags & TG_LAYER_INPUT_SSQ) || (dm->flags & TG_LAYER_NORMS_FOLDED));
 }
 
 tg_status layer_dims_supported(const tg_layer_dims* dm) {
   if (!dtype_ok(dm->dtype)) return TG_ERR_UNSUPPORTED;
   if (dm->d != 64 && dm->d != 128) return TG_ERR_UNSUPPORTED;
+  if ((dm->flags & TG_LAYER_NORMS_FOLDED) && dm->dtype != TG_BF16) return TG_ERR_UNSUPPORTED;
   if (dm->dtype == TG_BF16) {
     const int G = dm->Hq / dm->Hkv;
     if (G != 1 && G != 2 && G != 4) return TG_ERR_UNSUPPORTED;
@@ -77,7 +79,7 @@ const char* tg_status_string(tg_status s) {
   }
 }
 
-int tg_abi_version(void) { return (2 << 16) | 0; }
+int tg_abi_version(void) { return (3 << 16) | 0; }
 
 // ---------------------------------------------------------------------------
 size_t tg_gate_score_workspace_size(int64_t T_in, int D, int H1, tg_dtype dtype) {
@@ -195,6 +197,18 @@ tg_status tg_gated_attn_fwd(const void* q, const void* k, const void* v, const f
 }
 
 // ---------------------------------------------------------------------------
+tg_status tg_fold_norm_weights(const void* norm_w, void* W, int64_t rows, int cols,
+                               tg_dtype dtype, hipStream_t stream) {
+  TG_CHECK(rows >= 0 && cols >= 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(dtype_ok(dtype), TG_ERR_UNSUPPORTED);
+  if (rows == 0 || cols == 0) return TG_OK;
+  TG_CHECK(norm_w && W, TG_ERR_INVALID_ARG);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+  return launched(tg::launch_fold_norm(norm_w, W, rows, cols, dtype == TG_BF16, stream));
+}
+
+// ---------------------------------------------------------------------------
 tg_status tg_upper_layer_ws_layout(const tg_layer_dims* dm, int64_t T, tg_layer_ws_layout* out) {
   TG_CHECK(dm && out && T >= 0, TG_ERR_INVALID_ARG);
   TG_CHECK(layer_dims_ok(dm), TG_ERR_INVALID_ARG);
@@ -214,6 +228,8 @@ tg_status tg_upper_layer_ws_layout(const tg_layer_dims* dm, int64_t T, tg_layer_
   off += align_up(t * dm->I * e);
   out->rope = off;
   off += align_up(t * dm->d * sizeof(float));
+  out->ssq = off;  // [2][T][D/64] fp32, fused RMSNorm
+  off += align_up(2 * t * (size_t)((dm->D + 63) / 64) * sizeof(float));
   if (dm->dtype == TG_F32) {  // raw q|k|v and the up projection
     off += align_up(t * (dm->Hq + 2 * dm->Hkv) * dm->d * sizeof(float));
     off += align_up(t * dm->I * sizeof(float));
@@ -242,9 +258,10 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   if (st != TG_OK) return st;
   if (T == 0 || B == 0) return TG_OK;
   TG_CHECK(max_k > 0, TG_ERR_INVALID_ARG);
-  TG_CHECK(w->attn_norm && w->wq && w->wk && w->wv && w->wo && w->ffn_norm && w->wg && w->wu &&
-               w->wd && w->t && w->g,
+  const bool fused = (dm->flags & TG_LAYER_NORMS_FOLDED) != 0;
+  TG_CHECK(w->wq && w->wk && w->wv && w->wo && w->wg && w->wu && w->wd && w->t && w->g,
            TG_ERR_INVALID_ARG);
+  TG_CHECK(fused || (w->attn_norm && w->ffn_norm), TG_ERR_INVALID_ARG);
   TG_CHECK(x_in && x_out && pos_c && s_c && d_cu_kept && kcache && vcache, TG_ERR_INVALID_ARG);
   tg_layer_ws_layout L;
   st = tg_upper_layer_ws_layout(dm, T, &L);
@@ -260,6 +277,8 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   void* x1 = base + L.x1;
   void* act = base + L.act;
   float* rope = (float*)(base + L.rope);
+  float* ssq_x = (float*)(base + L.ssq);                   // x_in, then x_out
+  float* ssq_x1 = ssq_x + (size_t)T * (size_t)(dm->D / 64);  // x1
   const int M = (int)T;
   const int D = dm->D, Hq = dm->Hq, Hkv = dm->Hkv, d = dm->d, I = dm->I;
   const bool bf = dm->dtype == TG_BF16;
@@ -269,12 +288,16 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   if (!(dm->flags & TG_LAYER_ROPE_READY))
     TG_LAUNCH(tg::launch_rope_table(pos_c, T, d, dm->rope_base, rope, stream));
   TG_LAUNCH(mark(1));
-  TG_LAUNCH(tg::launch_rmsnorm(x_in, w->attn_norm, norm, T, D, dm->rms_eps, bf, stream));
+  if (!fused)
+    TG_LAUNCH(tg::launch_rmsnorm(x_in, w->attn_norm, norm, T, D, dm->rms_eps, bf, stream));
+  else if (!(dm->flags & TG_LAYER_INPUT_SSQ))
+    TG_LAUNCH(tg::launch_row_ssq(x_in, ssq_x, T, D, stream));
   TG_LAUNCH(mark(2));
   if (bf) {
     tg::QkvOut qo{(bf16*)qb, (bf16*)kcache, (bf16*)vcache, rope, Hq, Hkv, d};
-    TG_LAUNCH(tg::gemm_bf16_qkv((const bf16*)norm, (const bf16*)w->wq, (const bf16*)w->wk,
-                                (const bf16*)w->wv, qo, M, D, stream));
+    TG_LAUNCH(tg::gemm_bf16_qkv((const bf16*)(fused ? x_in : norm), (const bf16*)w->wq,
+                                (const bf16*)w->wk, (const bf16*)w->wv, qo, M, D, stream,
+                                fused ? ssq_x : nullptr, dm->rms_eps));
   } else {
     float* raw = (float*)(base + L.rope + align_up((size_t)T * d * sizeof(float)));
     const int ldr = (Hq + 2 * Hkv) * d;
@@ -292,20 +315,21 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   TG_LAUNCH(mark(4));
   if (bf) {
     TG_LAUNCH(tg::gemm_bf16_plain((const bf16*)attn, (const bf16*)w->wo, (const bf16*)x_in,
-                                  (bf16*)x1, M, D, Hq * d, stream));
+                                  (bf16*)x1, M, D, Hq * d, stream, fused ? ssq_x1 : nullptr));
   } else {
     TG_LAUNCH(tg::gemm_f32((const float*)attn, (const float*)w->wo, (const float*)x_in, (float*)x1,
                            M, D, Hq * d, D, stream));
   }
   TG_LAUNCH(mark(5));
-  TG_LAUNCH(tg::launch_rmsnorm(x1, w->ffn_norm, norm, T, D, dm->rms_eps, bf, stream));
+  if (!fused) TG_LAUNCH(tg::launch_rmsnorm(x1, w->ffn_norm, norm, T, D, dm->rms_eps, bf, stream));
   TG_LAUNCH(mark(6));
   if (bf) {
-    TG_LAUNCH(tg::gemm_bf16_swiglu((const bf16*)norm, (const bf16*)w->wg, (const bf16*)w->wu,
-                                   (bf16*)act, M, I, D, stream));
+    TG_LAUNCH(tg::gemm_bf16_swiglu((const bf16*)(fused ? x1 : norm), (const bf16*)w->wg,
+                                   (const bf16*)w->wu, (bf16*)act, M, I, D, stream,
+                                   fused ? ssq_x1 : nullptr, dm->rms_eps));
     TG_LAUNCH(mark(7));
     TG_LAUNCH(tg::gemm_bf16_plain((const bf16*)act, (const bf16*)w->wd, (const bf16*)x1,
-                                  (bf16*)x_out, M, D, I, stream));
+                                  (bf16*)x_out, M, D, I, stream, fused ? ssq_x : nullptr));
     return launched(mark(8));
   }
   float* raw = (float*)(base + L.rope + align_up((size_t)T * d * sizeof(float)));

@@ -66,6 +66,12 @@ struct GemmParams {
   const bf16* b2;
   float* s_out;
   float* partial;
+  // fused RMSNorm: row sums of squares [M][N/64] of the stored output (PLAIN),
+  // and of the input rows [M][K/64] that scale QKV / SwiGLU products by
+  // rsqrt(sum / K + rs_eps)
+  float* ssq_out;
+  const float* ssq_in;
+  float rs_eps;
 };
 
 // Buffer resources of the operands: W0..W2 (weights; QKV uses all three,
@@ -207,6 +213,20 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
                      __builtin_amdgcn_readfirstlane(base_lds + NW * i * 1024));
   };
 
+  // fused RMSNorm (QKV, SwiGLU): thread tid < BM requests the 64-feature sums
+  // of squares of token m0 + tid now; the epilogue reduces them
+  constexpr bool ROWSCALE = MODE == MODE_QKV || MODE == MODE_SWIGLU;
+  constexpr int SQV = 8;  // up to 32 slots prefetched as f32x4
+  const int nslot = K >> 6;
+  const bool sq_vec = ROWSCALE && p.ssq_in && (nslot & 3) == 0 && nslot <= 4 * SQV;
+  f32x4 sqv[ROWSCALE ? SQV : 1];
+  if (ROWSCALE && sq_vec && tid < BM && m0 + tid < p.M) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.ssq_in + (size_t)(m0 + tid) * nslot);
+#pragma unroll
+    for (int i = 0; i < SQV; ++i)
+      if (4 * i < nslot) sqv[i] = src[i];
+  }
+
   f32x16 acc[SN][SM];
 #pragma unroll
   for (int j = 0; j < SN; ++j)
@@ -318,6 +338,7 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
         const int r = r0 + lane / LPR, c = (lane % LPR) * 8;
         const int m = m0 + wm * TM + c0 * 32 + r;
         const int n = n0 + wn * TN + c;
+        float ss = 0.f;
         if (m < p.M && n < p.N) {
           const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + r * PADW + c);
           const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + r * PADW + c + 4);
@@ -330,8 +351,24 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
           }
           bf16x8 w;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) w[t] = f2bf(y[t]);
+          for (int t = 0; t < 8; ++t) {
+            w[t] = f2bf(y[t]);
+            const float f = bf2f(w[t]);
+            ss = fmaf(f, f, ss);
+          }
           *reinterpret_cast<bf16x8*>(p.out + o) = w;
+        }
+        if constexpr (TN == 64) {
+          // fused RMSNorm of the next projection: the 8 lanes of a row hold
+          // its 64 features of this wave; row shifts 1, 2, 4 gather their
+          // sum in lane 8c+7 (all lanes take part in the moves)
+          if (p.ssq_out) {
+            ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x111, 0xf, 0xf, false));
+            ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x112, 0xf, 0xf, false));
+            ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x114, 0xf, 0xf, false));
+            if ((lane & 7) == 7 && m < p.M && n < p.N)
+              p.ssq_out[(size_t)m * (p.N >> 6) + ((n0 + wn * TN) >> 6)] = ss;
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next round overwrites
@@ -357,6 +394,28 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     float* stg = reinterpret_cast<float*>(smem);
     auto fpos = [](int f) { return ((f >> 2) & 1) * (W / 2) + (f >> 3) * 4 + (f & 3); };
     constexpr int CPR = W / 8;  // chunks per staged row
+    // fused RMSNorm: 1 / rms of each token of the tile, after the staging rows
+    float* rstd_s = stg + CHT * RW;
+    static_assert(CHT * RW * 4 + BM * 4 <= STAGE * NSTAGE, "row scales fit in the LDS ring");
+    if (p.ssq_in) {
+      float rs = 1.f;
+      if (tid < BM) {
+        const int m = m0 + tid;
+        float a = 0.f;
+        if (m < p.M) {
+          if (sq_vec) {
+#pragma unroll
+            for (int i = 0; i < SQV; ++i)
+              if (4 * i < nslot) a += (sqv[i][0] + sqv[i][1]) + (sqv[i][2] + sqv[i][3]);
+          } else {
+            for (int sl = 0; sl < nslot; ++sl) a += p.ssq_in[(size_t)m * nslot + sl];
+          }
+        }
+        rs = rsqrtf(a / (float)K + p.rs_eps);
+      }
+      __syncthreads();  // the LDS ring is no longer read
+      if (tid < BM) rstd_s[tid] = rs;
+    }
     static_assert(MODE != MODE_QKV || (BN == 256 && NW * 64 == CHT * 8),
                   "QKV: one (token, head pair, 8-dim slice) task per thread and round");
     // QKV task of this thread: token row qr of the round, head pair qhp, slice qj
@@ -395,6 +454,7 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
                   f32x4{acc[j][i][rq * 4], acc[j][i][rq * 4 + 1], acc[j][i][rq * 4 + 2], acc[j][i][rq * 4 + 3]};
             }
         } else {
+          const float rs = p.ssq_in ? rstd_s[tl + ml] : 1.f;  // this lane's token
 #pragma unroll
           for (int jj = 0; jj < SN / 2; ++jj)
 #pragma unroll
@@ -402,7 +462,7 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
               f32x4 y;
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
-                const float gt = acc[2 * jj][i][rq * 4 + t], up = acc[2 * jj + 1][i][rq * 4 + t];
+                const float gt = acc[2 * jj][i][rq * 4 + t] * rs, up = acc[2 * jj + 1][i][rq * 4 + t] * rs;
                 y[t] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // v_rcp_f32: 1 ulp
               }
               *reinterpret_cast<f32x4*>(row + fpos(wn * (TN / 2) + jj * 32 + rq * 8 + half * 4)) = y;
@@ -414,6 +474,7 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
         const int m = m0 + c0 + qr;
         const int hd = p.hd, hh = hd >> 1;
         const float* row = stg + qr * RW;
+        const float rs = p.ssq_in ? rstd_s[c0 + qr] : 1.f;
         const float c[8] = {tab[0][0], tab[0][1], tab[0][2], tab[0][3], tab[1][0], tab[1][1], tab[1][2], tab[1][3]};
         const float sn[8] = {tab[2][0], tab[2][1], tab[2][2], tab[2][3], tab[3][0], tab[3][1], tab[3][2], tab[3][3]};
 #pragma unroll
@@ -426,8 +487,10 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
           const f32x4 lb = *reinterpret_cast<const f32x4*>(row + fpos(flo + 4));
           const f32x4 ha = *reinterpret_cast<const f32x4*>(row + fpos(fhi));
           const f32x4 hb = *reinterpret_cast<const f32x4*>(row + fpos(fhi + 4));
-          float ylo[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
-          float yhi[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+          float ylo[8] = {la[0] * rs, la[1] * rs, la[2] * rs, la[3] * rs,
+                          lb[0] * rs, lb[1] * rs, lb[2] * rs, lb[3] * rs};
+          float yhi[8] = {ha[0] * rs, ha[1] * rs, ha[2] * rs, ha[3] * rs,
+                          hb[0] * rs, hb[1] * rs, hb[2] * rs, hb[3] * rs};
           if (gh < p.Hq + p.Hkv) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -557,7 +620,7 @@ static hipError_t launch_auto(const GemmParams& p, int Ncols, hipStream_t stream
 }
 
 hipError_t gemm_bf16_plain(const bf16* X, const bf16* W, const bf16* resid, bf16* out, int M,
-                           int N, int K, hipStream_t stream) {
+                           int N, int K, hipStream_t stream, float* ssq_out) {
   if (M <= 0) return hipSuccess;
   GemmParams p{};
   p.X = X;
@@ -567,11 +630,13 @@ hipError_t gemm_bf16_plain(const bf16* X, const bf16* W, const bf16* resid, bf16
   p.W0 = W;
   p.resid = resid;
   p.out = out;
+  p.ssq_out = ssq_out;  // both PLAIN tilings have 64-feature wave tiles
   return launch_auto<MODE_PLAIN>(p, N, stream);
 }
 
 hipError_t gemm_bf16_qkv(const bf16* X, const bf16* wq, const bf16* wk, const bf16* wv,
-                         const QkvOut& o, int M, int K, hipStream_t stream) {
+                         const QkvOut& o, int M, int K, hipStream_t stream, const float* ssq_in,
+                         float eps) {
   if (M <= 0) return hipSuccess;
   GemmParams p{};
   p.X = X;
@@ -588,11 +653,13 @@ hipError_t gemm_bf16_qkv(const bf16* X, const bf16* wq, const bf16* wk, const bf
   p.Hq = o.Hq;
   p.Hkv = o.Hkv;
   p.hd = o.d;
+  p.ssq_in = ssq_in;
+  p.rs_eps = eps;
   return launch_auto<MODE_QKV>(p, p.N, stream);
 }
 
 hipError_t gemm_bf16_swiglu(const bf16* X, const bf16* wg, const bf16* wu, bf16* act, int M,
-                            int I, int K, hipStream_t stream) {
+                            int I, int K, hipStream_t stream, const float* ssq_in, float eps) {
   if (M <= 0) return hipSuccess;
   GemmParams p{};
   p.X = X;
@@ -603,6 +670,8 @@ hipError_t gemm_bf16_swiglu(const bf16* X, const bf16* wg, const bf16* wu, bf16*
   p.W1 = wu;
   p.act = act;
   p.I = I;
+  p.ssq_in = ssq_in;
+  p.rs_eps = eps;
   return launch_auto<MODE_SWIGLU>(p, 2 * I, stream);
 }
 

@@ -20,6 +20,13 @@ hipError_t launch_compact(const void* h, const int32_t* pos, const float* s, con
 hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int D, float eps,
                           bool is_bf16, hipStream_t stream);
 
+// fused RMSNorm: ssq[r, s] = sum of x[r, 64s .. 64s+63]^2 (bf16 x, fp32 ssq, D % 64 == 0)
+hipError_t launch_row_ssq(const void* x, float* ssq, int64_t rows, int D, hipStream_t stream);
+
+// W[r, c] *= w[c] (fp32 product, rounded to the storage type)
+hipError_t launch_fold_norm(const void* w, void* W, int64_t rows, int cols, bool is_bf16,
+                            hipStream_t stream);
+
 // cos/sin table [T, d] fp32: [.., i] = cos(pos*base^(-2i/d)), [.., d/2 + i] = sin(..)
 hipError_t launch_rope_table(const int32_t* pos, int64_t T, int d, float base, float* table,
                              hipStream_t stream);
@@ -33,12 +40,17 @@ struct QkvOut {
   int Hq, Hkv, d;
 };
 
+// Fused RMSNorm (all optional, NULL = off): ssq_out [M][N/64] receives the row
+// sums of squares of the stored output (PLAIN); with ssq_in [M][K/64] the QKV and
+// SwiGLU products of row m are scaled by rsqrt(sum(ssq_in[m]) / K + eps).
 hipError_t gemm_bf16_plain(const bf16* X, const bf16* W, const bf16* resid, bf16* out, int M,
-                           int N, int K, hipStream_t stream);
+                           int N, int K, hipStream_t stream, float* ssq_out = nullptr);
 hipError_t gemm_bf16_qkv(const bf16* X, const bf16* wq, const bf16* wk, const bf16* wv,
-                         const QkvOut& o, int M, int K, hipStream_t stream);
+                         const QkvOut& o, int M, int K, hipStream_t stream,
+                         const float* ssq_in = nullptr, float eps = 0.f);
 hipError_t gemm_bf16_swiglu(const bf16* X, const bf16* wg, const bf16* wu, bf16* act, int M,
-                            int I, int K, hipStream_t stream);
+                            int I, int K, hipStream_t stream, const float* ssq_in = nullptr,
+                            float eps = 0.f);
 // scorer; partial [nblk, M] fp32 scratch needed when H1 > 256 (nblk = ceil(H1/256))
 hipError_t gemm_bf16_score(const bf16* X, const bf16* W1, const bf16* b1, const bf16* w2,
                            const bf16* b2, float* s_out, float* partial, int M, int H1, int K,

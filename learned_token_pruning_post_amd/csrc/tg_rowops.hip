@@ -257,4 +257,70 @@ hipError_t launch_rope_table(const int32_t* pos, int64_t T, int d, float base, f
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Row sums of squares for the fused RMSNorm: ssq[r, s] = sum of x[r, c]^2
+// over the 64 features c = 64s..64s+63 (fp32), one thread per (row, slot):
+// consecutive threads read consecutive 128-byte segments of a row. The sum
+// is taken in the order of the GEMM epilogue that writes the same values for
+// the layer's later rows (8-feature fma chains, then pairwise), so a layer
+// reading sums from either source computes bit-identical results.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void row_ssq_bf16_kernel(const bf16* __restrict__ x,
+                                                           float* __restrict__ ssq, int64_t rows,
+                                                           int nslot) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * nslot) return;
+  const bf16x8* src = reinterpret_cast<const bf16x8*>(x) + idx * 8;
+  bf16x8 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = src[i];
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    c[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = bf2f(v[i][e]);
+      c[i] = fmaf(f, f, c[i]);
+    }
+  }
+  ssq[idx] = ((c[7] + c[6]) + (c[5] + c[4])) + ((c[3] + c[2]) + (c[1] + c[0]));
+}
+
+hipError_t launch_row_ssq(const void* x, float* ssq, int64_t rows, int D, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int nslot = D / 64;
+  const int64_t n = rows * nslot;
+  hipLaunchKernelGGL(row_ssq_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     (const bf16*)x, ssq, rows, nslot);
+  return hipGetLastError();
+}
+
+// Norm-weight folding: W[r, c] *= w[c] in fp32, rounded to the storage type.
+template <class T>
+__global__ __launch_bounds__(256) void fold_norm_kernel(const T* __restrict__ w, T* __restrict__ W,
+                                                        int64_t n, int cols) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % cols);
+  if constexpr (sizeof(T) == 2)
+    W[i] = f2bf(bf2f(W[i]) * bf2f(w[c]));
+  else
+    W[i] = W[i] * w[c];
+}
+
+hipError_t launch_fold_norm(const void* w, void* W, int64_t rows, int cols, bool is_bf16,
+                            hipStream_t stream) {
+  const int64_t n = rows * cols;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (is_bf16)
+    hipLaunchKernelGGL(fold_norm_kernel<bf16>, grid, dim3(256), 0, stream, (const bf16*)w, (bf16*)W,
+                       n, cols);
+  else
+    hipLaunchKernelGGL(fold_norm_kernel<float>, grid, dim3(256), 0, stream, (const float*)w,
+                       (float*)W, n, cols);
+  return hipGetLastError();
+}
+
 }  // namespace tg

@@ -30,8 +30,13 @@ def torch_dtype(w: Workload) -> torch.dtype:
 class DeviceWorkload:
     """Seeded inputs and weights of a workload, resident in HBM."""
 
-    def __init__(self, w: Workload, n_layers: Optional[int] = None, device="cuda", keep_host=False):
+    def __init__(self, w: Workload, n_layers: Optional[int] = None, device="cuda", keep_host=False,
+                 norms_folded: bool = False):
+        """``norms_folded`` (bf16): fold each layer's RMSNorm weights into its
+        projections once here, so the layers run with the norms fused into the
+        GEMMs (tg_layer_dims flag TG_LAYER_NORMS_FOLDED)."""
         self.w = w
+        self.norms_folded = bool(norms_folded) and w.dims.dtype == "bf16"
         self.device = device
         gi = gate_inputs(w)
         self.host_gate = gi if keep_host else None
@@ -58,6 +63,11 @@ class DeviceWorkload:
                     "wd": to_device(lw.wd, device),
                     "t": torch.from_numpy(lw.t).to(device), "g": torch.from_numpy(lw.g).to(device),
                 }
+                if self.norms_folded:
+                    for n in ("wq", "wk", "wv"):
+                        tg.fold_norm_weights(tens["attn_norm"], tens[n])
+                    for n in ("wg", "wu"):
+                        tg.fold_norm_weights(tens["ffn_norm"], tens[n])
                 self.layers.append(tg.UpperLayerWeights(tens))
         dm = w.dims
         self.dims = tg.layer_dims(dm.D, dm.Hq, dm.Hkv, dm.d, dm.I, torch_dtype(w), dm.rope_base, dm.rms_eps)
@@ -101,10 +111,13 @@ class GatedPrefill:
 
     def layer(self, l: int):
         d = self.dw
-        # layers after the first reuse the RoPE table the first one left in the workspace
+        # layers after the first reuse the RoPE table the first one left in the
+        # workspace and, with folded norms, the row sums of squares of their input
+        # that the previous layer's down projection wrote there
         tg.upper_layer_fwd(d.layers[l], d.dims, self.x, self.pos_c, self.s_c, d.cu_kept, d.w.max_k,
                            x_out=self.x, kcache=self.kcache[l], vcache=self.vcache[l], ws=self.ws,
-                           rope_ready=l > 0)
+                           rope_ready=l > 0, norms_folded=d.norms_folded,
+                           input_ssq=d.norms_folded and l > 0)
 
     def run(self):
         self.score()

@@ -44,7 +44,7 @@ def test_status_strings_and_version(L):
     for code in range(5):
         assert tg.status_string(code)
     assert tg.status_string(99) == "unknown status"
-    assert L.tg_abi_version() >> 16 == 2
+    assert L.tg_abi_version() >> 16 == 3
 
 
 def test_gate_score_argument_errors(L):
@@ -92,6 +92,19 @@ def test_attention_argument_errors(L):
     assert f(FAKE, FAKE, None, *([FAKE] * 4), 1, 64, 8, 4, 128, 1, FAKE, None, None, 0, None) == INVALID
 
 
+def test_fold_norm_weights_argument_errors(L):
+    f = L.tg_fold_norm_weights
+    assert f(FAKE, FAKE, -1, 8, 1, None) == INVALID
+    assert f(FAKE, FAKE, 8, -1, 1, None) == INVALID
+    assert f(None, FAKE, 8, 8, 1, None) == INVALID
+    assert f(FAKE, None, 8, 8, 0, None) == INVALID
+    assert f(FAKE, FAKE, 8, 8, 7, None) == UNSUP
+    assert f(None, None, 0, 8, 1, None) == OK  # empty
+    with pytest.raises(ValueError):
+        import torch
+        tg.fold_norm_weights(torch.ones(3, dtype=torch.bfloat16), torch.ones(2, 4, dtype=torch.bfloat16))
+
+
 def _dims(**kw):
     base = dict(D=256, Hq=4, Hkv=2, d=64, I=512, rope_base=1e6, rms_eps=1e-6, dtype=1)
     base.update(kw)
@@ -103,9 +116,10 @@ def test_layer_layout_and_errors(L):
     dm = _dims()
     lay = tg.LayerWsLayout()
     assert L.tg_upper_layer_ws_layout(ctypes.byref(dm), 1000, ctypes.byref(lay)) == OK
-    offs = [lay.norm, lay.q, lay.attn, lay.x1, lay.act, lay.rope, lay.total]
+    offs = [lay.norm, lay.q, lay.attn, lay.x1, lay.act, lay.rope, lay.ssq, lay.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay.q - lay.norm >= 1000 * 256 * 2 and lay.total - lay.rope >= 1000 * 64 * 4
+    assert lay.q - lay.norm >= 1000 * 256 * 2 and lay.ssq - lay.rope >= 1000 * 64 * 4
+    assert lay.total - lay.ssq >= 2 * 1000 * (256 // 64) * 4  # [2][T][D/64] fp32
     assert L.tg_upper_layer_workspace_size(ctypes.byref(dm), 1000, 1, 1000) == lay.total
     w = tg.LayerWeights(*([0x100000] * 11))
     f = L.tg_upper_layer_fwd
@@ -116,9 +130,23 @@ def test_layer_layout_and_errors(L):
     assert f(*args(_dims(Hq=6, Hkv=4), 1 << 40)) == INVALID
     assert f(*args(_dims(D=200), 1 << 40)) == UNSUP  # bf16 needs D % 64 == 0
     bad_flags = _dims()
-    bad_flags.flags = 2  # only TG_LAYER_ROPE_READY is defined
+    bad_flags.flags = 8  # TG_LAYER_ROPE_READY | NORMS_FOLDED | INPUT_SSQ are the defined bits
     assert f(*args(bad_flags, 1 << 40)) == INVALID
     assert L.tg_upper_layer_ws_layout(ctypes.byref(bad_flags), 1000, ctypes.byref(lay)) == INVALID
+    ssq_alone = _dims()
+    ssq_alone.flags = tg.LAYER_INPUT_SSQ  # needs NORMS_FOLDED
+    assert f(*args(ssq_alone, 1 << 40)) == INVALID
+    folded32 = _dims(dtype=0)
+    folded32.flags = tg.LAYER_NORMS_FOLDED  # bf16 only
+    assert f(*args(folded32, 1 << 40)) == UNSUP
+    # folded norms: the norm weight pointers may be NULL (rejected without the flag)
+    w_nonorm = tg.LayerWeights(None, *([0x100000] * 4), None, *([0x100000] * 5))
+    no_norm = (ctypes.byref(w_nonorm), ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1000, 1000,
+               FAKE, FAKE, FAKE, 16, None)
+    assert f(*no_norm) == INVALID
+    folded = _dims()
+    folded.flags = tg.LAYER_NORMS_FOLDED | tg.LAYER_INPUT_SSQ
+    assert f(ctypes.byref(w_nonorm), *no_norm[1:1], ctypes.byref(folded), *no_norm[2:]) == WS
     assert f(None, ctypes.byref(dm), *([FAKE] * 5), 1, 1000, 1000, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
     # fp32 layout carries the raw projections too
     lay32 = tg.LayerWsLayout()

@@ -29,10 +29,10 @@ def gpu():
     tg.lib()  # raises loudly if the HIP library is missing
 
 
-def _stage_parity(w, score_rows=None, layer_rows_per_seq=None, seed=0):
+def _stage_parity(w, score_rows=None, layer_rows_per_seq=None, seed=0, norms_folded=False):
     dt = w.dims.dtype
-    say("workload", w.name, "N", w.N[:3], "K", w.K[:3], "T", w.T)
-    dw = DeviceWorkload(w, n_layers=1, keep_host=True)
+    say("workload", w.name, "N", w.N[:3], "K", w.K[:3], "T", w.T, "folded norms" if norms_folded else "")
+    dw = DeviceWorkload(w, n_layers=1, keep_host=True, norms_folded=norms_folded)
     gi = dw.host_gate
     gp = GatedPrefill(dw)
 
@@ -112,6 +112,12 @@ def test_stages_qwen32k(k):
                   layer_rows_per_seq=None if k <= 2048 else 384)
 
 
+def test_stages_qwen32k_folded_norms():
+    """The benchmark's launch configuration: RMSNorms fused into the GEMMs."""
+    _stage_parity(workload("qwen32k", k=4096, layers=1), score_rows=8192, layer_rows_per_seq=384,
+                  norms_folded=True)
+
+
 @pytest.mark.parametrize("n", [65536, 131072])
 def test_stages_long(n):
     _stage_parity(workload("long", n=n), score_rows=8192, layer_rows_per_seq=384)
@@ -121,18 +127,21 @@ def test_stages_multibudget():
     _stage_parity(workload("multibudget"), score_rows=8192, layer_rows_per_seq=96)
 
 
-def test_stages_ragged_small_bf16():
+@pytest.mark.parametrize("folded", [False, True])
+def test_stages_ragged_small_bf16(folded):
     dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=96, dtype="bf16")
     w = custom(21, N=[300, 1, 77, 1000], K=[150, 1, 77, 333], F=1, dims=dims)
-    _stage_parity(w)
+    _stage_parity(w, norms_folded=folded)
 
 
-def test_stages_ragged_bf16_k_and_v_head_in_one_pair():
+@pytest.mark.parametrize("folded", [False, True])
+def test_stages_ragged_bf16_k_and_v_head_in_one_pair(folded):
     # Hq + Hkv odd: the QKV epilogue's head pair (2, 3) of the only 256-feature
-    # tile holds the k head (rotated) and the v head (not rotated)
+    # tile holds the k head (rotated) and the v head (not rotated). D = 128
+    # also takes the fused norm's scalar path (D/64 = 2 sums per row).
     dims = ModelDims(D=128, Hq=2, Hkv=1, d=64, I=256, H1=64, dtype="bf16")
     w = custom(23, N=[97, 260], K=[40, 130], F=2, dims=dims)
-    _stage_parity(w)
+    _stage_parity(w, norms_folded=folded)
 
 
 def test_stages_ragged_gqa4_fp32_d128():
@@ -167,6 +176,83 @@ def test_layer_stack_reuses_rope_table():
     _, q_r, k_r, v_r = O.qkv_rope(f64(x_in), gp.pos_c.cpu().numpy(), W, w.dims, rows=rows)
     e = assert_close(f64(reuse[1])[rows], k_r[rows], w.dims.dtype, "layer-1 k cache")
     say("  layer 1 on the reused RoPE table: bit-identical to a rebuilt one; k err %.3g" % e)
+
+
+def test_layer_stack_folded_norms_reuses_input_sums():
+    """With folded norms, layer 1 reads its input's row sums of squares from the
+    workspace, as written by layer 0's down projection (TG_LAYER_INPUT_SSQ): its
+    outputs equal a run on a fresh workspace, where a kernel of its own computes
+    them, bit for bit; x out and the k cache match the oracle."""
+    w = workload("qwen8k", layers=2)
+    dw = DeviceWorkload(w, n_layers=2, keep_host=True, norms_folded=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    gp.select()
+    gp.compact()
+    gp.layer(0)
+    x_in = gp.x.clone()
+    gp.layer(1)
+    torch.cuda.synchronize()
+    reuse = (gp.x.clone(), gp.kcache[1].clone(), gp.vcache[1].clone())
+    fresh_ws = torch.zeros_like(gp.ws)
+    x2, k2, v2, _ = tg.upper_layer_fwd(dw.layers[1], dw.dims, x_in, gp.pos_c, gp.s_c, dw.cu_kept,
+                                       w.max_k, ws=fresh_ws, norms_folded=True)
+    torch.cuda.synchronize()
+    for a, b, name in zip(reuse, (x2, k2, v2), ("x out", "k cache", "v cache")):
+        assert torch.equal(a, b), name
+    W = layer_dict(dw.host_layers[1])
+    rows = sample_rows(dw.host_gate.cu_kept, 256, 1)
+    _, q_r, k_r, v_r = O.qkv_rope(f64(x_in), gp.pos_c.cpu().numpy(), W, w.dims, rows=rows)
+    e = assert_close(f64(reuse[1])[rows], k_r[rows], w.dims.dtype, "layer-1 k cache")
+    say("  layer 1 on its input sums from layer 0: bit-identical to a fresh run; k err %.3g" % e)
+
+
+def test_folded_norm_weights_not_ones():
+    """Fold non-unit norm weights into the projections and run the fused layer:
+    every stage matches the oracle evaluated with the unfolded weights."""
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=64, dtype="bf16")
+    w = custom(24, N=[200, 333], K=[120, 200], F=4, dims=dims)
+    dw = DeviceWorkload(w, n_layers=1, keep_host=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    gp.select()
+    gp.compact()
+    torch.cuda.synchronize()
+    lw = dw.host_layers[0]
+    rng = np.random.default_rng(5)
+    t = dict(dw.layers[0].tensors)
+    norms = {}
+    for n in ("attn_norm", "ffn_norm"):
+        v = torch.from_numpy(rng.uniform(0.5, 1.5, dims.D).astype(np.float32)).to(torch.bfloat16)
+        norms[n] = v.float().numpy().astype(np.float64)
+        t[n] = v.cuda()
+    for n in ("wq", "wk", "wv", "wg", "wu"):
+        t[n] = t[n].clone()
+    for n in ("wq", "wk", "wv"):
+        tg.fold_norm_weights(t["attn_norm"], t[n])
+    for n in ("wg", "wu"):
+        tg.fold_norm_weights(t["ffn_norm"], t[n])
+    # the fold is W * w rounded to bf16, column by column
+    ref_fold = (f64(dw.layers[0].tensors["wq"]) * norms["attn_norm"][None, :]).astype(np.float32)
+    assert np.array_equal(bits(t["wq"]), bits(torch.from_numpy(ref_fold).to(torch.bfloat16)))
+    x_in = gp.x.clone()
+    x_out, k_g, v_g, ws = tg.upper_layer_fwd(tg.UpperLayerWeights(t), dw.dims, x_in, gp.pos_c, gp.s_c,
+                                             dw.cu_kept, w.max_k, norms_folded=True)
+    torch.cuda.synchronize()
+    W = layer_dict(lw)
+    W["attn_norm"], W["ffn_norm"] = norms["attn_norm"], norms["ffn_norm"]
+    lay = tg.upper_layer_ws_layout(dw.dims, w.T)
+    T = w.T
+    x_in64 = f64(x_in)
+    _, q_r, k_r, v_r = O.qkv_rope(x_in64, gp.pos_c.cpu().numpy(), W, dims)
+    assert_close(f64(k_g), k_r, "bf16", "k cache")
+    assert_close(f64(v_g), v_r, "bf16", "v cache")
+    assert_close(f64(ws_view(ws, lay.q, (T, dims.Hq, dims.d), torch.bfloat16)), q_r, "bf16", "q")
+    x1_g = f64(ws_view(ws, lay.x1, (T, dims.D), torch.bfloat16))
+    act_g = f64(ws_view(ws, lay.act, (T, dims.I), torch.bfloat16))
+    _, act_r = O.swiglu_act(x1_g, W, dims.rms_eps)
+    assert_close(act_g, act_r, "bf16", "swiglu act")
+    assert_close(f64(x_out), O.down_proj(x1_g, act_g, W["wd"]), "bf16", "x out")
 
 
 def test_scorer_wide_hidden_uses_partials():
