@@ -213,18 +213,21 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
                      __builtin_amdgcn_readfirstlane(base_lds + NW * i * 1024));
   };
 
-  // fused RMSNorm (QKV, SwiGLU): thread tid < BM requests the 64-feature sums
-  // of squares of token m0 + tid now; the epilogue reduces them
+  // fused RMSNorm (QKV, SwiGLU): threads 2t and 2t+1 request one half each of
+  // the 64-feature sums of squares of token m0 + t now (held through the main
+  // loop: 16 registers, not 32); the epilogue reduces them. Loading them in
+  // the epilogue instead exposes their latency once per tile.
   constexpr bool ROWSCALE = MODE == MODE_QKV || MODE == MODE_SWIGLU;
-  constexpr int SQV = 8;  // up to 32 slots prefetched as f32x4
+  constexpr int SQV = 4;  // f32x4 per thread: up to 32 slots per token
   const int nslot = K >> 6;
-  const bool sq_vec = ROWSCALE && p.ssq_in && (nslot & 3) == 0 && nslot <= 4 * SQV;
+  const bool sq_vec = ROWSCALE && p.ssq_in && (nslot & 7) == 0 && nslot <= 8 * SQV;
   f32x4 sqv[ROWSCALE ? SQV : 1];
-  if (ROWSCALE && sq_vec && tid < BM && m0 + tid < p.M) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.ssq_in + (size_t)(m0 + tid) * nslot);
+  if (ROWSCALE && sq_vec && (tid >> 1) < BM && m0 + (tid >> 1) < p.M) {
+    const f32x4* src =
+        reinterpret_cast<const f32x4*>(p.ssq_in + (size_t)(m0 + (tid >> 1)) * nslot) + (tid & 1) * (nslot >> 3);
 #pragma unroll
     for (int i = 0; i < SQV; ++i)
-      if (4 * i < nslot) sqv[i] = src[i];
+      if (8 * i < nslot) sqv[i] = src[i];
   }
 
   f32x16 acc[SN][SM];
@@ -399,22 +402,25 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     static_assert(CHT * RW * 4 + BM * 4 <= STAGE * NSTAGE, "row scales fit in the LDS ring");
     if (p.ssq_in) {
       float rs = 1.f;
-      if (tid < BM) {
+      if (sq_vec) {
+        float a = 0.f;
+        if ((tid >> 1) < BM && m0 + (tid >> 1) < p.M) {
+#pragma unroll
+          for (int i = 0; i < SQV; ++i)
+            if (8 * i < nslot) a += (sqv[i][0] + sqv[i][1]) + (sqv[i][2] + sqv[i][3]);
+        }
+        // add the other half from lane ^ 1 (quad_perm 1,0,3,2; every lane takes part)
+        a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xb1, 0xf, 0xf, false));
+        rs = rsqrtf(a / (float)K + p.rs_eps);
+      } else if (tid < BM) {
         const int m = m0 + tid;
         float a = 0.f;
-        if (m < p.M) {
-          if (sq_vec) {
-#pragma unroll
-            for (int i = 0; i < SQV; ++i)
-              if (4 * i < nslot) a += (sqv[i][0] + sqv[i][1]) + (sqv[i][2] + sqv[i][3]);
-          } else {
-            for (int sl = 0; sl < nslot; ++sl) a += p.ssq_in[(size_t)m * nslot + sl];
-          }
-        }
+        if (m < p.M)
+          for (int sl = 0; sl < nslot; ++sl) a += p.ssq_in[(size_t)m * nslot + sl];
         rs = rsqrtf(a / (float)K + p.rs_eps);
       }
       __syncthreads();  // the LDS ring is no longer read
-      if (tid < BM) rstd_s[tid] = rs;
+      if (sq_vec ? ((tid >> 1) < BM && (tid & 1) == 0) : tid < BM) rstd_s[sq_vec ? (tid >> 1) : tid] = rs;
     }
     static_assert(MODE != MODE_QKV || (BN == 256 && NW * 64 == CHT * 8),
                   "QKV: one (token, head pair, 8-dim slice) task per thread and round");
