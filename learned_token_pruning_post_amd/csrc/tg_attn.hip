@@ -96,11 +96,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
   // (sequence, kv-head), one tile after the other, so every workgroup sees
   // about n_qt + 1 key tiles. Consecutive L differ in kv-head first: with 8
   // kv-heads, each XCD (L % 8) serves one head, whose K and V stay in its L2.
+  // Then pairs, then sequences: the workgroups of one sequence are dispatched
+  // together, so those of a head sweep its keys at about the same time and
+  // share K/V tiles in L2 (with the sequences interleaved, a 16K-key sequence
+  // next to short ones ran 3x slower).
   const int L = blockIdx.x;
-  const int per = Hkv * B;
-  const int p = L / per;
-  const int rem = L - p * per;
-  const int hk = rem % Hkv, b = rem / Hkv;
+  const int npair = (n_qt + 1) >> 1;
+  const int hk = L % Hkv;
+  const int p = (L / Hkv) % npair, b = L / (Hkv * npair);
   const int seq0 = cu_kept[b];
   const int Kb = cu_kept[b + 1] - seq0;
   const int Ttot = cu_kept[B];

@@ -255,6 +255,19 @@ def test_folded_norm_weights_not_ones():
     assert_close(f64(x_out), O.down_proj(x1_g, act_g, W["wd"]), "bf16", "x out")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fold_norm_weights_ragged_shapes(dtype):
+    """W[r, c] * w[c] rounded once to the dtype, for rows/cols that are not tile multiples."""
+    g = torch.Generator().manual_seed(7)
+    for rows, cols in [(1, 1), (37, 129), (300, 64)]:
+        W = torch.randn(rows, cols, generator=g).to(dtype)
+        wn = (torch.rand(cols, generator=g) + 0.5).to(dtype)
+        ref = (W.double() * wn.double()[None, :]).float().to(dtype)
+        got = tg.fold_norm_weights(wn.cuda(), W.cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(got.cpu(), ref), (rows, cols)
+
+
 def test_scorer_wide_hidden_uses_partials():
     dims = ModelDims(D=128, Hq=2, Hkv=1, d=64, I=128, H1=600, dtype="bf16")
     w = custom(23, N=[777], K=[10], F=2, dims=dims)
