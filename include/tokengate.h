@@ -55,6 +55,7 @@ typedef int tg_status;
 #define TG_DEV_FORCED_GT_BUDGET 1 /* more forced tokens than K_b: kept slots of b are -1 */
 #define TG_DEV_BUDGET_GT_LEN    2 /* K_b > N_b: kept slots of b are -1 */
 #define TG_DEV_NAN_SCORE        4 /* a score of b is NaN (informational; NaN ranks lowest) */
+#define TG_DEV_LEN_GT_MAX_N     8 /* N_b > max_n passed by the host: kept slots of b are -1 */
 
 typedef enum tg_dtype { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
 
@@ -97,7 +98,11 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1,
  *  keep_mask [T_in]   uint8, 1 = unprunable; NULL = nothing forced
  *  d_cu_in   [B+1]    int32 device, prefix sums of N_b (d_cu_in[0] = 0, d_cu_in[B] = T_in)
  *  d_cu_kept [B+1]    int32 device, prefix sums of K_b (d_cu_kept[B] = T)
- *  max_n              an upper bound of every N_b (chooses the kernel variant)
+ *  max_n              an upper bound of every N_b: up to 32768 the keys of a
+ *                     sequence stay in LDS after one load; above, the kernel
+ *                     walks every sequence in rounds of 32768 tokens, reloading
+ *                     each round before each pass (a sequence longer than max_n
+ *                     gets TG_DEV_LEN_GT_MAX_N)
  *  kept_idx  [T]      int32 out: GLOBAL row indices into s/h, ascending inside
  *                     each sequence, at that sequence's cu_kept offsets
  *  d_status  [B]      int32 device out, TG_DEV_* flags of each sequence

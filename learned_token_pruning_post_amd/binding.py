@@ -22,6 +22,7 @@ TG_BF16 = 1
 DEV_FORCED_GT_BUDGET = 1
 DEV_BUDGET_GT_LEN = 2
 DEV_NAN_SCORE = 4
+DEV_LEN_GT_MAX_N = 8
 
 # every entry point declared in include/tokengate.h
 ABI_FUNCTIONS = (

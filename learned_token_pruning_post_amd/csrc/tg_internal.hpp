@@ -8,8 +8,8 @@
 namespace tg {
 
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
-                              const int32_t* cu_kept, int B, int32_t* kept, int32_t* status,
-                              hipStream_t stream);
+                              const int32_t* cu_kept, int B, int max_n, int32_t* kept,
+                              int32_t* status, hipStream_t stream);
 
 hipError_t launch_compact(const void* h, const int32_t* pos, const float* s, const int32_t* kept,
                           const int32_t* cu_in, const int32_t* cu_kept, int B, int64_t T,

@@ -335,6 +335,43 @@ def test_select_all_equal_and_budget_extremes():
     assert np.array_equal(kept, ref.astype(np.int32)) and not status.any()
 
 
+def test_select_rounds_ties_across_rounds():
+    """Sequences longer than one LDS round (32768 tokens): equal scores whose ties
+    straddle rounds, forced tokens in every round, a ragged last round."""
+    N = [100003, 32769, 65536, 7]
+    K = [50001, 32768, 40000, 7]
+    T_in = sum(N)
+    s = np.full(T_in, 0.25, np.float32)
+    rng = np.random.default_rng(3)
+    s[N[0]:N[0] + N[1]] = rng.integers(0, 5, N[1]).astype(np.float32)  # 5 levels, heavy ties
+    s[N[0] + N[1]:] = scores_with_ties(4, N[2] + N[3], 11)
+    mask = np.zeros(T_in, np.uint8)
+    mask[rng.choice(N[0], 300, replace=False)] = 1
+    mask[N[0] + rng.choice(N[1], 50, replace=False)] = 1
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, flags = O.topk_select(s, mask, cu_in, cu_k)
+    assert np.array_equal(status, flags.astype(np.int32))
+    assert np.array_equal(kept, ref.astype(np.int32))
+
+
+def test_select_sequence_longer_than_max_n_is_flagged():
+    """The one-round kernel (max_n <= 32768) on a longer sequence: that
+    sequence is flagged and its slots are -1; the others are selected."""
+    dev = "cuda"
+    N, K = [40000, 1000], [10, 20]
+    s = scores_with_ties(5, sum(N), 7)
+    cu_in = np.concatenate([[0], np.cumsum(N)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
+    kept, status = tg.topk_select(torch.from_numpy(s).to(dev), None, torch.from_numpy(cu_in).to(dev),
+                                  torch.from_numpy(cu_k).to(dev), int(cu_k[-1]), 32768)
+    torch.cuda.synchronize()
+    kept, status = kept.cpu().numpy(), status.cpu().numpy()
+    assert status[0] == tg.DEV_LEN_GT_MAX_N and status[1] == 0
+    assert (kept[:10] == -1).all()
+    ref, _ = O.topk_select(s, np.zeros(sum(N), np.uint8), cu_in, cu_k)
+    assert np.array_equal(kept[10:], ref[10:].astype(np.int32))
+
+
 def test_select_error_flags():
     N = [10, 10, 10]
     K = [3, 11, 4]  # seq 0: 5 forced > 3; seq 1: K > N
