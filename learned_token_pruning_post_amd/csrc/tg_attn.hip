@@ -74,7 +74,7 @@ template <int G, int HD>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ s_c, const float* __restrict__ t, const float* __restrict__ g,
-    const int32_t* __restrict__ cu_kept, int B, int Hq, int Hkv, int n_qt, bf16* __restrict__ o,
+    const int32_t* __restrict__ cu_kept, int B, int Hq, int Hkv, int n_qt, int single, bf16* __restrict__ o,
     float* __restrict__ lse) {
   using LY = AttnLayout<HD>;
   constexpr int WPH = 4 / G;     // waves per q-head in a group
@@ -100,8 +100,10 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
   // together, so those of a head sweep its keys at about the same time and
   // share K/V tiles in L2 (with the sequences interleaved, a 16K-key sequence
   // next to short ones ran 3x slower).
+  // With `single` (few query tiles: pairing would leave CUs idle) workgroup
+  // L takes only the tile n_qt-1-p, p < n_qt, heavy tiles first.
   const int L = blockIdx.x;
-  const int npair = (n_qt + 1) >> 1;
+  const int npair = single ? n_qt : (n_qt + 1) >> 1;
   const int hk = L % Hkv;
   const int p = (L / Hkv) % npair, b = L / (Hkv * npair);
   const int seq0 = cu_kept[b];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
 
   for (int pass = 0; pass < 2; ++pass) {
     const int qt = pass == 0 ? n_qt - 1 - p : p;
-    if (pass == 1 && qt == n_qt - 1 - p) break;  // middle tile of an odd count
+    if (pass == 1 && (single || qt == n_qt - 1 - p)) break;  // (or the middle tile of an odd count)
     const int q0 = qt * BQ;
     if (q0 >= Kb) continue;  // uniform over the workgroup
     const int qw0 = q0 + qs * 32;
@@ -440,11 +442,14 @@ static hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, 
     attr_set = true;
   }
   const int n_qt = (max_k + BQ - 1) / BQ;
-  const long blocks = (long)((n_qt + 1) / 2) * Hkv * B;  // one query-tile pair each
+  // one query-tile pair per workgroup; single tiles while they fit one
+  // workgroup per CU
+  const int single = (long)n_qt * Hkv * B <= 256;
+  const long blocks = (long)(single ? n_qt : (n_qt + 1) / 2) * Hkv * B;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((attn_bf16_kernel<G, HD>), dim3((unsigned)blocks), dim3(512), lds, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, s_c, t, g, cu_kept, B, Hq,
-                     Hkv, n_qt, (bf16*)o, lse);
+                     Hkv, n_qt, single, (bf16*)o, lse);
   return hipGetLastError();
 }
 

@@ -448,6 +448,34 @@ def test_attention_varlen(dtype, G, d):
     assert torch.equal(o, o2)  # deterministic
 
 
+@pytest.mark.parametrize("G,d", [(1, 128), (4, 64)])
+def test_attention_many_short_sequences(G, d):
+    """Enough query tiles that workgroups take pairs of them (heavy, light),
+    next to the few-tile batches above, where each takes one tile."""
+    rng = np.random.default_rng(54)
+    lens = [int(x) for x in rng.integers(0, 300, size=90)] + [300, 1]
+    T = sum(lens)
+    Hkv = 2
+    Hq = Hkv * G
+    q = activations(54, 1, (T, Hq, d), "bf16")
+    k = activations(54, 2, (T, Hkv, d), "bf16")
+    v = activations(54, 3, (T, Hkv, d), "bf16")
+    s_c = rng.random(T).astype(np.float32)
+    t = rng.uniform(0.8, 1.2, Hq).astype(np.float32)
+    g = rng.uniform(0.0, 2.0, Hq).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    BQ = 32 * (4 // G)
+    assert -(-max(lens) // BQ) * Hkv * len(lens) > 256  # paired tiles
+    dev = "cuda"
+    o, lse = tg.gated_attn_fwd(to_device(q), to_device(k), to_device(v), torch.from_numpy(s_c).to(dev),
+                               torch.from_numpy(t).to(dev), torch.from_numpy(g).to(dev),
+                               torch.from_numpy(cu).to(dev), max(lens), want_lse=True)
+    torch.cuda.synchronize()
+    o_r, lse_r = O.gated_attention(q.value, k.value, v.value, s_c, t, g, cu)
+    assert_close(f64(o), o_r, "bf16", "attention out")
+    assert_close(lse.cpu().numpy(), lse_r, "bf16", "lse")
+
+
 def test_attention_bias_reduces_to_plain_when_gain_zero():
     """g = 0: the kernel's result must not depend on s_c at all."""
     lens = [300, 257]
