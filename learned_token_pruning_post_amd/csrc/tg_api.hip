@@ -310,15 +310,8 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
                                      Hkv, d, stream));
   }
   TG_LAUNCH(mark(3));
-  // the O, gate/up and down weights are pulled into the memory-side cache
-  // while attention runs (each layer's weights are otherwise cold)
-  const auto wbytes = [](size_t n) { return (uint32_t)(n < 0xffffffffu ? n : 0xffffffffu); };
-  const size_t esz = elt_size(dm->dtype);
-  const tg::CacheWarm warm{{w->wo, w->wg, w->wu, w->wd},
-                           {wbytes((size_t)D * Hq * d * esz), wbytes((size_t)dm->I * D * esz),
-                            wbytes((size_t)dm->I * D * esz), wbytes((size_t)D * dm->I * esz)}};
   TG_LAUNCH(tg::attn_fwd(qb, kcache, vcache, s_c, w->t, w->g, d_cu_kept, B, max_k, Hq, Hkv, d, bf,
-                         attn, nullptr, stream, &warm));
+                         attn, nullptr, stream));
   TG_LAUNCH(mark(4));
   if (bf) {
     TG_LAUNCH(tg::gemm_bf16_plain((const bf16*)attn, (const bf16*)w->wo, (const bf16*)x_in,

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ s_c, const float* __restrict__ t, const float* __restrict__ g,
     const int32_t* __restrict__ cu_kept, int B, int Hq, int Hkv, int n_qt, int single, bf16* __restrict__ o,
-    float* __restrict__ lse, CacheWarm warm) {
+    float* __restrict__ lse) {
   using LY = AttnLayout<HD>;
   constexpr int WPH = 4 / G;     // waves per q-head in a group
   constexpr int BQ = 32 * WPH;   // queries per query tile
@@ -179,40 +179,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
     voff[db] = vkey_lo * LY::RB + (((d >> 3) ^ LY::vswz(vkey_lo)) << 4) + (d & 7) * 2;
   }
   const int ksw = LY::kswz(l31);  // same for key l31 and 32 + l31
-
-  // Cache warm-up: the ranges in `warm` are cut into 8 KB chunks (one dword
-  // per 128-byte line, 64 lanes) and workgroup L takes a contiguous share;
-  // in every key-tile step waves 0 and 1 each touch one chunk, landing the
-  // dwords in a scratch LDS word range that nothing reads. The step's
-  // vmcnt(0) wait then also covers these loads, issued a whole step earlier.
-  int wchunk = 0, wend = 0;
-  {
-    int total = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) total += (int)((warm.bytes[r] + 8191u) >> 13);
-    const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-    wchunk = min(total, L * per);
-    wend = min(total, wchunk + per);
-  }
-  const uint32_t wjunk = glds - grp * LY::BYTES + 2 * LY::BYTES;
-  auto warm_step = [&]() {
-    if (wave8 < 2) {
-      const int c = wchunk + wave8;
-      if (c < wend) {
-        int rc = c;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int nr = (int)((warm.bytes[r] + 8191u) >> 13);
-          if (rc >= 0 && rc < nr) {
-            const i32x4 rw = make_rsrc(warm.p[r], warm.bytes[r]);
-            buf_dma4(rw, ((uint32_t)rc << 13) + (uint32_t)lane * 128u, wjunk);
-          }
-          rc -= nr;
-        }
-      }
-    }
-    wchunk += 2;
-  };
   const bf16x2 ones = {f2bf(1.f), f2bf(1.f)};
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -285,7 +251,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(
       __syncthreads();  // K/scores of tile j+1 and V of tile j landed; slots of j-1 free
       if (j + 2 < nt) issue_k(t0 + j + 2, j & 1);
       if (j + 1 < nt) issue_v(t0 + j + 1, (j + 1) & 1);
-      if (j + 1 < nh) warm_step();  // (the last step's wait would not cover it)
       if (j >= nt || j > jw) continue;  // uniform per wave; it stays for the barriers
       const int kbase = (t0 + j) * 64;
       // keys past a query (diagonal tiles only) -> -inf
@@ -466,9 +431,9 @@ template <int G, int HD>
 static hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const float* s_c,
                                    const float* t, const float* g, const int32_t* cu_kept, int B,
                                    int max_k, int Hq, int Hkv, void* o, float* lse,
-                                   hipStream_t stream, const CacheWarm& warm) {
+                                   hipStream_t stream) {
   constexpr int BQ = 32 * (4 / G);
-  constexpr size_t lds = (size_t)2 * AttnLayout<HD>::BYTES + 256;  // + the warm-up scratch
+  constexpr size_t lds = (size_t)2 * AttnLayout<HD>::BYTES;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, HD>,
@@ -484,15 +449,13 @@ static hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, 
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((attn_bf16_kernel<G, HD>), dim3((unsigned)blocks), dim3(512), lds, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, s_c, t, g, cu_kept, B, Hq,
-                     Hkv, n_qt, single, (bf16*)o, lse, warm);
+                     Hkv, n_qt, single, (bf16*)o, lse);
   return hipGetLastError();
 }
 
 hipError_t attn_fwd(const void* q, const void* k, const void* v, const float* s_c, const float* t,
                     const float* g, const int32_t* cu_kept, int B, int max_k, int Hq, int Hkv,
-                    int d, bool is_bf16, void* o, float* lse, hipStream_t stream,
-                    const CacheWarm* warm) {
-  const CacheWarm none{};
+                    int d, bool is_bf16, void* o, float* lse, hipStream_t stream) {
   if (B <= 0 || max_k <= 0) return hipSuccess;
   if (!is_bf16) {
     dim3 grid((max_k + 63) / 64, Hq, B);
@@ -510,7 +473,7 @@ hipError_t attn_fwd(const void* q, const void* k, const void* v, const float* s_
 #define TG_ATTN_CASE(GG, DD)                                                                    \
   if (G == GG && d == DD)                                                                       \
     return launch_attn_bf16<GG, DD>(q, k, v, s_c, t, g, cu_kept, B, max_k, Hq, Hkv, o, lse, \
-                                    stream, warm ? *warm : none);
+                                    stream);
   TG_ATTN_CASE(1, 64)
   TG_ATTN_CASE(2, 64)
   TG_ATTN_CASE(4, 64)

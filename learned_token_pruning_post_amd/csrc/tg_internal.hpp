@@ -68,17 +68,8 @@ hipError_t swiglu_f32(const float* gate, const float* up, float* act, int64_t n,
                       hipStream_t stream);
 
 // ---- attention ----
-// Up to four device byte ranges that the bf16 attention kernel pulls into the
-// memory-side cache while it runs (a hint: no result depends on it). The layer
-// passes the weights of the projections that follow attention, which would
-// otherwise start cold.
-struct CacheWarm {
-  const void* p[4];
-  uint32_t bytes[4];
-};
 hipError_t attn_fwd(const void* q, const void* k, const void* v, const float* s_c, const float* t,
                     const float* g, const int32_t* cu_kept, int B, int max_k, int Hq, int Hkv,
-                    int d, bool is_bf16, void* o, float* lse, hipStream_t stream,
-                    const CacheWarm* warm = nullptr);
+                    int d, bool is_bf16, void* o, float* lse, hipStream_t stream);
 
 }  // namespace tg
