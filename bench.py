@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device-to-device copy of BYTES (counter calibration "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay pass (ms_per_step_hip_graph)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only the whole step (no per-kernel events)")
     return ap.parse_args()
@@ -207,13 +209,13 @@ def main():
 
     per_step = 4 + L * (tg.LAYER_STAGES + 1)
     use_ev = not args.no_kernel_events
-    ev = HipEvents(4 + (per_step * args.steps if use_ev else 0))
+    ev = HipEvents(6 + (per_step * args.steps if use_ev else 0))
 
     def step(sidx=None):
         if sidx is None:
             gp.run()
             return
-        base = 4 + sidx * per_step
+        base = 6 + sidx * per_step
         ev.record(base + 0, stream)
         gp.score()
         ev.record(base + 1, stream)
@@ -263,6 +265,24 @@ def main():
         torch.cuda.synchronize()
         ms_instr = ev.ms(2, 3) / args.steps
         attn_bias = attention_bias_ratio(tg, torch, w, dw, gp, stream)
+    # The same step captured once into a HIP graph and replayed `steps` times
+    # (reported beside `value`; the library makes no allocation, copy or
+    # synchronisation inside its calls, so the whole step captures).
+    ms_graph = None
+    if not args.no_graph:
+        print("[bench] HIP graph of one step: capture, %d replays" % args.steps, file=sys.stderr, flush=True)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        ev.record(4, stream)
+        for i in range(args.steps):
+            graph.replay()
+        ev.record(5, stream)
+        torch.cuda.synchronize()
+        ms_graph = ev.ms(4, 5) / args.steps
+        del graph
     ms_per_step = total_ms / args.steps
     tokens_per_s = w.T_in / (ms_per_step / 1e3)
     peak_mem = torch.cuda.max_memory_allocated()
@@ -340,6 +360,7 @@ def main():
         },
         "host_wall_s_timed": round(t_host1 - t_host0, 3),
         "ms_per_step_with_kernel_events": round(ms_instr, 4) if ms_instr else None,
+        "ms_per_step_hip_graph": round(ms_graph, 4) if ms_graph else None,
         "kept_tokens_per_s": round(w.T / (ms_per_step / 1e3), 1),
         "peak_device_mem_gb": round(peak_mem / 1e9, 3),
     }

@@ -207,6 +207,35 @@ def test_layer_stack_folded_norms_reuses_input_sums():
     say("  layer 1 on its input sums from layer 0: bit-identical to a fresh run; k err %.3g" % e)
 
 
+def test_step_replays_from_a_hip_graph():
+    """The whole step (scorer, select, compact, 3 fused layers) captured into a
+    HIP graph: the library makes no allocation, copy or synchronisation inside
+    its calls, so capture works, and every replay (with eager work of the
+    program and synchronisations between replays) equals the eager step bit for
+    bit."""
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=64, dtype="bf16")
+    w = custom(91, N=[700, 333, 64], K=[200, 99, 64], F=16, dims=dims, layers=3)
+    dw = DeviceWorkload(w, n_layers=3, norms_folded=True)
+    gp = GatedPrefill(dw)
+    gp.run()
+    torch.cuda.synchronize()
+    ref = (gp.x.clone(), gp.kept.clone(), gp.kcache.clone(), gp.vcache.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gp.run()
+    for i in range(3):
+        gp.x.zero_()
+        gp.kcache.zero_()
+        junk = torch.randn(1 << 20, device="cuda")  # eager work between replays
+        gp.score()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(junk.abs().sum()) > 0
+        for a, r, name in zip((gp.x, gp.kept, gp.kcache, gp.vcache), ref, ("x", "kept", "k cache", "v cache")):
+            assert torch.equal(a, r), "replay %d: %s" % (i, name)
+
+
 def test_folded_norm_weights_not_ones():
     """Fold non-unit norm weights into the projections and run the fused layer:
     every stage matches the oracle evaluated with the unfolded weights."""
