@@ -37,7 +37,10 @@
 //    output rows are rescaled only when some row's tile maximum exceeds the
 //    running one by more than 8 (P <= 2^8, far from overflow; exact after
 //    the final division by the row sum, which uses the same reference);
-//  * heavy (late) and light (early) query tiles are dispatched in pairs.
+//  * heavy (late) and light (early) query tiles are dispatched in pairs, so
+//    every workgroup sees about the same number of key tiles; when all query
+//    tiles fit one workgroup per CU, each workgroup takes a single tile,
+//    heaviest first.
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
