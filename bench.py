@@ -209,13 +209,14 @@ def main():
 
     per_step = 4 + L * (tg.LAYER_STAGES + 1)
     use_ev = not args.no_kernel_events
-    ev = HipEvents(6 + (per_step * args.steps if use_ev else 0))
+    EV0 = 6  # events 0-1: timed region, 2-3: per-kernel pass, 4-5: graph replays
+    ev = HipEvents(EV0 + (per_step * args.steps if use_ev else 0))
 
     def step(sidx=None):
         if sidx is None:
             gp.run()
             return
-        base = 6 + sidx * per_step
+        base = EV0 + sidx * per_step
         ev.record(base + 0, stream)
         gp.score()
         ev.record(base + 1, stream)
@@ -312,7 +313,7 @@ def main():
     if use_ev:
         acc = {}
         for i in range(args.steps):
-            base = 4 + i * per_step
+            base = EV0 + i * per_step
             for name, a in (("gate_score", 0), ("topk_select", 1), ("compact", 2)):
                 acc.setdefault(name, []).append(ev.ms(base + a, base + a + 1))
             for l in range(L):
