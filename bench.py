@@ -185,8 +185,8 @@ def measured_traffic(stage, workload_name):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the gated prefill path of one "
-              "device); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py: runs on one GPU only (the gated prefill path of one device); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
