@@ -364,6 +364,54 @@ def test_select_all_equal_and_budget_extremes():
     assert np.array_equal(kept, ref.astype(np.int32)) and not status.any()
 
 
+def test_select_and_compact_empty_sequences():
+    """Sequences with no tokens (N_b = 0, K_b = 0) between ordinary ones: the
+    selection skips them and its other outputs match the oracle; compaction
+    of the result is a bit copy."""
+    rng = np.random.default_rng(35)
+    N = [0, 5, 0, 900, 0]
+    K = [0, 5, 0, 77, 0]
+    s = rng.random(sum(N)).astype(np.float32)
+    mask = np.zeros(sum(N), np.uint8)
+    mask[5 + 890:] = 1
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, _ = O.topk_select(s, mask, cu_in, cu_k)
+    assert np.array_equal(kept, ref.astype(np.int32)) and not status.any()
+    D = 64
+    h = activations(35, 1, (sum(N), D), "bf16")
+    dev = "cuda"
+    hc, pc, sc = tg.compact(to_device(h), None, torch.from_numpy(s).to(dev), torch.from_numpy(kept).to(dev),
+                            torch.from_numpy(cu_in).to(dev), torch.from_numpy(cu_k).to(dev))
+    torch.cuda.synchronize()
+    hr, pr, sr = O.compact(h.device_array, None, s, ref, cu_in, cu_k)
+    assert np.array_equal(bits(hc), np.ascontiguousarray(hr).view(bits(hc).dtype))
+    assert np.array_equal(pc.cpu().numpy(), pr.astype(np.int32))
+
+
+def test_layer_ignores_empty_sequences():
+    """Empty sequences in the kept-token batch (repeated cu_kept entries) change
+    nothing: the layer's outputs equal those of the batch without them, bit for
+    bit (every kernel works per token row or per sequence)."""
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=64, dtype="bf16")
+    w = custom(92, N=[300, 200], K=[150, 97], F=8, dims=dims)
+    dw = DeviceWorkload(w, n_layers=1, norms_folded=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    gp.select()
+    gp.compact()
+    torch.cuda.synchronize()
+    x0 = gp.x.clone()
+    outs = []
+    for cu in ([0, 150, 247], [0, 0, 150, 150, 150, 247, 247]):
+        cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        x, kc, vc, _ = tg.upper_layer_fwd(dw.layers[0], dw.dims, x0, gp.pos_c, gp.s_c, cu_t, 150,
+                                          norms_folded=True)
+        torch.cuda.synchronize()
+        outs.append((x.clone(), kc.clone(), vc.clone()))
+    for a, b, name in zip(outs[0], outs[1], ("x out", "k cache", "v cache")):
+        assert torch.equal(a, b), name
+
+
 def test_select_rounds_ties_across_rounds():
     """Sequences longer than one LDS round (32768 tokens): equal scores whose ties
     straddle rounds, forced tokens in every round, a ragged last round."""
