@@ -144,6 +144,27 @@ def test_stages_ragged_bf16_k_and_v_head_in_one_pair(folded):
     _stage_parity(w, norms_folded=folded)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_stages_random_small_configs(seed):
+    """Seeded random shapes within the supported set (bf16): model widths,
+    head dims, GQA groups, batch sizes, lengths, budgets and forced tails drawn
+    per seed; every stage against the oracle, with and without folded norms."""
+    rng = np.random.default_rng(1000 + seed)
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4]))
+    Hkv = int(rng.choice([1, 2]))
+    D = int(rng.choice([128, 256, 384]))
+    I = int(rng.choice([256, 512]))
+    H1 = int(rng.choice([64, 128, 256]))
+    dims = ModelDims(D=D, Hq=Hkv * G, Hkv=Hkv, d=d, I=I, H1=H1, dtype="bf16")
+    B = int(rng.integers(1, 5))
+    N = [int(x) for x in rng.integers(16, 700, size=B)]
+    F = int(rng.integers(0, 9))
+    K = [int(rng.integers(max(F, 1), n + 1)) for n in N]
+    w = custom(1100 + seed, N=N, K=K, F=F, dims=dims)
+    _stage_parity(w, norms_folded=bool(seed % 2))
+
+
 def test_stages_ragged_gqa4_fp32_d128():
     dims = ModelDims(D=256, Hq=8, Hkv=2, d=128, I=384, H1=40, dtype="f32")
     w = custom(22, N=[129, 64, 200], K=[65, 64, 3], F=3, dims=dims)
