@@ -251,6 +251,25 @@ tg_status tg_upper_layer_fwd(const tg_layer_weights* w, const tg_layer_dims* dim
                              void* kcache, void* vcache,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* A stack of upper layers on the same kept tokens — [TC] early token
+ * filtering: every layer above the gate runs on the K kept tokens only.
+ * Runs tg_upper_layer_fwd for l = 0 .. n_layers-1 in order on x in place
+ * (x [T, D] holds the input and receives the last layer's output), with
+ * layer l's weights w[l] and its K/V caches at element offset l*T*Hkv*d of
+ * kcache / vcache ([n_layers, T, Hkv, d], dtype). Layers after the first
+ * reuse the RoPE table (TG_LAYER_ROPE_READY) and, when dims->flags holds
+ * TG_LAYER_NORMS_FOLDED, their input's row sums of squares
+ * (TG_LAYER_INPUT_SSQ) from the shared workspace; dims->flags may hold
+ * only TG_LAYER_NORMS_FOLDED. Workspace: tg_upper_layer_workspace_size()
+ * (one layer's). Argument errors are checked for every layer before the
+ * first launch; n_layers = 0 is a no-op. */
+tg_status tg_upper_layer_stack_fwd(const tg_layer_weights* w, int n_layers,
+                                   const tg_layer_dims* dims, void* x,
+                                   const int32_t* pos_c, const float* s_c,
+                                   const int32_t* d_cu_kept, int B, int64_t T, int max_k,
+                                   void* kcache, void* vcache,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Instrumentation: exactly tg_upper_layer_fwd, and in addition records
  * events[i] on `stream` right before stage i of the layer and
  * events[TG_LAYER_STAGES] after the last one, so hipEventElapsedTime gives each

@@ -32,7 +32,7 @@ ABI_FUNCTIONS = (
     "tg_compact",
     "tg_gated_attn_workspace_size", "tg_gated_attn_fwd",
     "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
-    "tg_upper_layer_fwd_timed", "tg_fold_norm_weights",
+    "tg_upper_layer_fwd_timed", "tg_fold_norm_weights", "tg_upper_layer_stack_fwd",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -105,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.tg_upper_layer_fwd.restype = i32
     L.tg_upper_layer_fwd_timed.argtypes = L.tg_upper_layer_fwd.argtypes + [vp]
     L.tg_upper_layer_fwd_timed.restype = i32
+    L.tg_upper_layer_stack_fwd.argtypes = [ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
+                                           vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, sz, vp]
+    L.tg_upper_layer_stack_fwd.restype = i32
     L.tg_fold_norm_weights.argtypes = [vp, vp, i64, i32, i32, vp]
     L.tg_fold_norm_weights.restype = i32
     _lib = L
@@ -220,6 +223,26 @@ class UpperLayerWeights:
     def __init__(self, tensors: Dict[str, torch.Tensor]):
         self.tensors = tensors
         self.c = LayerWeights(*[_p(tensors[n]) for n, _ in LayerWeights._fields_])
+
+
+def upper_layer_stack_fwd(layers, dims: LayerDims, x, pos_c, s_c, cu_kept, max_k: int, kcache, vcache,
+                          ws=None, norms_folded=False):
+    """All layers of ``layers`` (UpperLayerWeights) on x in place, one native
+    call; kcache / vcache are [n_layers, T, Hkv, d]. Returns x."""
+    n = len(layers)
+    T = x.shape[0]
+    B = cu_kept.numel() - 1
+    if norms_folded:
+        dims = LayerDims(*[getattr(dims, f) for f, _ in LayerDims._fields_])
+        dims.flags |= LAYER_NORMS_FOLDED
+    need = lib().tg_upper_layer_workspace_size(ctypes.byref(dims), T, B, max_k)
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(need, x.device)
+    arr = (LayerWeights * max(n, 1))(*[l.c for l in layers])
+    _check(lib().tg_upper_layer_stack_fwd(arr, n, ctypes.byref(dims), _p(x), _p(pos_c), _p(s_c), _p(cu_kept),
+                                          B, T, max_k, _p(kcache), _p(vcache), _p(ws), ws.numel(), _stream()),
+           "tg_upper_layer_stack_fwd")
+    return x
 
 
 def fold_norm_weights(norm_w: torch.Tensor, W: torch.Tensor) -> torch.Tensor:

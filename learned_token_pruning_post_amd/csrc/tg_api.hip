@@ -79,7 +79,7 @@ const char* tg_status_string(tg_status s) {
   }
 }
 
-int tg_abi_version(void) { return (3 << 16) | 0; }
+int tg_abi_version(void) { return (3 << 16) | 1; }
 
 // ---------------------------------------------------------------------------
 size_t tg_gate_score_workspace_size(int64_t T_in, int D, int H1, tg_dtype dtype) {
@@ -349,6 +349,38 @@ tg_status tg_upper_layer_fwd(const tg_layer_weights* w, const tg_layer_dims* dm,
                              void* vcache, void* ws, size_t ws_bytes, hipStream_t stream) {
   return upper_layer_impl(w, dm, x_in, x_out, pos_c, s_c, d_cu_kept, B, T, max_k, kcache, vcache,
                           ws, ws_bytes, stream, nullptr);
+}
+
+tg_status tg_upper_layer_stack_fwd(const tg_layer_weights* w, int n_layers, const tg_layer_dims* dm,
+                                   void* x, const int32_t* pos_c, const float* s_c,
+                                   const int32_t* d_cu_kept, int B, int64_t T, int max_k,
+                                   void* kcache, void* vcache, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  TG_CHECK(n_layers >= 0 && dm, TG_ERR_INVALID_ARG);
+  if (n_layers == 0) return TG_OK;
+  TG_CHECK(w, TG_ERR_INVALID_ARG);
+  TG_CHECK((dm->flags & ~TG_LAYER_NORMS_FOLDED) == 0, TG_ERR_INVALID_ARG);
+  const bool fused = (dm->flags & TG_LAYER_NORMS_FOLDED) != 0;
+  // every layer's weights before the first launch (the other arguments are
+  // shared, and layer 0 checks them before it launches anything)
+  for (int l = 0; l < n_layers; ++l) {
+    const tg_layer_weights& wl = w[l];
+    TG_CHECK(wl.wq && wl.wk && wl.wv && wl.wo && wl.wg && wl.wu && wl.wd && wl.t && wl.g,
+             TG_ERR_INVALID_ARG);
+    TG_CHECK(fused || (wl.attn_norm && wl.ffn_norm), TG_ERR_INVALID_ARG);
+  }
+  TG_CHECK(dm->Hkv > 0 && dm->d > 0, TG_ERR_INVALID_ARG);
+  const size_t cache_layer = (size_t)(T > 0 ? T : 0) * (size_t)dm->Hkv * (size_t)dm->d * elt_size(dm->dtype);
+  for (int l = 0; l < n_layers; ++l) {
+    tg_layer_dims dl = *dm;
+    if (l > 0) dl.flags |= TG_LAYER_ROPE_READY | (fused ? TG_LAYER_INPUT_SSQ : 0);
+    const tg_status st = upper_layer_impl(&w[l], &dl, x, x, pos_c, s_c, d_cu_kept, B, T, max_k,
+                                          kcache ? (char*)kcache + l * cache_layer : nullptr,
+                                          vcache ? (char*)vcache + l * cache_layer : nullptr, ws,
+                                          ws_bytes, stream, nullptr);
+    if (st != TG_OK) return st;
+  }
+  return TG_OK;
 }
 
 tg_status tg_upper_layer_fwd_timed(const tg_layer_weights* w, const tg_layer_dims* dm,

@@ -120,9 +120,14 @@ class GatedPrefill:
                            input_ssq=d.norms_folded and l > 0)
 
     def run(self):
+        """One step: scorer, select, compact, then the whole layer stack in one
+        native call (tg_upper_layer_stack_fwd; the same kernels as layer(l) for
+        every l in order)."""
         self.score()
         self.select()
         self.compact()
-        for l in range(len(self.dw.layers)):
-            self.layer(l)
+        d = self.dw
+        if d.layers:
+            tg.upper_layer_stack_fwd(d.layers, d.dims, self.x, self.pos_c, self.s_c, d.cu_kept, d.w.max_k,
+                                     self.kcache, self.vcache, ws=self.ws, norms_folded=d.norms_folded)
         return self.x

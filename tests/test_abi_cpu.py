@@ -92,6 +92,24 @@ def test_attention_argument_errors(L):
     assert f(FAKE, FAKE, None, *([FAKE] * 4), 1, 64, 8, 4, 128, 1, FAKE, None, None, 0, None) == INVALID
 
 
+def test_layer_stack_argument_errors(L):
+    f = L.tg_upper_layer_stack_fwd
+    dm = _dims()
+    good = tg.LayerWeights(*([0x100000] * 11))
+    bad = tg.LayerWeights(*([0x100000] * 11))
+    bad.wd = None
+    args = lambda arr, n, dims: (arr, n, ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, 1, 1000, 1000,
+                                 FAKE, FAKE, FAKE, 1 << 40, None)
+    two = (tg.LayerWeights * 2)(good, bad)
+    assert f(*args(two, -1, dm)) == INVALID
+    assert f(*args(None, 0, dm)) == OK          # no layers: nothing to do
+    assert f(*args(None, 2, dm)) == INVALID
+    assert f(*args(two, 2, dm)) == INVALID      # layer 1's weights checked before any launch
+    rope = _dims()
+    rope.flags = tg.LAYER_ROPE_READY            # set per layer by the stack itself
+    assert f(*args(two, 1, rope)) == INVALID
+
+
 def test_fold_norm_weights_argument_errors(L):
     f = L.tg_fold_norm_weights
     assert f(FAKE, FAKE, -1, 8, 1, None) == INVALID

@@ -228,6 +228,33 @@ def test_layer_stack_folded_norms_reuses_input_sums():
     say("  layer 1 on its input sums from layer 0: bit-identical to a fresh run; k err %.3g" % e)
 
 
+def test_native_layer_stack_equals_layer_loop():
+    """tg_upper_layer_stack_fwd (one call for all layers, flags set per layer
+    inside) gives the same x and K/V caches as calling tg_upper_layer_fwd layer
+    by layer, bit for bit, with and without folded norms."""
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=64, dtype="bf16")
+    w = custom(93, N=[500, 260], K=[180, 77], F=8, dims=dims, layers=3)
+    for folded in (False, True):
+        dw = DeviceWorkload(w, n_layers=3, norms_folded=folded)
+        gp = GatedPrefill(dw)
+        gp.score()
+        gp.select()
+        gp.compact()
+        x0 = gp.x.clone()
+        for l in range(3):
+            gp.layer(l)
+        torch.cuda.synchronize()
+        loop = (gp.x.clone(), gp.kcache.clone(), gp.vcache.clone())
+        gp.x.copy_(x0)
+        gp.kcache.zero_()
+        gp.vcache.zero_()
+        tg.upper_layer_stack_fwd(dw.layers, dw.dims, gp.x, gp.pos_c, gp.s_c, dw.cu_kept, w.max_k,
+                                 gp.kcache, gp.vcache, ws=torch.zeros_like(gp.ws), norms_folded=folded)
+        torch.cuda.synchronize()
+        for a, r, name in zip((gp.x, gp.kcache, gp.vcache), loop, ("x", "k cache", "v cache")):
+            assert torch.equal(a, r), "%s (folded=%s)" % (name, folded)
+
+
 def test_step_replays_from_a_hip_graph():
     """The whole step (scorer, select, compact, 3 fused layers) captured into a
     HIP graph: the library makes no allocation, copy or synchronisation inside
