@@ -270,6 +270,41 @@ tg_status tg_upper_layer_stack_fwd(const tg_layer_weights* w, int n_layers,
                                    void* kcache, void* vcache,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* -------------------------------------------------------------------------
+ * One gated prefill step above layer L, the whole path in one call — [FW]
+ * the method: score after layer L, keep K tokens, run the layers above on
+ * them; [TC] early token filtering. In order on `stream`: tg_gate_score on h,
+ * tg_topk_select, tg_compact (pos NULL: a token's position is its index in
+ * its sequence), tg_upper_layer_stack_fwd on the compacted rows.
+ *  h [T_in, D] dtype (D = dims->D); gate: the scorer's weights (W1 [H1, D],
+ *  b1 [H1], w2 [H1], b2 [1], dtype); layers [n_layers], dims as for the
+ *  stack (flags 0 or TG_LAYER_NORMS_FOLDED).
+ *  Outputs: s [T_in] fp32, kept_idx [T] int32, d_status [B] int32 (may be
+ *  NULL), x [T, D] dtype (the compacted rows, then the last layer's output),
+ *  pos_c [T] int32, s_c [T] fp32, kcache / vcache [n_layers, T, Hkv, d].
+ * Workspace: tg_gated_prefill_workspace_size() (the larger of the scorer's
+ * and one layer's). The first failing stage's status is returned; stages
+ * before it have been enqueued.
+ * ------------------------------------------------------------------------- */
+typedef struct tg_gate_weights {
+  const void* W1;  /* [H1, D] */
+  const void* b1;  /* [H1]    */
+  const void* w2;  /* [H1]    */
+  const void* b2;  /* [1]     */
+  int H1;
+} tg_gate_weights;
+
+size_t tg_gated_prefill_workspace_size(const tg_layer_dims* dims, int H1, int64_t T_in, int64_t T,
+                                       int B, int max_k);
+tg_status tg_gated_prefill(const void* h, const int32_t* pos, const uint8_t* keep_mask,
+                           const int32_t* d_cu_in, const int32_t* d_cu_kept, int B,
+                           int64_t T_in, int64_t T, int max_n, int max_k,
+                           const tg_gate_weights* gate, const tg_layer_weights* layers,
+                           int n_layers, const tg_layer_dims* dims,
+                           float* s, int32_t* kept_idx, int32_t* d_status,
+                           void* x, int32_t* pos_c, float* s_c, void* kcache, void* vcache,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Instrumentation: exactly tg_upper_layer_fwd, and in addition records
  * events[i] on `stream` right before stage i of the layer and
  * events[TG_LAYER_STAGES] after the last one, so hipEventElapsedTime gives each

@@ -33,6 +33,7 @@ ABI_FUNCTIONS = (
     "tg_gated_attn_workspace_size", "tg_gated_attn_fwd",
     "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
     "tg_upper_layer_fwd_timed", "tg_fold_norm_weights", "tg_upper_layer_stack_fwd",
+    "tg_gated_prefill_workspace_size", "tg_gated_prefill",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -48,6 +49,11 @@ class TokenGateError(RuntimeError):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd", "t", "g")]
+
+
+class GateWeights(ctypes.Structure):
+    _fields_ = [("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("H1", ctypes.c_int)]
 
 
 class LayerDims(ctypes.Structure):
@@ -108,6 +114,12 @@ def lib() -> ctypes.CDLL:
     L.tg_upper_layer_stack_fwd.argtypes = [ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
                                            vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, sz, vp]
     L.tg_upper_layer_stack_fwd.restype = i32
+    L.tg_gated_prefill_workspace_size.argtypes = [ctypes.POINTER(LayerDims), i32, i64, i64, i32, i32]
+    L.tg_gated_prefill_workspace_size.restype = sz
+    L.tg_gated_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, ctypes.POINTER(GateWeights),
+                                   ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
+                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tg_gated_prefill.restype = i32
     L.tg_fold_norm_weights.argtypes = [vp, vp, i64, i32, i32, vp]
     L.tg_fold_norm_weights.restype = i32
     _lib = L
@@ -242,6 +254,31 @@ def upper_layer_stack_fwd(layers, dims: LayerDims, x, pos_c, s_c, cu_kept, max_k
     _check(lib().tg_upper_layer_stack_fwd(arr, n, ctypes.byref(dims), _p(x), _p(pos_c), _p(s_c), _p(cu_kept),
                                           B, T, max_k, _p(kcache), _p(vcache), _p(ws), ws.numel(), _stream()),
            "tg_upper_layer_stack_fwd")
+    return x
+
+
+def gated_prefill(h, keep_mask, cu_in, cu_kept, T: int, max_n: int, max_k: int, W1, b1, w2, b2,
+                  layers, dims: LayerDims, s, kept, status, x, pos_c, s_c, kcache, vcache, ws=None,
+                  norms_folded=False, pos=None):
+    """The whole step in one native call (tg_gated_prefill): scorer, select,
+    compact, then every layer of ``layers`` on the kept tokens. All outputs
+    are caller-allocated tensors; returns x."""
+    B = cu_in.numel() - 1
+    T_in = h.shape[0]
+    if norms_folded:
+        dims = LayerDims(*[getattr(dims, f) for f, _ in LayerDims._fields_])
+        dims.flags |= LAYER_NORMS_FOLDED
+    H1 = W1.shape[0]
+    need = lib().tg_gated_prefill_workspace_size(ctypes.byref(dims), H1, T_in, T, B, max_k)
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(need, h.device)
+    gate = GateWeights(_p(W1), _p(b1), _p(w2), _p(b2), H1)
+    n = len(layers)
+    arr = (LayerWeights * max(n, 1))(*[l.c for l in layers])
+    _check(lib().tg_gated_prefill(_p(h), _p(pos), _p(keep_mask), _p(cu_in), _p(cu_kept), B, T_in, T, max_n,
+                                  max_k, ctypes.byref(gate), arr, n, ctypes.byref(dims), _p(s), _p(kept),
+                                  _p(status), _p(x), _p(pos_c), _p(s_c), _p(kcache), _p(vcache), _p(ws),
+                                  ws.numel(), _stream()), "tg_gated_prefill")
     return x
 
 

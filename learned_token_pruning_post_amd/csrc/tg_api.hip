@@ -383,6 +383,39 @@ tg_status tg_upper_layer_stack_fwd(const tg_layer_weights* w, int n_layers, cons
   return TG_OK;
 }
 
+size_t tg_gated_prefill_workspace_size(const tg_layer_dims* dm, int H1, int64_t T_in, int64_t T,
+                                       int B, int max_k) {
+  if (!dm) return 0;
+  const size_t a = tg_gate_score_workspace_size(T_in, dm->D, H1, dm->dtype);
+  tg_layer_dims base = *dm;
+  base.flags &= TG_LAYER_NORMS_FOLDED;
+  const size_t b = tg_upper_layer_workspace_size(&base, T, B, max_k);
+  const size_t c = tg_topk_select_workspace_size(B, T_in, INT_MAX);
+  const size_t ab = a > b ? a : b;
+  return ab > c ? ab : c;
+}
+
+tg_status tg_gated_prefill(const void* h, const int32_t* pos, const uint8_t* keep_mask,
+                           const int32_t* d_cu_in, const int32_t* d_cu_kept, int B, int64_t T_in,
+                           int64_t T, int max_n, int max_k, const tg_gate_weights* gate,
+                           const tg_layer_weights* layers, int n_layers, const tg_layer_dims* dm,
+                           float* s, int32_t* kept_idx, int32_t* d_status, void* x, int32_t* pos_c,
+                           float* s_c, void* kcache, void* vcache, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  TG_CHECK(gate && dm, TG_ERR_INVALID_ARG);
+  tg_status st = tg_gate_score(h, T_in, dm->D, gate->H1, gate->W1, gate->b1, gate->w2, gate->b2,
+                               dm->dtype, s, ws, ws_bytes, stream);
+  if (st != TG_OK) return st;
+  st = tg_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx, d_status,
+                      ws, ws_bytes, stream);
+  if (st != TG_OK) return st;
+  st = tg_compact(h, pos, s, kept_idx, d_cu_in, d_cu_kept, B, T, dm->D, dm->dtype, x, pos_c, s_c,
+                  stream);
+  if (st != TG_OK) return st;
+  return tg_upper_layer_stack_fwd(layers, n_layers, dm, x, pos_c, s_c, d_cu_kept, B, T, max_k,
+                                  kcache, vcache, ws, ws_bytes, stream);
+}
+
 tg_status tg_upper_layer_fwd_timed(const tg_layer_weights* w, const tg_layer_dims* dm,
                                    const void* x_in, void* x_out, const int32_t* pos_c,
                                    const float* s_c, const int32_t* d_cu_kept, int B, int64_t T,

@@ -120,14 +120,11 @@ class GatedPrefill:
                            input_ssq=d.norms_folded and l > 0)
 
     def run(self):
-        """One step: scorer, select, compact, then the whole layer stack in one
-        native call (tg_upper_layer_stack_fwd; the same kernels as layer(l) for
-        every l in order)."""
-        self.score()
-        self.select()
-        self.compact()
+        """One step in one native call (tg_gated_prefill): the same kernels as
+        score(), select(), compact() and layer(l) for every l, in that order."""
         d = self.dw
-        if d.layers:
-            tg.upper_layer_stack_fwd(d.layers, d.dims, self.x, self.pos_c, self.s_c, d.cu_kept, d.w.max_k,
-                                     self.kcache, self.vcache, ws=self.ws, norms_folded=d.norms_folded)
+        tg.gated_prefill(d.h, d.keep_mask, d.cu_in, d.cu_kept, d.w.T, d.w.max_n, d.w.max_k,
+                         d.W1, d.b1, d.w2, d.b2, d.layers, d.dims, self.s, self.kept, self.status,
+                         self.x, self.pos_c, self.s_c, self.kcache, self.vcache, ws=self.ws,
+                         norms_folded=d.norms_folded)
         return self.x

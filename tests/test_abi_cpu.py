@@ -110,6 +110,23 @@ def test_layer_stack_argument_errors(L):
     assert f(*args(two, 1, rope)) == INVALID
 
 
+def test_gated_prefill_argument_errors(L):
+    f = L.tg_gated_prefill
+    dm = _dims()
+    lw = (tg.LayerWeights * 1)(tg.LayerWeights(*([0x100000] * 11)))
+    gate = tg.GateWeights(FAKE, FAKE, FAKE, FAKE, 64)
+    call = lambda g, dims: f(FAKE, None, None, FAKE, FAKE, 1, 1000, 100, 1000, 100, g, lw, 1, dims,
+                             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert call(None, ctypes.byref(dm)) == INVALID
+    assert call(ctypes.byref(gate), None) == INVALID
+    bad = tg.GateWeights(FAKE, FAKE, FAKE, FAKE, 6)  # bf16 scorer needs H1 % 4 == 0
+    assert call(ctypes.byref(bad), ctypes.byref(dm)) == UNSUP
+    ws = L.tg_gated_prefill_workspace_size(ctypes.byref(dm), 64, 1000, 100, 1, 100)
+    lay = tg.LayerWsLayout()
+    assert L.tg_upper_layer_ws_layout(ctypes.byref(dm), 100, ctypes.byref(lay)) == OK
+    assert ws >= lay.total and ws >= L.tg_gate_score_workspace_size(1000, 256, 64, 1)
+
+
 def test_fold_norm_weights_argument_errors(L):
     f = L.tg_fold_norm_weights
     assert f(FAKE, FAKE, -1, 8, 1, None) == INVALID

@@ -255,6 +255,30 @@ def test_native_layer_stack_equals_layer_loop():
             assert torch.equal(a, r), "%s (folded=%s)" % (name, folded)
 
 
+def test_native_step_equals_staged_calls():
+    """tg_gated_prefill (the whole step in one call) gives the same scores,
+    selection, status, compacted positions and scores, x and K/V caches as the
+    stage-by-stage calls, bit for bit."""
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=64, dtype="bf16")
+    w = custom(94, N=[640, 300, 90], K=[200, 150, 90], F=16, dims=dims, layers=2)
+    dw = DeviceWorkload(w, n_layers=2, norms_folded=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    gp.select()
+    gp.compact()
+    for l in range(2):
+        gp.layer(l)
+    torch.cuda.synchronize()
+    bufs = ("s", "kept", "status", "pos_c", "s_c", "x", "kcache", "vcache")
+    staged = {n: getattr(gp, n).clone() for n in bufs}
+    for n in bufs:
+        getattr(gp, n).zero_()
+    gp.run()
+    torch.cuda.synchronize()
+    for n in bufs:
+        assert torch.equal(getattr(gp, n), staged[n]), n
+
+
 def test_step_replays_from_a_hip_graph():
     """The whole step (scorer, select, compact, 3 fused layers) captured into a
     HIP graph: the library makes no allocation, copy or synchronisation inside
