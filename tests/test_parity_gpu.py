@@ -436,6 +436,40 @@ def test_select_all_equal_and_budget_extremes():
     assert np.array_equal(kept, ref.astype(np.int32)) and not status.any()
 
 
+def test_select_many_small_random_batches():
+    """One batch of 300 short sequences (0 to 80 tokens) with random budgets,
+    forced tokens, few distinct values (ties), NaN, -0.0, +-inf and +-0
+    mixed in: bit-exact against the oracle, status flags included (budgets
+    below the forced count and above the length are flagged)."""
+    rng = np.random.default_rng(36)
+    nseq = 300
+    N = [int(x) for x in rng.integers(0, 81, size=nseq)]
+    specials = np.array([np.nan, -0.0, 0.0, np.inf, -np.inf, 1e-30, -1e-30], np.float32)
+    s = rng.choice(rng.uniform(-2, 2, 6).astype(np.float32), size=sum(N))
+    pick = rng.random(sum(N)) < 0.15
+    s[pick] = rng.choice(specials, size=int(pick.sum()))
+    mask = (rng.random(sum(N)) < 0.1).astype(np.uint8)
+    K = []
+    off = 0
+    for n in N:
+        f = int(mask[off:off + n].sum())
+        r = rng.random()
+        k = f - 1 if (r < 0.03 and f > 0) else (n + 1 if r < 0.06 else int(rng.integers(min(f, n), n + 1)))
+        K.append(max(k, 0))
+        off += n
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, flags = O.topk_select(s, mask, cu_in, cu_k)
+    assert np.array_equal(status, flags.astype(np.int32))
+    ok = (flags & 3) == 0
+    for b in range(nseq):
+        lo, hi = cu_k[b], cu_k[b + 1]
+        if ok[b]:
+            assert np.array_equal(kept[lo:hi], ref[lo:hi].astype(np.int32)), b
+        else:
+            assert (kept[lo:hi] == -1).all(), b
+    assert (~ok).any() and ok.sum() > 250
+
+
 def test_select_and_compact_empty_sequences():
     """Sequences with no tokens (N_b = 0, K_b = 0) between ordinary ones: the
     selection skips them and its other outputs match the oracle; compaction
