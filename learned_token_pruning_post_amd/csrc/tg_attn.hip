@@ -437,12 +437,9 @@ static hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, 
                                    hipStream_t stream) {
   constexpr int BQ = 32 * (4 / G);
   constexpr size_t lds = (size_t)2 * AttnLayout<HD>::BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, HD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = ensure_dynamic_lds<attn_bf16_kernel<G, HD>>((int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int n_qt = (max_k + BQ - 1) / BQ;
   // one query-tile pair per workgroup; single tiles while they fit one

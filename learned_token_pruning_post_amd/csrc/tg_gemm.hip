@@ -599,12 +599,9 @@ template <int MODE, int BN, int BM, int WN, int WM, int NSTAGE>
 static hipError_t launch_gemm(const GemmParams& p, int Ncols, hipStream_t stream) {
   constexpr size_t lds = (size_t)NSTAGE * (BN + BM) * 128;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MODE, BN, BM, WN, WM, NSTAGE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = ensure_dynamic_lds<gemm_bf16_kernel<MODE, BN, BM, WN, WM, NSTAGE>>((int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int NB = (Ncols + BN - 1) / BN, MB = (p.M + BM - 1) / BM;
   hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BN, BM, WN, WM, NSTAGE>), dim3(NB * MB),

@@ -1,11 +1,27 @@
 // Internal launchers of libtokengate (host side). Every launcher enqueues on
 // `stream`, assumes validated arguments, and returns hipGetLastError().
 #pragma once
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "tg_common.hpp"
 
 namespace tg {
+
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per device (the limit
+// is a per-device function attribute; later calls on that device skip it).
+template <auto Kernel>
+hipError_t ensure_dynamic_lds(int bytes) {
+  static std::atomic<bool> done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute((const void*)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && slot) done[dev].store(true, std::memory_order_relaxed);
+  return e;
+}
 
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
                               const int32_t* cu_kept, int B, int max_n, int32_t* kept,

@@ -417,12 +417,9 @@ static hipError_t launch_select(const float* s, const uint8_t* mask, const int32
                                 const int32_t* cu_kept, int B, int32_t* kept, int32_t* status,
                                 hipStream_t stream) {
   constexpr size_t lds = (size_t)SEL_LDS_MAX * sizeof(uint32_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<MULTI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = ensure_dynamic_lds<topk_select_kernel<MULTI>>((int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL(topk_select_kernel<MULTI>, dim3(B), dim3(SEL_THREADS), lds, stream, s, mask,
                      cu_in, cu_kept, kept, status);
