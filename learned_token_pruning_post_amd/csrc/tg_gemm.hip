@@ -311,6 +311,8 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   // ---------------- epilogues ----------------
   const int ml = lane & 31;
   if (MODE == MODE_PLAIN) {
+    static_assert(MODE != MODE_PLAIN || TN == 64,
+                  "the fused sum of squares for the next RMSNorm covers 64-feature slots, one per wave");
     // Stage the wave's fp32 tile in LDS ([token][feature], rows padded by 16
     // bytes so the 16 rows of a write phase hit distinct banks), then each
     // lane adds the residual and stores 8 consecutive features (16 bytes):
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
           }
           *reinterpret_cast<bf16x8*>(p.out + o) = w;
         }
-        if constexpr (TN == 64) {
+        {
           // fused RMSNorm of the next projection: the 8 lanes of a row hold
           // its 64 features of this wave; row shifts 1, 2, 4 gather their
           // sum in lane 8c+7 (all lanes take part in the moves)
