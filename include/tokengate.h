@@ -98,16 +98,21 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1,
  *  keep_mask [T_in]   uint8, 1 = unprunable; NULL = nothing forced
  *  d_cu_in   [B+1]    int32 device, prefix sums of N_b (d_cu_in[0] = 0, d_cu_in[B] = T_in)
  *  d_cu_kept [B+1]    int32 device, prefix sums of K_b (d_cu_kept[B] = T)
- *  max_n              an upper bound of every N_b: up to 32768 the keys of a
- *                     sequence stay in LDS after one load; above, the kernel
- *                     walks every sequence in rounds of 32768 tokens, reloading
- *                     each round before each pass (a sequence longer than max_n
- *                     gets TG_DEV_LEN_GT_MAX_N)
+ *  max_n              an upper bound of every N_b. Up to 32768 one workgroup
+ *                     per sequence holds its keys in LDS (no workspace); above,
+ *                     every sequence is searched by workgroups of 4096 tokens
+ *                     in a chain of short kernels, with a workspace of
+ *                     tg_topk_select_workspace_size bytes (256-byte aligned).
+ *                     A sequence longer than max_n gets TG_DEV_LEN_GT_MAX_N
+ *                     and -1 slots.
  *  kept_idx  [T]      int32 out: GLOBAL row indices into s/h, ascending inside
  *                     each sequence, at that sequence's cu_kept offsets
  *  d_status  [B]      int32 device out, TG_DEV_* flags of each sequence
  *                     (overwritten, 0 when fine); may be NULL
- * The workspace may be empty (ws_bytes 0) for the current kernels.
+ *  ws, ws_bytes       scratch for max_n > 32768 (state and a 4096-bin
+ *                     histogram per sequence, two counts per 4096-token chunk;
+ *                     B * 16.4 KB + T_in / 512 bytes); NULL / 0 otherwise.
+ *                     Too small: TG_ERR_WORKSPACE; misaligned: TG_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
 size_t tg_topk_select_workspace_size(int B, int64_t T_in, int max_n);
 tg_status tg_topk_select(const float* s, const uint8_t* keep_mask,

@@ -176,14 +176,18 @@ def gate_score(h, W1, b1, w2, b2, s_out=None, ws=None):
     return s_out
 
 
-def topk_select(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, kept=None, status=None):
+def topk_select(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, kept=None, status=None, ws=None):
     B = cu_in.numel() - 1
     if kept is None:
         kept = torch.empty(max(T, 0), dtype=torch.int32, device=s.device)
     if status is None:
         status = torch.empty(max(B, 1), dtype=torch.int32, device=s.device)
+    need = lib().tg_topk_select_workspace_size(max(B, 0), s.numel(), max_n)
+    if need and (ws is None or ws.numel() < need):
+        ws = _empty_ws(need, s.device)
     _check(lib().tg_topk_select(_p(s), _p(keep_mask), _p(cu_in), _p(cu_kept), B, s.numel(), T,
-                                max_n, _p(kept), _p(status), None, 0, _stream()),
+                                max_n, _p(kept), _p(status), _p(ws) if need else None,
+                                ws.numel() if need else 0, _stream()),
            "tg_topk_select")
     return kept, status
 

@@ -114,18 +114,14 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1, const void* 
 
 // ---------------------------------------------------------------------------
 size_t tg_topk_select_workspace_size(int B, int64_t T_in, int max_n) {
-  (void)B;
-  (void)T_in;
-  (void)max_n;
-  return 0;
+  if (B < 0 || T_in < 0) return 0;
+  return tg::topk_select_workspace_bytes(B, T_in, max_n);
 }
 
 tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t* d_cu_in,
                          const int32_t* d_cu_kept, int B, int64_t T_in, int64_t T, int max_n,
                          int32_t* kept_idx, int32_t* d_status, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   TG_CHECK(B >= 0 && T_in >= 0 && T >= 0 && max_n >= 0, TG_ERR_INVALID_ARG);
   TG_CHECK(T_in <= INT_MAX && T <= INT_MAX, TG_ERR_INVALID_ARG);
   TG_CHECK(T <= T_in, TG_ERR_INVALID_ARG);  // K_b <= N_b summed over the batch
@@ -133,10 +129,15 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t
   TG_CHECK(d_cu_in && d_cu_kept, TG_ERR_INVALID_ARG);
   TG_CHECK(T_in == 0 || s, TG_ERR_INVALID_ARG);
   TG_CHECK(T == 0 || kept_idx, TG_ERR_INVALID_ARG);
+  // one workgroup per (sequence, 4096-token chunk) on the long-sequence path
+  TG_CHECK((int64_t)((max_n + 4095) / 4096) * B <= INT_MAX, TG_ERR_INVALID_ARG);
+  const size_t need = tg::topk_select_workspace_bytes(B, T_in, max_n);
+  TG_CHECK(need == 0 || (ws && ws_bytes >= need), TG_ERR_WORKSPACE);
+  TG_CHECK(need == 0 || ((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);
   tg_status a = check_arch();
   if (a != TG_OK) return a;
-  return launched(tg::launch_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, max_n, kept_idx,
-                                         d_status, stream));
+  return launched(tg::launch_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, max_n, kept_idx,
+                                         d_status, ws, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -12,9 +12,10 @@
 // radix would pile every key into one or two bins). A final pass keeps forced
 // tokens, keys > T, and the first `need` keys == T in index order.
 //
-// Keys live in LDS (select_keys): a sequence of up to SEL_LDS_MAX tokens is
-// loaded once; a longer one is walked in rounds of SEL_LDS_MAX tokens, each
-// reloaded with coalesced 16-byte loads before every walk over it.
+// Up to SEL_LDS_MAX tokens per sequence, one workgroup holds a sequence's keys
+// in LDS (select_keys). Longer sequences run the same search and emit spread
+// over many workgroups of MW_CHUNK tokens each, as a chain of short kernels
+// (the "mw" kernels below).
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
@@ -32,8 +33,16 @@ __device__ __forceinline__ uint32_t score_key(float x, bool& is_nan) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Search key of a token: 0 if forced, 1 if a NaN candidate, else its order
+// key (>= 0x007fffff, the key of -inf), so range tests skip forced tokens by
+// value.
+__device__ __forceinline__ uint32_t sel_key(float x, bool forced, bool& is_nan) {
+  const uint32_t k = score_key(x, is_nan);
+  return forced ? 0u : (is_nan ? 1u : k);
+}
+
 // ---------------------------------------------------------------------------
-// Keys in LDS, in rounds of SEL_LDS_MAX tokens (one round: loaded once).
+// Keys in LDS (sequences of up to SEL_LDS_MAX tokens, loaded once).
 //  * load: every thread issues all of its 16-byte score loads and 4-byte
 //    mask loads before using any; forced tokens are stored as key 0 and NaN
 //    candidates as key 1, below every number's key, so no separate forced
@@ -77,31 +86,20 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
 
-template <bool MULTI>
 __device__ __forceinline__ void select_keys(const float* __restrict__ sp, const uint8_t* __restrict__ mp, int n,
                            int K, int in0, int32_t* __restrict__ kp, int32_t* __restrict__ status_b,
                            uint32_t* keys, uint32_t* hist, int* red, uint32_t* list) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int NG = SEL_LDS_MAX / 4 / SEL_THREADS;  // 4-token groups per thread
-  // tokens in rounds of SEL_LDS_MAX: a sequence that fits (!MULTI) stays in
-  // LDS after the first load; longer ones reload round r before each walk
-  // over it (a separate instantiation, so the one-round code carries none of it)
-  const int nrounds = MULTI ? (n + SEL_LDS_MAX - 1) / SEL_LDS_MAX : (n > 0);
-  auto round_len = [&](int r) { return min(n - r * SEL_LDS_MAX, SEL_LDS_MAX); };
 
   // ---- load ----
-  // LDS key of a token: 0 if forced, 1 if a NaN candidate, else its order
-  // key (>= 0x007fffff, the key of -inf), so range tests skip forced tokens
-  // by value and the tail of a partial 4-token chunk (0) is never in range.
+  // LDS key of a token: sel_key; the tail of a partial 4-token chunk holds 0,
+  // so it is never in range either.
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   int nf = 0, nan_seen = 0;
-  auto lds_key = [](float x, bool f, bool& isn) -> uint32_t {
-    const uint32_t k = score_key(x, isn);
-    return f ? 0u : (isn ? 1u : k);
-  };
   auto take_key = [&](float x, bool f) -> uint32_t {  // with the statistics
     bool isn;
-    const uint32_t k = lds_key(x, f, isn);
+    const uint32_t k = sel_key(x, f, isn);
     nan_seen |= isn;
     nf += f;
     if (!f) {
@@ -112,21 +110,16 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ sp, const 
   };
   const bool vec = (reinterpret_cast<uintptr_t>(sp) & 15u) == 0 &&
                    (reinterpret_cast<uintptr_t>(mp) & 3u) == 0;
-  // load round r into LDS (store = false: statistics only, nothing written)
-  auto load_round = [&](int r, bool stats, bool store) {
-    const int nr = round_len(r);
-    const float* spr = sp + (size_t)r * SEL_LDS_MAX;
-    const uint8_t* mpr = mp ? mp + (size_t)r * SEL_LDS_MAX : nullptr;
-    auto key = [&](float x, bool f) -> uint32_t {
-      if (stats) return take_key(x, f);
-      bool isn;
-      return lds_key(x, f, isn);
-    };
+  // load the sequence into LDS with the statistics
+  {
+    const int nr = n;
+    const float* spr = sp;
+    const uint8_t* mpr = mp;
+    auto key = [&](float x, bool f) -> uint32_t { return take_key(x, f); };
     if (vec) {
-      // chunk g = u*1024 + tid holds tokens 4g..4g+3: the loads of a batch
-      // are all issued first (one batch of 8 for a single round; rounds that
-      // are reloaded inside the passes use batches of 4, fewer registers)
-      constexpr int NGB = MULTI ? NG / 2 : NG;
+      // chunk g = u*1024 + tid holds tokens 4g..4g+3: all loads are issued
+      // before any is used
+      constexpr int NGB = NG;
 #pragma unroll
       for (int u0 = 0; u0 < NG; u0 += NGB) {
         f32x4 xv[NGB];
@@ -153,25 +146,16 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ sp, const 
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             kv[e] = i + e < nr ? key(xv[uu][e], ((mv[uu] >> (8 * e)) & 0xffu) != 0) : 0u;
-          if (store && i < nr) *reinterpret_cast<u32x4*>(keys + 4 * kchunk(g)) = kv;
+          if (i < nr) *reinterpret_cast<u32x4*>(keys + 4 * kchunk(g)) = kv;
         }
       }
     } else {
       for (int i = tid; i < ((nr + 3) & ~3); i += SEL_THREADS) {
         const uint32_t k = i < nr ? key(spr[i], mpr && mpr[i]) : 0u;
-        if (store) keys[4 * kchunk(i >> 2) + (i & 3)] = k;
+        keys[4 * kchunk(i >> 2) + (i & 3)] = k;
       }
     }
-  };
-  // walks over the keys of every round: a single round is loaded once (here)
-  auto reload = [&](int r) {
-    if (MULTI) {
-      __syncthreads();  // the previous round's readers are done
-      load_round(r, false, true);
-      __syncthreads();
-    }
-  };
-  for (int r = 0; r < nrounds; ++r) load_round(r, true, !MULTI);
+  }
   // ---- fused reduction ----
   nf = lane63(wave_incl_scan(nf));
   nan_seen = lane63(wave_incl_scan(nan_seen));
@@ -250,9 +234,8 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ sp, const 
           for (int e = 0; e < 4; ++e) m |= (uint32_t)(kv[e] - lo <= span) << e;
           return m;
         };
-        for (int rr = 0; rr < nrounds; ++rr) {
-          reload(rr);
-          const int ng = (round_len(rr) + 3) / 4;
+        {
+          const int ng = (n + 3) / 4;
           int cnt = 0;
           for (int g = tid; g < ng; g += SEL_THREADS) {
             u32x4 kv;
@@ -328,16 +311,14 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ sp, const 
   }
 
   // ---- emit ----
-  // per round, thread t owns tokens [32t, 32t + 32): 32-bit masks of sure
-  // keeps (forced, key 0, or key > T) and of ties (candidate key == T), one
-  // block scan of the packed (sure, tie) counts, the first needT ties in
-  // index order are kept, and each thread writes its kept indices in order;
-  // the counts of earlier rounds carry over. T = 0 keeps every token;
-  // T = 0xffffffff (no candidate slot) keeps the forced ones.
-  int sure_run = 0, tie_run = 0;  // kept sure tokens and ties seen in earlier rounds
-  for (int rr = 0; rr < nrounds; ++rr) {
-    reload(rr);
-    const int nr = round_len(rr);
+  // thread t owns tokens [32t, 32t + 32): 32-bit masks of sure keeps
+  // (forced, key 0, or key > T) and of ties (candidate key == T), one block
+  // scan of the packed (sure, tie) counts, the first needT ties in index
+  // order are kept, and each thread writes its kept indices in order.
+  // T = 0 keeps every token; T = 0xffffffff (no candidate slot) keeps the
+  // forced ones.
+  {
+    const int nr = n;
     uint32_t sure = 0u, tie = 0u;
     const int i0 = 32 * tid;
     if (i0 < nr) {
@@ -354,39 +335,31 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ sp, const 
         }
       }
     }
-    // per-round sure and tie totals are <= 32768, so the packed halves never carry
+    // sure and tie totals are <= 32768, so the packed halves never carry
     const uint32_t packed = (uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16);
     const uint32_t incl = (uint32_t)wave_incl_scan((int)packed);
     __syncthreads();  // red is free
     if (lane == 63) red[w] = (int)incl;
     __syncthreads();
-    uint32_t excl = incl - packed, total = 0u;
+    uint32_t excl = incl - packed;
 #pragma unroll
-    for (int v = 0; v < SEL_WAVES; ++v) {
-      excl += v < w ? (uint32_t)red[v] : 0u;
-      total += (uint32_t)red[v];
-    }
-    const int sure_before = sure_run + (int)(excl & 0xffffu), tie_before = tie_run + (int)(excl >> 16);
+    for (int v = 0; v < SEL_WAVES; ++v) excl += v < w ? (uint32_t)red[v] : 0u;
+    const int sure_before = (int)(excl & 0xffffu), tie_before = (int)(excl >> 16);
     const int take = min(max(needT - tie_before, 0), __popc(tie));
     uint32_t rest = tie;  // drop the lowest `take` tie bits from rest: they are kept
     for (int c = 0; c < take; ++c) rest &= rest - 1u;
     uint32_t keep = sure | (tie ^ rest);
     int pos = sure_before + min(tie_before, needT);
-    const int tok0 = in0 + rr * SEL_LDS_MAX + i0;
+    const int tok0 = in0 + i0;
     while (keep) {
       const int bit = __builtin_ctz(keep);
       if (pos < K) kp[pos] = tok0 + bit;  // pos < K always holds; the guard keeps a logic slip in bounds
       ++pos;
       keep &= keep - 1u;
     }
-    sure_run += (int)(total & 0xffffu);
-    tie_run += (int)(total >> 16);
   }
 }
 
-// MULTI: some sequence may be longer than one LDS round (max_n > SEL_LDS_MAX);
-// a separate kernel, so the one-round kernel keeps its lower register count
-template <bool MULTI>
 __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
     const float* __restrict__ s, const uint8_t* __restrict__ mask,
     const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
@@ -404,35 +377,453 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
   const float* sp = s + in0;
   const uint8_t* mp = mask ? mask + in0 : nullptr;
   int32_t* st = status ? status + b : nullptr;
-  if (!MULTI && n > SEL_LDS_MAX) {  // longer than the max_n the host announced
+  if (n > SEL_LDS_MAX) {  // longer than the max_n the host announced
     if (threadIdx.x == 0 && st) *st = 8;  // TG_DEV_LEN_GT_MAX_N
     for (int i = threadIdx.x; i < K; i += SEL_THREADS) kept[out0 + i] = -1;
     return;
   }
-  select_keys<MULTI>(sp, mp, n, K, in0, kept + out0, st, sel_smem, hist, red, list);
+  select_keys(sp, mp, n, K, in0, kept + out0, st, sel_smem, hist, red, list);
 }
 
-template <bool MULTI>
-static hipError_t launch_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
-                                const int32_t* cu_kept, int B, int32_t* kept, int32_t* status,
-                                hipStream_t stream) {
-  constexpr size_t lds = (size_t)SEL_LDS_MAX * sizeof(uint32_t);
-  {
-    const hipError_t e = ensure_dynamic_lds<topk_select_kernel<MULTI>>((int)lds);
-    if (e != hipSuccess) return e;
+// ---------------------------------------------------------------------------
+// Sequences longer than SEL_LDS_MAX: the LDS path's range search and emit,
+// spread over workgroups of MW_CHUNK consecutive tokens of one sequence, as a
+// chain of kernels in which no workgroup waits for another:
+//   init   clears each sequence's histogram and statistics (workspace)
+//   stats  per chunk: forced count, NaN seen, candidate key min and max,
+//          merged with global atomics
+//   plan   per sequence: status flags and -1 slots for a rejected sequence;
+//          the threshold at once when the budget takes no candidate, every
+//          candidate, or the live range is one key; else [kmin, kmax]
+//   3 x  { hist (per chunk: LDS histogram of the live range in 4096
+//          power-of-two bins, merged with global atomics), pick (per
+//          sequence: the bin that holds the threshold; clears the histogram
+//          for the next pass) }: a range shrinks 2^12-fold per pass, so three
+//          passes reach one key from any 32-bit span
+//   count  per chunk: sure keeps (forced or key > T) and ties (key == T)
+//   emit   per chunk: the earlier chunks' counts, one block scan, the first
+//          needT ties of the sequence in index order, indices ascending
+// Keys are formed again from the scores on every walk (sel_key), so the
+// workspace holds per sequence only its state and one histogram, plus two
+// counts per chunk. Thread t of a chunk owns its tokens 16t..16t+15.
+// ---------------------------------------------------------------------------
+constexpr int MW_THREADS = 256;
+constexpr int MW_TPT = 16;                     // consecutive tokens per thread
+constexpr int MW_CHUNK = MW_THREADS * MW_TPT;  // tokens per workgroup
+constexpr int MW_BINS = 4096;
+constexpr int MW_PICK_THREADS = MW_BINS / 4;   // 4 bins per thread
+constexpr int MW_PASSES = 3;
+
+struct MwState {
+  uint32_t lo, hi;      // live key range of the search
+  int need;             // candidates still to take inside [lo, hi]
+  int active;           // the range search is still running
+  uint32_t T;           // threshold key
+  int needT;            // keys equal to T that are kept, lowest indices first
+  int nf, nan_seen;     // forced tokens; some candidate score is NaN
+  uint32_t kmin, kmax;  // candidate key range
+  int skip;             // rejected sequence: its slots already hold -1
+  int pad[5];
+};
+static_assert(sizeof(MwState) == 64, "64-byte per-sequence state");
+
+struct MwWs {
+  MwState* st;     // [B]
+  uint32_t* hist;  // [B][MW_BINS]
+  int2* counts;    // (sure, tie) per chunk; chunk c of sequence b at mw_chunk_slot(in0_b, b) + c
+};
+
+__host__ __device__ inline size_t mw_align(size_t x) { return (x + 255) & ~(size_t)255; }
+// Chunk slots of sequence b start at in0_b / MW_CHUNK + b: the sequences
+// before b hold sum(ceil(N / MW_CHUNK)) <= in0_b / MW_CHUNK + b chunks, so
+// the ranges never overlap and T_in / MW_CHUNK + B + 1 slots cover a batch.
+__device__ __forceinline__ int64_t mw_chunk_slot(int in0, int b) { return (int64_t)(in0 / MW_CHUNK) + b; }
+
+static size_t mw_workspace_bytes(int B, int64_t T_in) {
+  return mw_align((size_t)B * sizeof(MwState)) + mw_align((size_t)B * MW_BINS * sizeof(uint32_t)) +
+         mw_align((size_t)(T_in / MW_CHUNK + B + 1) * sizeof(int2));
+}
+
+static MwWs mw_carve(void* ws, int B) {
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  MwWs w;
+  w.st = reinterpret_cast<MwState*>(p);
+  p += mw_align((size_t)B * sizeof(MwState));
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += mw_align((size_t)B * MW_BINS * sizeof(uint32_t));
+  w.counts = reinterpret_cast<int2*>(p);
+  return w;
+}
+
+// keys of the thread's tokens [i0, i0 + 16) of a sequence; returns how many
+// of them exist (tokens at or past n read as key 0 and are never used);
+// nan_bits marks NaN scores, forced tokens included (they set the status flag)
+__device__ __forceinline__ int mw_keys(const float* __restrict__ sp, const uint8_t* __restrict__ mp,
+                                       int n, int i0, bool vec, uint32_t (&k)[MW_TPT], uint32_t& nan_bits) {
+  const int nv = min(max(n - i0, 0), MW_TPT);
+  nan_bits = 0u;
+  if (vec && nv == MW_TPT) {
+    f32x4 x[MW_TPT / 4];
+    u32x4 m = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < MW_TPT / 4; ++q) x[q] = *reinterpret_cast<const f32x4*>(sp + i0 + 4 * q);
+    if (mp) m = *reinterpret_cast<const u32x4*>(mp + i0);
+#pragma unroll
+    for (int q = 0; q < MW_TPT / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool isn;
+        k[4 * q + e] = sel_key(x[q][e], ((m[q] >> (8 * e)) & 0xffu) != 0u, isn);
+        nan_bits |= (uint32_t)isn << (4 * q + e);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < MW_TPT; ++j) {
+      bool isn = false;
+      k[j] = j < nv ? sel_key(sp[i0 + j], mp && mp[i0 + j], isn) : 0u;
+      nan_bits |= (uint32_t)isn << j;
+    }
   }
-  hipLaunchKernelGGL(topk_select_kernel<MULTI>, dim3(B), dim3(SEL_THREADS), lds, stream, s, mask,
-                     cu_in, cu_kept, kept, status);
-  return hipGetLastError();
+  return nv;
+}
+
+// the workgroup's sequence and chunk; false if the chunk is past the sequence
+struct MwChunk {
+  int b, c, in0, n, i0;
+  const float* sp;
+  const uint8_t* mp;
+  bool vec;
+};
+__device__ __forceinline__ bool mw_chunk(const float* s, const uint8_t* mask, const int32_t* cu_in, int nch,
+                                         MwChunk& ck) {
+  ck.b = blockIdx.x / nch;
+  ck.c = blockIdx.x % nch;
+  ck.in0 = cu_in[ck.b];
+  ck.n = cu_in[ck.b + 1] - ck.in0;
+  if (ck.c * MW_CHUNK >= ck.n) return false;
+  ck.i0 = ck.c * MW_CHUNK + (int)threadIdx.x * MW_TPT;
+  ck.sp = s + ck.in0;
+  ck.mp = mask ? mask + ck.in0 : nullptr;
+  ck.vec = (reinterpret_cast<uintptr_t>(ck.sp) & 15u) == 0 && (reinterpret_cast<uintptr_t>(ck.mp) & 15u) == 0;
+  return true;
+}
+
+__global__ __launch_bounds__(MW_THREADS) void mw_init_kernel(MwWs ws) {
+  const int b = blockIdx.x;
+  uint32_t* h = ws.hist + (size_t)b * MW_BINS;
+  for (int i = threadIdx.x; i < MW_BINS; i += MW_THREADS) h[i] = 0u;
+  if (threadIdx.x == 0) {
+    MwState z = {};
+    z.kmin = 0xffffffffu;
+    ws.st[b] = z;
+  }
+}
+
+__global__ __launch_bounds__(MW_THREADS) void mw_stats_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
+                                                              const int32_t* __restrict__ cu_in, int nch, MwWs ws) {
+  MwChunk ck;
+  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
+  uint32_t k[MW_TPT], nanb;
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
+  int nf = 0;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < MW_TPT; ++j)
+    if (j < nv) {
+      nf += k[j] == 0u;
+      if (k[j] != 0u) {
+        kmin = min(kmin, k[j]);
+        kmax = max(kmax, k[j]);
+      }
+    }
+  int nan_seen = nanb != 0u;
+  nf = lane63(wave_incl_scan(nf));
+  nan_seen = lane63(wave_incl_scan(nan_seen));
+  kmin = (uint32_t)lane63((int)wave_scan_u32(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
+  kmax = (uint32_t)lane63((int)wave_scan_u32(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }));
+  __shared__ uint32_t red[MW_THREADS / 64][4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[w][0] = (uint32_t)nf;
+    red[w][1] = (uint32_t)nan_seen;
+    red[w][2] = kmin;
+    red[w][3] = kmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0u, o = 0u, lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int v = 0; v < MW_THREADS / 64; ++v) {
+      a += red[v][0];
+      o |= red[v][1];
+      lo = min(lo, red[v][2]);
+      hi = max(hi, red[v][3]);
+    }
+    MwState* st = ws.st + ck.b;
+    if (a) atomicAdd(&st->nf, (int)a);
+    if (o) atomicOr(&st->nan_seen, 1);
+    if (lo <= hi) {
+      atomicMin(&st->kmin, lo);
+      atomicMax(&st->kmax, hi);
+    }
+  }
+}
+
+// One wave per sequence: flags, rejection, or the start of the range search.
+__global__ __launch_bounds__(64) void mw_plan_kernel(const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
+                                                     int max_n, int32_t* __restrict__ kept, int32_t* __restrict__ status,
+                                                     MwWs ws) {
+  const int b = blockIdx.x;
+  const int in0 = cu_in[b], n = cu_in[b + 1] - in0;
+  const int out0 = cu_kept[b], K = cu_kept[b + 1] - out0;
+  MwState* st = ws.st + b;
+  const int nf = st->nf, nan_seen = st->nan_seen;
+  const uint32_t kmin = st->kmin, kmax = st->kmax;
+  // a sequence longer than max_n has chunks outside the grid: rejected
+  const int flags = n > max_n ? 8 : ((nan_seen ? 4 : 0) | (K > n ? 2 : 0) | (nf > K ? 1 : 0));
+  if (threadIdx.x == 0 && status) status[b] = flags;
+  if (flags & 11) {
+    for (int i = threadIdx.x; i < K; i += 64) kept[out0 + i] = -1;
+    if (threadIdx.x == 0) st->skip = 1;
+    return;
+  }
+  if (threadIdx.x != 0) return;
+  const int C = n - nf, r = K - nf;  // candidates, slots for them
+  uint32_t T = 0u;
+  int needT = 0, active = 0;
+  if (r == 0) {
+    T = 0xffffffffu;  // no key reaches it
+  } else if (r == C) {
+    needT = C;  // T = 0: every token is kept
+  } else if (kmin == kmax) {
+    T = kmin;
+    needT = r;
+  } else {
+    active = 1;
+  }
+  st->lo = kmin;
+  st->hi = kmax;
+  st->need = r;
+  st->T = T;
+  st->needT = needT;
+  st->active = active;
+}
+
+__global__ __launch_bounds__(MW_THREADS) void mw_hist_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
+                                                             const int32_t* __restrict__ cu_in, int nch, MwWs ws) {
+  MwChunk ck;
+  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
+  const MwState* st = ws.st + ck.b;
+  if (!st->active) return;
+  const uint32_t lo = st->lo, span = st->hi - lo;
+  const int bits = 32 - __clz(span);
+  const int shift = bits > 12 ? bits - 12 : 0;
+  const int nb = (int)(span >> shift) + 1;
+  __shared__ uint32_t h[MW_BINS];
+  for (int i = threadIdx.x; i < nb; i += MW_THREADS) h[i] = 0u;
+  __syncthreads();
+  uint32_t k[MW_TPT], nanb;
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
+#pragma unroll
+  for (int j = 0; j < MW_TPT; ++j)
+    if (j < nv && k[j] - lo <= span) atomicAdd(&h[(k[j] - lo) >> shift], 1u);
+  __syncthreads();
+  uint32_t* gh = ws.hist + (size_t)ck.b * MW_BINS;
+  for (int i = threadIdx.x; i < nb; i += MW_THREADS)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// Per sequence: thread t owns bins 4t'..4t'+3 with t' = 1023 - t, so an
+// inclusive scan in thread order counts the keys in every bin >= 4t'.
+__global__ __launch_bounds__(MW_PICK_THREADS) void mw_pick_kernel(MwWs ws) {
+  const int b = blockIdx.x;
+  MwState* st = ws.st + b;
+  if (!st->active) return;
+  const uint32_t lo = st->lo, hi = st->hi, span = hi - lo;
+  const int need = st->need;
+  const int bits = 32 - __clz(span);
+  const int shift = bits > 12 ? bits - 12 : 0;
+  const int nb = (int)(span >> shift) + 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tb = 4 * (MW_PICK_THREADS - 1 - tid);
+  uint32_t* gh = ws.hist + (size_t)b * MW_BINS;
+  int h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = tb + e < nb ? (int)gh[tb + e] : 0;
+    gh[tb + e] = 0u;  // cleared for the next pass (only this thread reads these bins)
+  }
+  __shared__ int red[MW_PICK_THREADS / 64 + 3];
+  const int mine = h[0] + h[1] + h[2] + h[3];
+  int incl = wave_incl_scan(mine);
+  if (lane == 63) red[w] = incl;
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < MW_PICK_THREADS / 64; ++v) incl += v < w ? red[v] : 0;
+  int above = incl - mine;  // keys in bins above tb + 3
+  constexpr int R = MW_PICK_THREADS / 64;
+  if (above < need && incl >= need) {
+    int bstar = tb;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      if (above + h[e] >= need) {
+        bstar = tb + e;
+        break;
+      }
+      above += h[e];
+    }
+    red[R] = bstar;
+    red[R + 1] = above;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  const uint64_t nlo = (uint64_t)lo + ((uint64_t)red[R] << shift);
+  const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+  const uint32_t lo2 = (uint32_t)nlo, hi2 = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+  const int need2 = need - red[R + 1];
+  st->lo = lo2;
+  st->hi = hi2;
+  st->need = need2;
+  if (shift == 0 || lo2 == hi2) {
+    st->T = lo2;
+    st->needT = need2;
+    st->active = 0;
+  }
+}
+
+// sure keeps (forced, key 0, or key > T) and ties (candidate key == T) of the
+// thread's tokens, bit j for token i0 + j
+__device__ __forceinline__ void mw_keep_bits(const uint32_t (&k)[MW_TPT], int nv, uint32_t T, uint32_t& sure,
+                                             uint32_t& tie) {
+  sure = 0u;
+  tie = 0u;
+#pragma unroll
+  for (int j = 0; j < MW_TPT; ++j) {
+    const bool in = j < nv;
+    sure |= (uint32_t)(in && (k[j] == 0u || k[j] > T)) << j;
+    tie |= (uint32_t)(in && k[j] != 0u && k[j] == T) << j;
+  }
+}
+
+__global__ __launch_bounds__(MW_THREADS) void mw_count_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
+                                                              const int32_t* __restrict__ cu_in, int nch, MwWs ws) {
+  MwChunk ck;
+  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
+  const MwState* st = ws.st + ck.b;
+  if (st->skip) return;
+  uint32_t k[MW_TPT], nanb, sure, tie;
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
+  mw_keep_bits(k, nv, st->T, sure, tie);
+  // chunk totals are <= 4096, so the packed halves never carry
+  const uint32_t packed = (uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16);
+  const uint32_t tot = (uint32_t)lane63(wave_incl_scan((int)packed));
+  __shared__ uint32_t red[MW_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0u;
+#pragma unroll
+    for (int v = 0; v < MW_THREADS / 64; ++v) a += red[v];
+    ws.counts[mw_chunk_slot(ck.in0, ck.b) + ck.c] = make_int2((int)(a & 0xffffu), (int)(a >> 16));
+  }
+}
+
+__global__ __launch_bounds__(MW_THREADS) void mw_emit_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
+                                                             const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
+                                                             int nch, int32_t* __restrict__ kept, MwWs ws) {
+  MwChunk ck;
+  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
+  const MwState* st = ws.st + ck.b;
+  if (st->skip) return;
+  const int out0 = cu_kept[ck.b], K = cu_kept[ck.b + 1] - out0;
+  const uint32_t T = st->T;
+  const int needT = st->needT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // kept sure tokens and ties of the sequence's earlier chunks
+  const int2* cnt = ws.counts + mw_chunk_slot(ck.in0, ck.b);
+  int ps = 0, pt = 0;
+  for (int c = tid; c < ck.c; c += MW_THREADS) {
+    const int2 v = cnt[c];
+    ps += v.x;
+    pt += v.y;
+  }
+  ps = lane63(wave_incl_scan(ps));
+  pt = lane63(wave_incl_scan(pt));
+  __shared__ int red[MW_THREADS / 64][2];
+  __shared__ uint32_t red2[MW_THREADS / 64];
+  if (lane == 0) {
+    red[w][0] = ps;
+    red[w][1] = pt;
+  }
+  uint32_t k[MW_TPT], nanb, sure, tie;
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
+  mw_keep_bits(k, nv, T, sure, tie);
+  const uint32_t packed = (uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16);
+  const uint32_t incl = (uint32_t)wave_incl_scan((int)packed);
+  if (lane == 63) red2[w] = incl;
+  __syncthreads();
+  int sure_run = 0, tie_run = 0;
+  uint32_t excl = incl - packed;
+#pragma unroll
+  for (int v = 0; v < MW_THREADS / 64; ++v) {
+    sure_run += red[v][0];
+    tie_run += red[v][1];
+    excl += v < w ? red2[v] : 0u;
+  }
+  const int sure_before = sure_run + (int)(excl & 0xffffu), tie_before = tie_run + (int)(excl >> 16);
+  const int take = min(max(needT - tie_before, 0), __popc(tie));
+  uint32_t rest = tie;  // drop the lowest `take` tie bits from rest: they are kept
+  for (int c = 0; c < take; ++c) rest &= rest - 1u;
+  uint32_t keep = sure | (tie ^ rest);
+  int pos = sure_before + min(tie_before, needT);
+  int32_t* kp = kept + out0;
+  const int tok0 = ck.in0 + ck.i0;
+  while (keep) {
+    const int bit = __builtin_ctz(keep);
+    if (pos < K) kp[pos] = tok0 + bit;  // pos < K always holds; the guard keeps a logic slip in bounds
+    ++pos;
+    keep &= keep - 1u;
+  }
+}
+
+size_t topk_select_workspace_bytes(int B, int64_t T_in, int max_n) {
+  return max_n <= SEL_LDS_MAX || B <= 0 ? 0 : mw_workspace_bytes(B, T_in);
 }
 
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
-                              const int32_t* cu_kept, int B, int max_n, int32_t* kept,
-                              int32_t* status, hipStream_t stream) {
+                              const int32_t* cu_kept, int B, int64_t T_in, int max_n, int32_t* kept,
+                              int32_t* status, void* ws, hipStream_t stream) {
   if (B <= 0) return hipSuccess;
-  return max_n <= SEL_LDS_MAX
-             ? launch_select<false>(s, mask, cu_in, cu_kept, B, kept, status, stream)
-             : launch_select<true>(s, mask, cu_in, cu_kept, B, kept, status, stream);
+  if (max_n <= SEL_LDS_MAX) {
+    constexpr size_t lds = (size_t)SEL_LDS_MAX * sizeof(uint32_t);
+    const hipError_t e = ensure_dynamic_lds<topk_select_kernel>((int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(SEL_THREADS), lds, stream, s, mask, cu_in,
+                       cu_kept, kept, status);
+    return hipGetLastError();
+  }
+  const int nch = (int)(((int64_t)max_n + MW_CHUNK - 1) / MW_CHUNK);
+  const int64_t nblk = (int64_t)nch * B;
+  if (nblk > INT32_MAX) return hipErrorInvalidValue;
+  const MwWs w = mw_carve(ws, B);
+  const dim3 g((unsigned)nblk);
+#define TG_MW(...)                                   \
+  do {                                               \
+    hipLaunchKernelGGL(__VA_ARGS__);                 \
+    const hipError_t e_ = hipGetLastError();         \
+    if (e_ != hipSuccess) return e_;                 \
+  } while (0)
+  TG_MW(mw_init_kernel, dim3(B), dim3(MW_THREADS), 0, stream, w);
+  TG_MW(mw_stats_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, nch, w);
+  TG_MW(mw_plan_kernel, dim3(B), dim3(64), 0, stream, cu_in, cu_kept, max_n, kept, status, w);
+  for (int p = 0; p < MW_PASSES; ++p) {
+    TG_MW(mw_hist_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, nch, w);
+    TG_MW(mw_pick_kernel, dim3(B), dim3(MW_PICK_THREADS), 0, stream, w);
+  }
+  TG_MW(mw_count_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, nch, w);
+  TG_MW(mw_emit_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, cu_kept, nch, kept, w);
+#undef TG_MW
+  return hipSuccess;
 }
 
 }  // namespace tg

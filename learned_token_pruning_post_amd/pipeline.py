@@ -93,6 +93,7 @@ class GatedPrefill:
         lib = tg.lib()
         need = lib.tg_upper_layer_workspace_size(tg.ctypes.byref(dw.dims), T, w.B, w.max_k)
         need = max(need, lib.tg_gate_score_workspace_size(T_in, D, w.dims.H1, tg.dtype_code(dt)))
+        need = max(need, lib.tg_topk_select_workspace_size(w.B, T_in, w.max_n))
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def score(self):
@@ -102,7 +103,7 @@ class GatedPrefill:
     def select(self):
         d = self.dw
         tg.topk_select(self.s, d.keep_mask, d.cu_in, d.cu_kept, d.w.T, d.w.max_n,
-                       kept=self.kept, status=self.status)
+                       kept=self.kept, status=self.status, ws=self.ws)
 
     def compact(self):
         d = self.dw

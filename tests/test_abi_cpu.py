@@ -71,6 +71,23 @@ def test_topk_select_argument_errors(L):
     assert L.tg_topk_select_workspace_size(8, 1 << 17, 1 << 14) == 0
 
 
+def test_topk_select_long_path_workspace(L):
+    """Above 32768 tokens per sequence the selection needs scratch: a 64-byte
+    state and a 4096-bin histogram per sequence, two int32 counts per
+    4096-token chunk slot, each block 256-byte aligned."""
+    B, T_in, max_n = 3, 200000, 100000
+    a = lambda x: (x + 255) // 256 * 256
+    need = L.tg_topk_select_workspace_size(B, T_in, max_n)
+    assert need == a(B * 64) + a(B * 4096 * 4) + a((T_in // 4096 + B + 1) * 8)
+    assert L.tg_topk_select_workspace_size(B, T_in, 32768) == 0
+    assert L.tg_topk_select_workspace_size(B, T_in, 32769) == need
+    f = L.tg_topk_select
+    assert f(FAKE, None, FAKE, FAKE, B, T_in, 5, max_n, FAKE, None, None, 0, None) == WS
+    assert f(FAKE, None, FAKE, FAKE, B, T_in, 5, max_n, FAKE, None, FAKE, need - 1, None) == WS
+    odd = ctypes.c_void_p(0x100000 + 16)
+    assert f(FAKE, None, FAKE, FAKE, B, T_in, 5, max_n, FAKE, None, odd, need, None) == INVALID
+
+
 def test_compact_argument_errors(L):
     f = L.tg_compact
     assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 4, 0, 1, FAKE, FAKE, FAKE, None) == INVALID

@@ -385,14 +385,16 @@ def test_scorer_wide_hidden_uses_partials():
 # selection edge cases
 # ---------------------------------------------------------------------------
 
-def _select_case(N, K, mask, s):
+def _select_case(N, K, mask, s, max_n=None):
     dev = "cuda"
     cu_in = np.concatenate([[0], np.cumsum(N)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
     st = torch.from_numpy(s.astype(np.float32)).to(dev)
     mt = torch.from_numpy(mask.astype(np.uint8)).to(dev)
+    if max_n is None:
+        max_n = int(max(N) if len(N) else 0)
     kept, status = tg.topk_select(st, mt, torch.from_numpy(cu_in).to(dev), torch.from_numpy(cu_k).to(dev),
-                                  int(cu_k[-1]), int(max(N) if len(N) else 0))
+                                  int(cu_k[-1]), max_n)
     torch.cuda.synchronize()
     return kept.cpu().numpy(), status.cpu().numpy()[:len(N)], cu_in, cu_k
 
@@ -535,6 +537,45 @@ def test_select_rounds_ties_across_rounds():
     ref, flags = O.topk_select(s, mask, cu_in, cu_k)
     assert np.array_equal(status, flags.astype(np.int32))
     assert np.array_equal(kept, ref.astype(np.int32))
+
+
+def test_select_chunked_path_budget_extremes_and_short_sequences():
+    """The chunked path (max_n above 32768) on every kind of sequence in one
+    batch: budget = length, budget = forced count, all scores equal, one key
+    above a block of equal ones, lengths on and off 4096-token chunk borders,
+    unaligned sequence starts, one token, an empty sequence."""
+    rng = np.random.default_rng(41)
+    N = [40000, 33001, 36864, 8192, 1, 0, 50003, 4097]
+    K = [40000, 300, 1000, 8191, 1, 0, 20000, 4084]
+    T_in = sum(N)
+    cu = np.concatenate([[0], np.cumsum(N)])
+    s = scores_with_ties(41, T_in, 23)
+    mask = np.zeros(T_in, np.uint8)
+    mask[cu[1] + rng.choice(N[1], 300, replace=False)] = 1  # K = F
+    s[cu[2]:cu[3]] = 0.5                                     # all equal
+    s[cu[3]:cu[4]] = 0.25
+    s[cu[3] + 5000] = 0.75                                   # one key above the block
+    mask[cu[6] + rng.choice(N[6], 700, replace=False)] = 1
+    s[cu[7]:cu[8]] = np.linspace(-1, 1, N[7], dtype=np.float32)
+    s[cu[7] + rng.choice(N[7], 40, replace=False)] = np.nan
+    for max_n in (max(N), 1 << 20):
+        kept, status, cu_in, cu_k = _select_case(N, K, mask, s, max_n=max_n)
+        ref, flags = O.topk_select(s, mask, cu_in, cu_k)
+        assert np.array_equal(status, flags.astype(np.int32))
+        assert np.array_equal(kept, ref.astype(np.int32))
+
+
+def test_select_chunked_path_sequence_longer_than_max_n_is_flagged():
+    """On the chunked path a sequence longer than max_n would have chunks
+    outside the grid: it is flagged with -1 slots, the others are selected."""
+    N, K = [50000, 40000, 100], [10, 20, 5]
+    s = scores_with_ties(6, sum(N), 9)
+    mask = np.zeros(sum(N), np.uint8)
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s, max_n=40000)
+    assert status[0] == tg.DEV_LEN_GT_MAX_N and status[1] == 0 and status[2] == 0
+    assert (kept[:10] == -1).all()
+    ref, _ = O.topk_select(s, mask, cu_in, cu_k)
+    assert np.array_equal(kept[10:], ref[10:].astype(np.int32))
 
 
 def test_select_sequence_longer_than_max_n_is_flagged():
