@@ -109,9 +109,9 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1,
  *                     each sequence, at that sequence's cu_kept offsets
  *  d_status  [B]      int32 device out, TG_DEV_* flags of each sequence
  *                     (overwritten, 0 when fine); may be NULL
- *  ws, ws_bytes       scratch for max_n > 32768 (state and a 4096-bin
- *                     histogram per sequence, two counts per 4096-token chunk;
- *                     B * 16.4 KB + T_in / 512 bytes); NULL / 0 otherwise.
+ *  ws, ws_bytes       scratch for max_n > 32768 (three 4096-bin histograms
+ *                     per sequence, a 32-byte record per 4096-token chunk:
+ *                     about B * 48 KB + T_in / 128 bytes); NULL / 0 otherwise.
  *                     Too small: TG_ERR_WORKSPACE; misaligned: TG_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
 size_t tg_topk_select_workspace_size(int B, int64_t T_in, int max_n);

@@ -130,7 +130,7 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t
   TG_CHECK(T_in == 0 || s, TG_ERR_INVALID_ARG);
   TG_CHECK(T == 0 || kept_idx, TG_ERR_INVALID_ARG);
   // one workgroup per (sequence, 4096-token chunk) on the long-sequence path
-  TG_CHECK((int64_t)((max_n + 4095) / 4096) * B <= INT_MAX, TG_ERR_INVALID_ARG);
+  TG_CHECK(((int64_t)max_n + 4095) / 4096 * B <= INT_MAX, TG_ERR_INVALID_ARG);
   const size_t need = tg::topk_select_workspace_bytes(B, T_in, max_n);
   TG_CHECK(need == 0 || (ws && ws_bytes >= need), TG_ERR_WORKSPACE);
   TG_CHECK(need == 0 || ((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);

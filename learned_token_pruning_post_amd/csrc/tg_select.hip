@@ -388,86 +388,96 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
 // ---------------------------------------------------------------------------
 // Sequences longer than SEL_LDS_MAX: the LDS path's range search and emit,
 // spread over workgroups of MW_CHUNK consecutive tokens of one sequence, as a
-// chain of kernels in which no workgroup waits for another:
-//   init   clears each sequence's histogram and statistics (workspace)
-//   stats  per chunk: forced count, NaN seen, candidate key min and max,
-//          merged with global atomics
-//   plan   per sequence: status flags and -1 slots for a rejected sequence;
-//          the threshold at once when the budget takes no candidate, every
-//          candidate, or the live range is one key; else [kmin, kmax]
-//   3 x  { hist (per chunk: LDS histogram of the live range in 4096
-//          power-of-two bins, merged with global atomics), pick (per
-//          sequence: the bin that holds the threshold; clears the histogram
-//          for the next pass) }: a range shrinks 2^12-fold per pass, so three
-//          passes reach one key from any 32-bit span
-//   count  per chunk: sure keeps (forced or key > T) and ties (key == T)
-//   emit   per chunk: the earlier chunks' counts, one block scan, the first
-//          needT ties of the sequence in index order, indices ascending
-// Keys are formed again from the scores on every walk (sel_key), so the
-// workspace holds per sequence only its state and one histogram, plus two
-// counts per chunk. Thread t of a chunk owns its tokens 16t..16t+15.
+// chain of six kernels in which no workgroup waits for another:
+//   stats      per chunk: forced count, NaN seen, candidate key min and max
+//              (one record per chunk); chunk 0 also clears the sequence's
+//              three histograms
+//   hist 0..2  per chunk: LDS histogram of the live key range in 4096
+//              power-of-two bins, merged into that pass's global histogram
+//              with atomics
+//   count      per chunk: sure keeps (forced or key > T) and ties (key == T)
+//   emit       per chunk: the earlier chunks' counts, one block scan, the
+//              first needT ties of the sequence in index order, indices
+//              written ascending; chunk 0 writes the status (and -1 slots
+//              for a rejected sequence)
+// The per-sequence decisions (status flags, the live range, the bin of each
+// pass) are not stored: every workgroup derives them again from the chunk
+// records and the finished histograms (mw_resolve), which costs a
+// reduction over the chunk records and one 4096-bin scan per finished pass
+// and saves a launch per decision. A range shrinks 2^12-fold per pass, so
+// three passes reach one key from any 32-bit span. Keys are formed again
+// from the scores on every walk (sel_key). Thread t of a chunk owns its
+// tokens 16t..16t+15.
 // ---------------------------------------------------------------------------
 constexpr int MW_THREADS = 256;
+constexpr int MW_WAVES = MW_THREADS / 64;
 constexpr int MW_TPT = 16;                     // consecutive tokens per thread
 constexpr int MW_CHUNK = MW_THREADS * MW_TPT;  // tokens per workgroup
 constexpr int MW_BINS = 4096;
-constexpr int MW_PICK_THREADS = MW_BINS / 4;   // 4 bins per thread
 constexpr int MW_PASSES = 3;
+static_assert(MW_BINS == MW_THREADS * 16, "a thread scans 16 bins");
 
-struct MwState {
-  uint32_t lo, hi;      // live key range of the search
-  int need;             // candidates still to take inside [lo, hi]
-  int active;           // the range search is still running
-  uint32_t T;           // threshold key
-  int needT;            // keys equal to T that are kept, lowest indices first
-  int nf, nan_seen;     // forced tokens; some candidate score is NaN
-  uint32_t kmin, kmax;  // candidate key range
-  int skip;             // rejected sequence: its slots already hold -1
-  int pad[5];
+struct MwRec {                 // one per chunk
+  int nf, nan_seen;            // forced tokens; some score is NaN
+  uint32_t kmin, kmax;         // candidate key range (kmin > kmax: none)
+  int sure, tie;               // kept sure tokens and ties (count kernel)
+  int pad[2];
 };
-static_assert(sizeof(MwState) == 64, "64-byte per-sequence state");
+static_assert(sizeof(MwRec) == 32, "32-byte chunk record");
 
 struct MwWs {
-  MwState* st;     // [B]
-  uint32_t* hist;  // [B][MW_BINS]
-  int2* counts;    // (sure, tie) per chunk; chunk c of sequence b at mw_chunk_slot(in0_b, b) + c
+  uint32_t* hist;  // [B][MW_PASSES][MW_BINS]
+  MwRec* rec;      // chunk c of sequence b at mw_chunk_slot(in0_b, b) + c
 };
 
 __host__ __device__ inline size_t mw_align(size_t x) { return (x + 255) & ~(size_t)255; }
-// Chunk slots of sequence b start at in0_b / MW_CHUNK + b: the sequences
-// before b hold sum(ceil(N / MW_CHUNK)) <= in0_b / MW_CHUNK + b chunks, so
-// the ranges never overlap and T_in / MW_CHUNK + B + 1 slots cover a batch.
+// Chunk slots of sequence b start at in0_b / MW_CHUNK + b. A sequence uses
+// max(ceil(N / MW_CHUNK), 1) slots (an empty one keeps slot 0 for its
+// status), and floor(in0 / C) + max(ceil(N / C), 1) <= floor((in0 + N) / C) + 1,
+// so the ranges never overlap and T_in / MW_CHUNK + B + 1 slots cover a batch.
 __device__ __forceinline__ int64_t mw_chunk_slot(int in0, int b) { return (int64_t)(in0 / MW_CHUNK) + b; }
 
 static size_t mw_workspace_bytes(int B, int64_t T_in) {
-  return mw_align((size_t)B * sizeof(MwState)) + mw_align((size_t)B * MW_BINS * sizeof(uint32_t)) +
-         mw_align((size_t)(T_in / MW_CHUNK + B + 1) * sizeof(int2));
+  return mw_align((size_t)B * MW_PASSES * MW_BINS * sizeof(uint32_t)) +
+         mw_align((size_t)(T_in / MW_CHUNK + B + 1) * sizeof(MwRec));
 }
 
 static MwWs mw_carve(void* ws, int B) {
   unsigned char* p = static_cast<unsigned char*>(ws);
   MwWs w;
-  w.st = reinterpret_cast<MwState*>(p);
-  p += mw_align((size_t)B * sizeof(MwState));
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += mw_align((size_t)B * MW_BINS * sizeof(uint32_t));
-  w.counts = reinterpret_cast<int2*>(p);
+  p += mw_align((size_t)B * MW_PASSES * MW_BINS * sizeof(uint32_t));
+  w.rec = reinterpret_cast<MwRec*>(p);
   return w;
+}
+
+// A thread's 16 scores and mask bytes, loaded with 16-byte loads when the
+// sequence is aligned and all 16 tokens exist (issued before the workgroup's
+// decisions are derived, so their latency overlaps that work).
+struct MwRaw {
+  f32x4 x[MW_TPT / 4];
+  u32x4 m;
+};
+__device__ __forceinline__ void mw_issue(const float* __restrict__ sp, const uint8_t* __restrict__ mp, int n,
+                                         int i0, bool vec, MwRaw& raw) {
+  if (vec && n - i0 >= MW_TPT) {
+#pragma unroll
+    for (int q = 0; q < MW_TPT / 4; ++q) raw.x[q] = *reinterpret_cast<const f32x4*>(sp + i0 + 4 * q);
+    raw.m = mp ? *reinterpret_cast<const u32x4*>(mp + i0) : u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // keys of the thread's tokens [i0, i0 + 16) of a sequence; returns how many
 // of them exist (tokens at or past n read as key 0 and are never used);
 // nan_bits marks NaN scores, forced tokens included (they set the status flag)
 __device__ __forceinline__ int mw_keys(const float* __restrict__ sp, const uint8_t* __restrict__ mp,
-                                       int n, int i0, bool vec, uint32_t (&k)[MW_TPT], uint32_t& nan_bits) {
+                                       int n, int i0, bool vec, const MwRaw& raw, uint32_t (&k)[MW_TPT],
+                                       uint32_t& nan_bits) {
   const int nv = min(max(n - i0, 0), MW_TPT);
   nan_bits = 0u;
   if (vec && nv == MW_TPT) {
-    f32x4 x[MW_TPT / 4];
-    u32x4 m = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < MW_TPT / 4; ++q) x[q] = *reinterpret_cast<const f32x4*>(sp + i0 + 4 * q);
-    if (mp) m = *reinterpret_cast<const u32x4*>(mp + i0);
+    const f32x4* x = raw.x;
+    const u32x4 m = raw.m;
 #pragma unroll
     for (int q = 0; q < MW_TPT / 4; ++q)
 #pragma unroll
@@ -487,20 +497,24 @@ __device__ __forceinline__ int mw_keys(const float* __restrict__ sp, const uint8
   return nv;
 }
 
-// the workgroup's sequence and chunk; false if the chunk is past the sequence
+// the workgroup's sequence and chunk; false if the chunk is past the
+// sequence (chunk 0 always exists, also for an empty sequence)
 struct MwChunk {
-  int b, c, in0, n, i0;
+  int b, c, in0, n, K, out0, i0, nchunks;
   const float* sp;
   const uint8_t* mp;
   bool vec;
 };
-__device__ __forceinline__ bool mw_chunk(const float* s, const uint8_t* mask, const int32_t* cu_in, int nch,
-                                         MwChunk& ck) {
+__device__ __forceinline__ bool mw_chunk(const float* s, const uint8_t* mask, const int32_t* cu_in,
+                                         const int32_t* cu_kept, int nch, MwChunk& ck) {
   ck.b = blockIdx.x / nch;
   ck.c = blockIdx.x % nch;
   ck.in0 = cu_in[ck.b];
   ck.n = cu_in[ck.b + 1] - ck.in0;
-  if (ck.c * MW_CHUNK >= ck.n) return false;
+  ck.nchunks = max((ck.n + MW_CHUNK - 1) / MW_CHUNK, 1);
+  if (ck.c >= ck.nchunks) return false;
+  ck.out0 = cu_kept[ck.b];
+  ck.K = cu_kept[ck.b + 1] - ck.out0;
   ck.i0 = ck.c * MW_CHUNK + (int)threadIdx.x * MW_TPT;
   ck.sp = s + ck.in0;
   ck.mp = mask ? mask + ck.in0 : nullptr;
@@ -508,25 +522,186 @@ __device__ __forceinline__ bool mw_chunk(const float* s, const uint8_t* mask, co
   return true;
 }
 
-__global__ __launch_bounds__(MW_THREADS) void mw_init_kernel(MwWs ws) {
-  const int b = blockIdx.x;
-  uint32_t* h = ws.hist + (size_t)b * MW_BINS;
-  for (int i = threadIdx.x; i < MW_BINS; i += MW_THREADS) h[i] = 0u;
-  if (threadIdx.x == 0) {
-    MwState z = {};
-    z.kmin = 0xffffffffu;
-    ws.st[b] = z;
+// Block-wide sum / or / min / max of one value per thread (all threads get
+// the result). `scratch` holds MW_WAVES words; the call syncs twice.
+template <class Op>
+__device__ __forceinline__ uint32_t mw_block_reduce(uint32_t x, uint32_t id, Op op, uint32_t* scratch) {
+  x = (uint32_t)lane63((int)wave_scan_u32(x, id, op));
+  __syncthreads();  // scratch is free
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint32_t r = id;
+#pragma unroll
+  for (int v = 0; v < MW_WAVES; ++v) r = op(r, scratch[v]);
+  return r;
+}
+
+// Block-wide (sum, or, min, max) of four values per thread in one exchange.
+__device__ __forceinline__ void mw_block_stats(uint32_t& nf, uint32_t& nan_seen, uint32_t& kmin, uint32_t& kmax,
+                                               uint32_t (*scratch)[4]) {
+  nf = (uint32_t)lane63((int)wave_scan_u32(nf, 0u, [](uint32_t a, uint32_t b) { return a + b; }));
+  nan_seen = (uint32_t)lane63((int)wave_scan_u32(nan_seen, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
+  kmin = (uint32_t)lane63((int)wave_scan_u32(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
+  kmax = (uint32_t)lane63((int)wave_scan_u32(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }));
+  __syncthreads();  // scratch is free
+  if ((threadIdx.x & 63) == 0) {
+    const int w = threadIdx.x >> 6;
+    scratch[w][0] = nf;
+    scratch[w][1] = nan_seen;
+    scratch[w][2] = kmin;
+    scratch[w][3] = kmax;
+  }
+  __syncthreads();
+  nf = 0u;
+  nan_seen = 0u;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int v = 0; v < MW_WAVES; ++v) {
+    nf += scratch[v][0];
+    nan_seen |= scratch[v][1];
+    kmin = min(kmin, scratch[v][2]);
+    kmax = max(kmax, scratch[v][3]);
   }
 }
 
+struct MwPlan {
+  int flags;           // status flags of the sequence
+  bool reject;         // flags & (1 | 2 | 8): slots hold -1
+  bool active;         // the range search is still open
+  uint32_t lo, hi;     // live range (active)
+  int need;            // candidates still to take inside [lo, hi] (active)
+  uint32_t T;          // threshold key (done)
+  int needT;           // keys equal to T that are kept (done)
+};
+
+// The sequence's decisions after `npass` finished histogram passes, derived
+// by the whole workgroup (uniform result). Same rules as the LDS path:
+// forced tokens always kept; K - F slots to the highest keys; equal keys to
+// the lowest indices.
+__device__ __forceinline__ MwPlan mw_resolve(const MwChunk& ck, int max_n, const MwWs& ws, int npass) {
+  __shared__ uint32_t scratch[MW_WAVES][4];
+  __shared__ int pick[2];
+  MwPlan P = {};
+  if (ck.n > max_n) {  // chunks outside the grid: rejected without statistics
+    P.flags = 8;  // TG_DEV_LEN_GT_MAX_N
+    P.reject = true;
+    return P;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // every load first: the chunk records, then the bins of the finished passes
+  // that this thread scans (16 per pass, see below)
+  const uint32_t* h0 = ws.hist + (size_t)ck.b * MW_PASSES * MW_BINS;
+  const int tb = 16 * (MW_THREADS - 1 - tid);
+  u32x4 hv[MW_PASSES][4];
+#pragma unroll
+  for (int p = 0; p < MW_PASSES; ++p)
+    if (p < npass)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[p][q] = reinterpret_cast<const u32x4*>(h0 + (size_t)p * MW_BINS + tb)[q];
+  const MwRec* rec = ws.rec + mw_chunk_slot(ck.in0, ck.b);
+  uint32_t nf = 0u, nan_seen = 0u, kmin = 0xffffffffu, kmax = 0u;
+  for (int c = tid; c < ck.nchunks; c += MW_THREADS) {
+    const MwRec r = rec[c];
+    nf += (uint32_t)r.nf;
+    nan_seen |= (uint32_t)r.nan_seen;
+    kmin = min(kmin, r.kmin);
+    kmax = max(kmax, r.kmax);
+  }
+  mw_block_stats(nf, nan_seen, kmin, kmax, scratch);
+  const int n = ck.n, K = ck.K;
+  P.flags = (nan_seen ? 4 : 0) | (K > n ? 2 : 0) | ((int)nf > K ? 1 : 0);
+  if (P.flags & 3) {
+    P.reject = true;
+    return P;
+  }
+  const int C = n - (int)nf, r = K - (int)nf;  // candidates, slots for them
+  if (r == 0) {
+    P.T = 0xffffffffu;  // no key reaches it
+    return P;
+  }
+  if (r == C) {
+    P.T = 0u;  // every token is kept
+    P.needT = C;
+    return P;
+  }
+  uint32_t lo = kmin, hi = kmax;
+  int need = r;
+#pragma unroll
+  for (int p = 0; p <= MW_PASSES; ++p) {
+    if (lo == hi) {
+      P.T = lo;
+      P.needT = need;
+      return P;
+    }
+    if (p == npass) break;
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __clz(span);
+    const int shift = bits > 12 ? bits - 12 : 0;
+    // thread t owns bins 16t'..16t'+15 with t' = 255 - t, so an inclusive
+    // scan in thread order counts the keys in every bin >= 16t' (bins past
+    // the range were never incremented)
+    int h[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[4 * q + e] = (int)hv[p < MW_PASSES ? p : 0][q][e];
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mine += h[e];
+    int incl = wave_incl_scan(mine);
+    __syncthreads();  // scratch and pick are free
+    if (lane == 63) scratch[w][0] = (uint32_t)incl;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < MW_WAVES; ++v) incl += v < w ? (int)scratch[v][0] : 0;
+    int above = incl - mine;  // keys in bins above tb + 15
+    if (above < need && incl >= need) {
+      int bstar = tb;
+#pragma unroll
+      for (int e = 15; e >= 0; --e) {
+        if (above + h[e] >= need) {
+          bstar = tb + e;
+          break;
+        }
+        above += h[e];
+      }
+      pick[0] = bstar;
+      pick[1] = above;
+    }
+    __syncthreads();
+    const uint64_t nlo = (uint64_t)lo + ((uint64_t)pick[0] << shift);
+    const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+    need -= pick[1];
+    if (shift == 0) {
+      P.T = lo;
+      P.needT = need;
+      return P;
+    }
+  }
+  P.active = true;
+  P.lo = lo;
+  P.hi = hi;
+  P.need = need;
+  return P;
+}
+
 __global__ __launch_bounds__(MW_THREADS) void mw_stats_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
-                                                              const int32_t* __restrict__ cu_in, int nch, MwWs ws) {
+                                                              const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
+                                                              int nch, MwWs ws) {
   MwChunk ck;
-  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
+  if (!mw_chunk(s, mask, cu_in, cu_kept, nch, ck)) return;
+  if (ck.c == 0) {  // the histograms of this call's passes start from zero
+    u32x4* h = reinterpret_cast<u32x4*>(ws.hist + (size_t)ck.b * MW_PASSES * MW_BINS);
+    for (int i = threadIdx.x; i < MW_PASSES * MW_BINS / 4; i += MW_THREADS) h[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  MwRaw raw;
+  mw_issue(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw);
   uint32_t k[MW_TPT], nanb;
-  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
-  int nf = 0;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw, k, nanb);
+  uint32_t nf = 0u, kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < MW_TPT; ++j)
     if (j < nv) {
@@ -536,86 +711,29 @@ __global__ __launch_bounds__(MW_THREADS) void mw_stats_kernel(const float* __res
         kmax = max(kmax, k[j]);
       }
     }
-  int nan_seen = nanb != 0u;
-  nf = lane63(wave_incl_scan(nf));
-  nan_seen = lane63(wave_incl_scan(nan_seen));
-  kmin = (uint32_t)lane63((int)wave_scan_u32(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
-  kmax = (uint32_t)lane63((int)wave_scan_u32(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }));
-  __shared__ uint32_t red[MW_THREADS / 64][4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) {
-    red[w][0] = (uint32_t)nf;
-    red[w][1] = (uint32_t)nan_seen;
-    red[w][2] = kmin;
-    red[w][3] = kmax;
-  }
-  __syncthreads();
+  __shared__ uint32_t scratch[MW_WAVES][4];
+  uint32_t nan_seen = nanb != 0u;
+  mw_block_stats(nf, nan_seen, kmin, kmax, scratch);
   if (threadIdx.x == 0) {
-    uint32_t a = 0u, o = 0u, lo = 0xffffffffu, hi = 0u;
-#pragma unroll
-    for (int v = 0; v < MW_THREADS / 64; ++v) {
-      a += red[v][0];
-      o |= red[v][1];
-      lo = min(lo, red[v][2]);
-      hi = max(hi, red[v][3]);
-    }
-    MwState* st = ws.st + ck.b;
-    if (a) atomicAdd(&st->nf, (int)a);
-    if (o) atomicOr(&st->nan_seen, 1);
-    if (lo <= hi) {
-      atomicMin(&st->kmin, lo);
-      atomicMax(&st->kmax, hi);
-    }
+    MwRec* r = ws.rec + mw_chunk_slot(ck.in0, ck.b) + ck.c;
+    r->nf = (int)nf;
+    r->nan_seen = (int)nan_seen;
+    r->kmin = kmin;
+    r->kmax = kmax;
   }
 }
 
-// One wave per sequence: flags, rejection, or the start of the range search.
-__global__ __launch_bounds__(64) void mw_plan_kernel(const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
-                                                     int max_n, int32_t* __restrict__ kept, int32_t* __restrict__ status,
-                                                     MwWs ws) {
-  const int b = blockIdx.x;
-  const int in0 = cu_in[b], n = cu_in[b + 1] - in0;
-  const int out0 = cu_kept[b], K = cu_kept[b + 1] - out0;
-  MwState* st = ws.st + b;
-  const int nf = st->nf, nan_seen = st->nan_seen;
-  const uint32_t kmin = st->kmin, kmax = st->kmax;
-  // a sequence longer than max_n has chunks outside the grid: rejected
-  const int flags = n > max_n ? 8 : ((nan_seen ? 4 : 0) | (K > n ? 2 : 0) | (nf > K ? 1 : 0));
-  if (threadIdx.x == 0 && status) status[b] = flags;
-  if (flags & 11) {
-    for (int i = threadIdx.x; i < K; i += 64) kept[out0 + i] = -1;
-    if (threadIdx.x == 0) st->skip = 1;
-    return;
-  }
-  if (threadIdx.x != 0) return;
-  const int C = n - nf, r = K - nf;  // candidates, slots for them
-  uint32_t T = 0u;
-  int needT = 0, active = 0;
-  if (r == 0) {
-    T = 0xffffffffu;  // no key reaches it
-  } else if (r == C) {
-    needT = C;  // T = 0: every token is kept
-  } else if (kmin == kmax) {
-    T = kmin;
-    needT = r;
-  } else {
-    active = 1;
-  }
-  st->lo = kmin;
-  st->hi = kmax;
-  st->need = r;
-  st->T = T;
-  st->needT = needT;
-  st->active = active;
-}
-
+template <int PASS>
 __global__ __launch_bounds__(MW_THREADS) void mw_hist_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
-                                                             const int32_t* __restrict__ cu_in, int nch, MwWs ws) {
+                                                             const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
+                                                             int nch, int max_n, MwWs ws) {
   MwChunk ck;
-  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
-  const MwState* st = ws.st + ck.b;
-  if (!st->active) return;
-  const uint32_t lo = st->lo, span = st->hi - lo;
+  if (!mw_chunk(s, mask, cu_in, cu_kept, nch, ck)) return;
+  MwRaw raw;
+  mw_issue(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw);
+  const MwPlan P = mw_resolve(ck, max_n, ws, PASS);
+  if (!P.active) return;
+  const uint32_t lo = P.lo, span = P.hi - lo;
   const int bits = 32 - __clz(span);
   const int shift = bits > 12 ? bits - 12 : 0;
   const int nb = (int)(span >> shift) + 1;
@@ -623,72 +741,14 @@ __global__ __launch_bounds__(MW_THREADS) void mw_hist_kernel(const float* __rest
   for (int i = threadIdx.x; i < nb; i += MW_THREADS) h[i] = 0u;
   __syncthreads();
   uint32_t k[MW_TPT], nanb;
-  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw, k, nanb);
 #pragma unroll
   for (int j = 0; j < MW_TPT; ++j)
     if (j < nv && k[j] - lo <= span) atomicAdd(&h[(k[j] - lo) >> shift], 1u);
   __syncthreads();
-  uint32_t* gh = ws.hist + (size_t)ck.b * MW_BINS;
+  uint32_t* gh = ws.hist + ((size_t)ck.b * MW_PASSES + PASS) * MW_BINS;
   for (int i = threadIdx.x; i < nb; i += MW_THREADS)
     if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-// Per sequence: thread t owns bins 4t'..4t'+3 with t' = 1023 - t, so an
-// inclusive scan in thread order counts the keys in every bin >= 4t'.
-__global__ __launch_bounds__(MW_PICK_THREADS) void mw_pick_kernel(MwWs ws) {
-  const int b = blockIdx.x;
-  MwState* st = ws.st + b;
-  if (!st->active) return;
-  const uint32_t lo = st->lo, hi = st->hi, span = hi - lo;
-  const int need = st->need;
-  const int bits = 32 - __clz(span);
-  const int shift = bits > 12 ? bits - 12 : 0;
-  const int nb = (int)(span >> shift) + 1;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int tb = 4 * (MW_PICK_THREADS - 1 - tid);
-  uint32_t* gh = ws.hist + (size_t)b * MW_BINS;
-  int h[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = tb + e < nb ? (int)gh[tb + e] : 0;
-    gh[tb + e] = 0u;  // cleared for the next pass (only this thread reads these bins)
-  }
-  __shared__ int red[MW_PICK_THREADS / 64 + 3];
-  const int mine = h[0] + h[1] + h[2] + h[3];
-  int incl = wave_incl_scan(mine);
-  if (lane == 63) red[w] = incl;
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < MW_PICK_THREADS / 64; ++v) incl += v < w ? red[v] : 0;
-  int above = incl - mine;  // keys in bins above tb + 3
-  constexpr int R = MW_PICK_THREADS / 64;
-  if (above < need && incl >= need) {
-    int bstar = tb;
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (above + h[e] >= need) {
-        bstar = tb + e;
-        break;
-      }
-      above += h[e];
-    }
-    red[R] = bstar;
-    red[R + 1] = above;
-  }
-  __syncthreads();
-  if (tid != 0) return;
-  const uint64_t nlo = (uint64_t)lo + ((uint64_t)red[R] << shift);
-  const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
-  const uint32_t lo2 = (uint32_t)nlo, hi2 = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
-  const int need2 = need - red[R + 1];
-  st->lo = lo2;
-  st->hi = hi2;
-  st->need = need2;
-  if (shift == 0 || lo2 == hi2) {
-    st->T = lo2;
-    st->needT = need2;
-    st->active = 0;
-  }
 }
 
 // sure keeps (forced, key 0, or key > T) and ties (candidate key == T) of the
@@ -706,81 +766,77 @@ __device__ __forceinline__ void mw_keep_bits(const uint32_t (&k)[MW_TPT], int nv
 }
 
 __global__ __launch_bounds__(MW_THREADS) void mw_count_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
-                                                              const int32_t* __restrict__ cu_in, int nch, MwWs ws) {
+                                                              const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
+                                                              int nch, int max_n, MwWs ws) {
   MwChunk ck;
-  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
-  const MwState* st = ws.st + ck.b;
-  if (st->skip) return;
+  if (!mw_chunk(s, mask, cu_in, cu_kept, nch, ck)) return;
+  MwRaw raw;
+  mw_issue(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw);
+  const MwPlan P = mw_resolve(ck, max_n, ws, MW_PASSES);
+  if (P.reject) return;
   uint32_t k[MW_TPT], nanb, sure, tie;
-  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
-  mw_keep_bits(k, nv, st->T, sure, tie);
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw, k, nanb);
+  mw_keep_bits(k, nv, P.T, sure, tie);
   // chunk totals are <= 4096, so the packed halves never carry
-  const uint32_t packed = (uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16);
-  const uint32_t tot = (uint32_t)lane63(wave_incl_scan((int)packed));
-  __shared__ uint32_t red[MW_THREADS / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
-  __syncthreads();
+  __shared__ uint32_t scratch[MW_WAVES];
+  const uint32_t tot = mw_block_reduce((uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16), 0u,
+                                       [](uint32_t a, uint32_t b) { return a + b; }, scratch);
   if (threadIdx.x == 0) {
-    uint32_t a = 0u;
-#pragma unroll
-    for (int v = 0; v < MW_THREADS / 64; ++v) a += red[v];
-    ws.counts[mw_chunk_slot(ck.in0, ck.b) + ck.c] = make_int2((int)(a & 0xffffu), (int)(a >> 16));
+    MwRec* r = ws.rec + mw_chunk_slot(ck.in0, ck.b) + ck.c;
+    r->sure = (int)(tot & 0xffffu);
+    r->tie = (int)(tot >> 16);
   }
 }
 
 __global__ __launch_bounds__(MW_THREADS) void mw_emit_kernel(const float* __restrict__ s, const uint8_t* __restrict__ mask,
                                                              const int32_t* __restrict__ cu_in, const int32_t* __restrict__ cu_kept,
-                                                             int nch, int32_t* __restrict__ kept, MwWs ws) {
+                                                             int nch, int max_n, int32_t* __restrict__ kept,
+                                                             int32_t* __restrict__ status, MwWs ws) {
   MwChunk ck;
-  if (!mw_chunk(s, mask, cu_in, nch, ck)) return;
-  const MwState* st = ws.st + ck.b;
-  if (st->skip) return;
-  const int out0 = cu_kept[ck.b], K = cu_kept[ck.b + 1] - out0;
-  const uint32_t T = st->T;
-  const int needT = st->needT;
+  if (!mw_chunk(s, mask, cu_in, cu_kept, nch, ck)) return;
+  MwRaw raw;
+  mw_issue(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw);
+  const MwPlan P = mw_resolve(ck, max_n, ws, MW_PASSES);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t* kp = kept + ck.out0;
+  if (ck.c == 0 && tid == 0 && status) status[ck.b] = P.flags;
+  if (P.reject) {
+    if (ck.c == 0)
+      for (int i = tid; i < ck.K; i += MW_THREADS) kp[i] = -1;
+    return;
+  }
   // kept sure tokens and ties of the sequence's earlier chunks
-  const int2* cnt = ws.counts + mw_chunk_slot(ck.in0, ck.b);
-  int ps = 0, pt = 0;
+  const MwRec* rec = ws.rec + mw_chunk_slot(ck.in0, ck.b);
+  uint32_t ps = 0u, pt = 0u;
   for (int c = tid; c < ck.c; c += MW_THREADS) {
-    const int2 v = cnt[c];
-    ps += v.x;
-    pt += v.y;
+    ps += (uint32_t)rec[c].sure;
+    pt += (uint32_t)rec[c].tie;
   }
-  ps = lane63(wave_incl_scan(ps));
-  pt = lane63(wave_incl_scan(pt));
-  __shared__ int red[MW_THREADS / 64][2];
-  __shared__ uint32_t red2[MW_THREADS / 64];
-  if (lane == 0) {
-    red[w][0] = ps;
-    red[w][1] = pt;
-  }
+  __shared__ uint32_t scratch[MW_WAVES];
+  const int sure_run = (int)mw_block_reduce(ps, 0u, [](uint32_t a, uint32_t b) { return a + b; }, scratch);
+  const int tie_run = (int)mw_block_reduce(pt, 0u, [](uint32_t a, uint32_t b) { return a + b; }, scratch);
   uint32_t k[MW_TPT], nanb, sure, tie;
-  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, k, nanb);
-  mw_keep_bits(k, nv, T, sure, tie);
+  const int nv = mw_keys(ck.sp, ck.mp, ck.n, ck.i0, ck.vec, raw, k, nanb);
+  mw_keep_bits(k, nv, P.T, sure, tie);
   const uint32_t packed = (uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16);
   const uint32_t incl = (uint32_t)wave_incl_scan((int)packed);
-  if (lane == 63) red2[w] = incl;
+  __syncthreads();  // scratch is free
+  if (lane == 63) scratch[w] = incl;
   __syncthreads();
-  int sure_run = 0, tie_run = 0;
   uint32_t excl = incl - packed;
 #pragma unroll
-  for (int v = 0; v < MW_THREADS / 64; ++v) {
-    sure_run += red[v][0];
-    tie_run += red[v][1];
-    excl += v < w ? red2[v] : 0u;
-  }
+  for (int v = 0; v < MW_WAVES; ++v) excl += v < w ? scratch[v] : 0u;
+  const int needT = P.needT;
   const int sure_before = sure_run + (int)(excl & 0xffffu), tie_before = tie_run + (int)(excl >> 16);
   const int take = min(max(needT - tie_before, 0), __popc(tie));
   uint32_t rest = tie;  // drop the lowest `take` tie bits from rest: they are kept
   for (int c = 0; c < take; ++c) rest &= rest - 1u;
   uint32_t keep = sure | (tie ^ rest);
   int pos = sure_before + min(tie_before, needT);
-  int32_t* kp = kept + out0;
   const int tok0 = ck.in0 + ck.i0;
   while (keep) {
     const int bit = __builtin_ctz(keep);
-    if (pos < K) kp[pos] = tok0 + bit;  // pos < K always holds; the guard keeps a logic slip in bounds
+    if (pos < ck.K) kp[pos] = tok0 + bit;  // pos < K always holds; the guard keeps a logic slip in bounds
     ++pos;
     keep &= keep - 1u;
   }
@@ -793,6 +849,7 @@ size_t topk_select_workspace_bytes(int B, int64_t T_in, int max_n) {
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
                               const int32_t* cu_kept, int B, int64_t T_in, int max_n, int32_t* kept,
                               int32_t* status, void* ws, hipStream_t stream) {
+  (void)T_in;
   if (B <= 0) return hipSuccess;
   if (max_n <= SEL_LDS_MAX) {
     constexpr size_t lds = (size_t)SEL_LDS_MAX * sizeof(uint32_t);
@@ -806,22 +863,19 @@ hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t
   const int64_t nblk = (int64_t)nch * B;
   if (nblk > INT32_MAX) return hipErrorInvalidValue;
   const MwWs w = mw_carve(ws, B);
-  const dim3 g((unsigned)nblk);
-#define TG_MW(...)                                   \
-  do {                                               \
-    hipLaunchKernelGGL(__VA_ARGS__);                 \
-    const hipError_t e_ = hipGetLastError();         \
-    if (e_ != hipSuccess) return e_;                 \
+  const dim3 g((unsigned)nblk), t(MW_THREADS);
+#define TG_MW(...)                           \
+  do {                                       \
+    hipLaunchKernelGGL(__VA_ARGS__);         \
+    const hipError_t e_ = hipGetLastError(); \
+    if (e_ != hipSuccess) return e_;         \
   } while (0)
-  TG_MW(mw_init_kernel, dim3(B), dim3(MW_THREADS), 0, stream, w);
-  TG_MW(mw_stats_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, nch, w);
-  TG_MW(mw_plan_kernel, dim3(B), dim3(64), 0, stream, cu_in, cu_kept, max_n, kept, status, w);
-  for (int p = 0; p < MW_PASSES; ++p) {
-    TG_MW(mw_hist_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, nch, w);
-    TG_MW(mw_pick_kernel, dim3(B), dim3(MW_PICK_THREADS), 0, stream, w);
-  }
-  TG_MW(mw_count_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, nch, w);
-  TG_MW(mw_emit_kernel, g, dim3(MW_THREADS), 0, stream, s, mask, cu_in, cu_kept, nch, kept, w);
+  TG_MW(mw_stats_kernel, g, t, 0, stream, s, mask, cu_in, cu_kept, nch, w);
+  TG_MW(mw_hist_kernel<0>, g, t, 0, stream, s, mask, cu_in, cu_kept, nch, max_n, w);
+  TG_MW(mw_hist_kernel<1>, g, t, 0, stream, s, mask, cu_in, cu_kept, nch, max_n, w);
+  TG_MW(mw_hist_kernel<2>, g, t, 0, stream, s, mask, cu_in, cu_kept, nch, max_n, w);
+  TG_MW(mw_count_kernel, g, t, 0, stream, s, mask, cu_in, cu_kept, nch, max_n, w);
+  TG_MW(mw_emit_kernel, g, t, 0, stream, s, mask, cu_in, cu_kept, nch, max_n, kept, status, w);
 #undef TG_MW
   return hipSuccess;
 }

@@ -72,13 +72,13 @@ def test_topk_select_argument_errors(L):
 
 
 def test_topk_select_long_path_workspace(L):
-    """Above 32768 tokens per sequence the selection needs scratch: a 64-byte
-    state and a 4096-bin histogram per sequence, two int32 counts per
-    4096-token chunk slot, each block 256-byte aligned."""
+    """Above 32768 tokens per sequence the selection needs scratch: three
+    4096-bin histograms per sequence and a 32-byte record per 4096-token
+    chunk slot, each block 256-byte aligned."""
     B, T_in, max_n = 3, 200000, 100000
     a = lambda x: (x + 255) // 256 * 256
     need = L.tg_topk_select_workspace_size(B, T_in, max_n)
-    assert need == a(B * 64) + a(B * 4096 * 4) + a((T_in // 4096 + B + 1) * 8)
+    assert need == a(B * 3 * 4096 * 4) + a((T_in // 4096 + B + 1) * 32)
     assert L.tg_topk_select_workspace_size(B, T_in, 32768) == 0
     assert L.tg_topk_select_workspace_size(B, T_in, 32769) == need
     f = L.tg_topk_select
