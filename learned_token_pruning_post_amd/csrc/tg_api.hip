@@ -136,7 +136,7 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t
   TG_CHECK(need == 0 || ((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);
   tg_status a = check_arch();
   if (a != TG_OK) return a;
-  return launched(tg::launch_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, max_n, kept_idx,
+  return launched(tg::launch_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, max_n, kept_idx,
                                          d_status, ws, stream));
 }
 

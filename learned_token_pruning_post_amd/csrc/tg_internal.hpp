@@ -26,7 +26,7 @@ hipError_t ensure_dynamic_lds(int bytes) {
 // Workspace of launch_topk_select (0 when max_n fits one workgroup's LDS).
 size_t topk_select_workspace_bytes(int B, int64_t T_in, int max_n);
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
-                              const int32_t* cu_kept, int B, int64_t T_in, int max_n, int32_t* kept,
+                              const int32_t* cu_kept, int B, int max_n, int32_t* kept,
                               int32_t* status, void* ws, hipStream_t stream);
 
 hipError_t launch_compact(const void* h, const int32_t* pos, const float* s, const int32_t* kept,

@@ -847,9 +847,8 @@ size_t topk_select_workspace_bytes(int B, int64_t T_in, int max_n) {
 }
 
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
-                              const int32_t* cu_kept, int B, int64_t T_in, int max_n, int32_t* kept,
+                              const int32_t* cu_kept, int B, int max_n, int32_t* kept,
                               int32_t* status, void* ws, hipStream_t stream) {
-  (void)T_in;
   if (B <= 0) return hipSuccess;
   if (max_n <= SEL_LDS_MAX) {
     constexpr size_t lds = (size_t)SEL_LDS_MAX * sizeof(uint32_t);
