@@ -308,6 +308,47 @@ def test_step_replays_from_a_hip_graph():
             assert torch.equal(a, r), "replay %d: %s" % (i, name)
 
 
+def test_chunked_select_replays_from_a_hip_graph():
+    """The chunked selection (max_n above 32768: six kernels, histograms
+    cleared by a kernel, no memset) captured once into a HIP graph and replayed
+    on new scores, with eager work between replays: every replay equals the
+    oracle on the scores of that replay, bit for bit."""
+    dev = "cuda"
+    N, K = [50000, 20000, 33000], [3000, 19000, 4096]
+    T_in, T = sum(N), sum(K)
+    cu_in = np.concatenate([[0], np.cumsum(N)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
+    rng = np.random.default_rng(58)
+    mask = np.zeros(T_in, np.uint8)
+    mask[rng.choice(T_in, 600, replace=False)] = 1
+    s_dev = torch.from_numpy(scores_with_ties(58, T_in, 41)).to(dev)
+    m_dev = torch.from_numpy(mask).to(dev)
+    ci, ck = torch.from_numpy(cu_in).to(dev), torch.from_numpy(cu_k).to(dev)
+    max_n = max(N)
+    need = tg.lib().tg_topk_select_workspace_size(len(N), T_in, max_n)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    kept = torch.empty(T, dtype=torch.int32, device=dev)
+    status = torch.empty(len(N), dtype=torch.int32, device=dev)
+    tg.topk_select(s_dev, m_dev, ci, ck, T, max_n, kept=kept, status=status, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tg.topk_select(s_dev, m_dev, ci, ck, T, max_n, kept=kept, status=status, ws=ws)
+    for i in range(3):
+        s_new = scores_with_ties(59 + i, T_in, 7 + 30 * i)
+        s_dev.copy_(torch.from_numpy(s_new))
+        kept.fill_(-7)
+        junk = torch.randn(1 << 20, device=dev)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(junk.abs().sum()) > 0
+        ref, flags = O.topk_select(s_new, mask, cu_in, cu_k)
+        assert np.array_equal(status.cpu().numpy(), flags.astype(np.int32)), "replay %d" % i
+        assert np.array_equal(kept.cpu().numpy(), ref.astype(np.int32)), "replay %d" % i
+
+
 def test_folded_norm_weights_not_ones():
     """Fold non-unit norm weights into the projections and run the fused layer:
     every stage matches the oracle evaluated with the unfolded weights."""
