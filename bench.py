@@ -264,7 +264,7 @@ def main():
             step(i)
         ev.record(3, stream)
         torch.cuda.synchronize()
-        ms_instr = ev.ms(2, 3) / args.steps
+        ms_instr_total = ev.ms(2, 3) / args.steps
         attn_bias = attention_bias_ratio(tg, torch, w, dw, gp, stream)
     # The same step captured once into a HIP graph and replayed `steps` times
     # (reported beside `value`; the library makes no allocation, copy or
@@ -310,10 +310,23 @@ def main():
         kbytes["rmsnorm_attn"] = 2.0 * T * D * elt
         kbytes["rmsnorm_ffn"] = 2.0 * T * D * elt
     kern = {}
+    gaps = None
     if use_ev:
         acc = {}
+        spans, in_step_gaps = [], []
+        last = per_step - 1  # the last layer's closing event
         for i in range(args.steps):
             base = EV0 + i * per_step
+            # first event -> last event of the step; the windows no kernel entry
+            # covers are host-side hops (compaction end -> first layer, layer ->
+            # layer), where the GPU waits for Python to marshal the next call
+            span = ev.ms(base, base + last)
+            covered = ev.ms(base, base + 3)
+            for l in range(L):
+                lb = base + 4 + l * (tg.LAYER_STAGES + 1)
+                covered += ev.ms(lb, lb + tg.LAYER_STAGES)
+            spans.append(span)
+            in_step_gaps.append(span - covered)
             for name, a in (("gate_score", 0), ("topk_select", 1), ("compact", 2)):
                 acc.setdefault(name, []).append(ev.ms(base + a, base + a + 1))
             for l in range(L):
@@ -342,6 +355,12 @@ def main():
                 e["gbs"] = round(gbs, 1)
                 e["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
             kern[name] = e
+        ms_instr = float(np.mean(spans))
+        gaps = {"in_step_ms_per_step": round(float(np.mean(in_step_gaps)), 4),
+                "between_steps_ms_per_step": round(ms_instr_total - ms_instr, 4),
+                "note": "GPU idle while the host marshals the next call: compaction end to the "
+                        "first layer and between layers inside a step, and from one step's last "
+                        "kernel to the next step's first; in no kernel entry"}
     ev.close()
 
     out = {
@@ -396,6 +415,7 @@ def main():
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": de["frac_hbm"],
                                "traffic": traffic, "work_per_launch": kbytes[dom]}
         out["kernels"] = kern
+        out["host_gaps"] = gaps
     if want_cpu:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         from learned_token_pruning_post_amd.workloads import gate_inputs, layer_weights

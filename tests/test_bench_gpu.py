@@ -1,6 +1,7 @@
 """bench.py end to end on a small workload: one JSON line with the fields the
-benchmark contract names, per-kernel durations that add up to the
-instrumented step, and a HIP-graph replay of the same step."""
+benchmark contract names, per-kernel durations that with the host-side hops
+between calls add up to the instrumented step, and a HIP-graph replay of the
+same step."""
 import json
 import os
 import subprocess
@@ -28,11 +29,16 @@ def test_bench_json_line_small_workload():
     rf = d["roofline"]
     assert rf["bound"] in ("mfma", "hbm", "alu") and 0 < rf["frac"] < 1
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
-    # per-kernel durations come from the instrumented pass and must add up to it
+    # the per-kernel entries and the host-side hops between calls tile each
+    # instrumented step exactly (first event to last event); the hops are GPU idle
+    # time that depends on the host, so they are reported apart and not bounded here
     kern = d["kernels"]
     total = sum(k["ms_per_step"] for k in kern.values())
     assert all(k["avg_us"] > 0 for k in kern.values())
-    assert abs(total - d["ms_per_step_with_kernel_events"]) < 0.1 * d["ms_per_step_with_kernel_events"]
+    gaps = d["host_gaps"]
+    span = d["ms_per_step_with_kernel_events"]
+    assert gaps["in_step_ms_per_step"] >= -1e-3 and gaps["between_steps_ms_per_step"] >= -1e-3
+    assert abs(total + gaps["in_step_ms_per_step"] - span) < 0.01 * span + 1e-3
     # the graph replay of the same step takes about as long as the eager step
     g = d["ms_per_step_hip_graph"]
     assert g is not None and 0.5 * d["ms_per_step"] < g < 1.5 * d["ms_per_step"]

@@ -174,7 +174,8 @@ def test_stages_ragged_gqa4_fp32_d128():
 def test_layer_stack_reuses_rope_table():
     """Layer 1 of a stack runs on the RoPE table layer 0 left in the workspace
     (TG_LAYER_ROPE_READY): its outputs equal a run that rebuilds the table, and
-    its post-RoPE K cache matches the oracle."""
+    its post-RoPE K cache and its output x match the oracle layer fed layer 0's
+    GPU output."""
     w = workload("qwen8k", layers=2)
     dw = DeviceWorkload(w, n_layers=2, keep_host=True)
     gp = GatedPrefill(dw)
@@ -194,16 +195,20 @@ def test_layer_stack_reuses_rope_table():
         assert torch.equal(a, b), name
     W = layer_dict(dw.host_layers[1])
     rows = sample_rows(dw.host_gate.cu_kept, 256, 1)
-    _, q_r, k_r, v_r = O.qkv_rope(f64(x_in), gp.pos_c.cpu().numpy(), W, w.dims, rows=rows)
-    e = assert_close(f64(reuse[1])[rows], k_r[rows], w.dims.dtype, "layer-1 k cache")
-    say("  layer 1 on the reused RoPE table: bit-identical to a rebuilt one; k err %.3g" % e)
+    ref = O.upper_layer(f64(x_in), gp.pos_c.cpu().numpy(), f64(gp.s_c), W, w.dims,
+                        dw.host_gate.cu_kept, rows=rows)
+    e = assert_close(f64(reuse[1])[rows], ref["k"][rows], w.dims.dtype, "layer-1 k cache")
+    ex = assert_close(f64(reuse[0])[rows], ref["x2"][rows], w.dims.dtype, "layer-1 x out")
+    say("  layer 1 on the reused RoPE table: bit-identical to a rebuilt one; k err %.3g, "
+        "x out err %.3g" % (e, ex))
 
 
 def test_layer_stack_folded_norms_reuses_input_sums():
     """With folded norms, layer 1 reads its input's row sums of squares from the
     workspace, as written by layer 0's down projection (TG_LAYER_INPUT_SSQ): its
     outputs equal a run on a fresh workspace, where a kernel of its own computes
-    them, bit for bit; x out and the k cache match the oracle."""
+    them, bit for bit; x out and the k cache match the oracle layer fed layer
+    0's GPU output."""
     w = workload("qwen8k", layers=2)
     dw = DeviceWorkload(w, n_layers=2, keep_host=True, norms_folded=True)
     gp = GatedPrefill(dw)
@@ -223,9 +228,12 @@ def test_layer_stack_folded_norms_reuses_input_sums():
         assert torch.equal(a, b), name
     W = layer_dict(dw.host_layers[1])
     rows = sample_rows(dw.host_gate.cu_kept, 256, 1)
-    _, q_r, k_r, v_r = O.qkv_rope(f64(x_in), gp.pos_c.cpu().numpy(), W, w.dims, rows=rows)
-    e = assert_close(f64(reuse[1])[rows], k_r[rows], w.dims.dtype, "layer-1 k cache")
-    say("  layer 1 on its input sums from layer 0: bit-identical to a fresh run; k err %.3g" % e)
+    ref = O.upper_layer(f64(x_in), gp.pos_c.cpu().numpy(), f64(gp.s_c), W, w.dims,
+                        dw.host_gate.cu_kept, rows=rows)
+    e = assert_close(f64(reuse[1])[rows], ref["k"][rows], w.dims.dtype, "layer-1 k cache")
+    ex = assert_close(f64(reuse[0])[rows], ref["x2"][rows], w.dims.dtype, "layer-1 x out")
+    say("  layer 1 on its input sums from layer 0: bit-identical to a fresh run; k err %.3g, "
+        "x out err %.3g" % (e, ex))
 
 
 def test_native_layer_stack_equals_layer_loop():
