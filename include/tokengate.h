@@ -14,10 +14,13 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Ownership: the caller owns every buffer. The library never allocates or
- *    frees device memory and keeps no mutable global state; scratch memory is
- *    passed in as (ws, ws_bytes), sized by the matching *_workspace_size().
- *    Calls on different streams with different workspaces may run
- *    concurrently.
+ *    frees device memory; scratch memory is passed in as (ws, ws_bytes),
+ *    sized by the matching *_workspace_size(). Calls on different streams
+ *    with different workspaces may run concurrently. Host-side state is
+ *    limited to per-device caches that are idempotent and thread-safe (the
+ *    gfx950 check, kernels' raised LDS limits, the address of the scratch of
+ *    tg_topk_select_noalloc); the one device-side state is that scratch,
+ *    which the library defines as a static device array.
  *  - Pointers: all tensor pointers are DEVICE pointers unless stated. Layouts
  *    are dense row-major with the last dimension contiguous.
  *  - Execution: every call validates its arguments on the host, enqueues its
@@ -120,6 +123,25 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask,
                          int B, int64_t T_in, int64_t T, int max_n,
                          int32_t* kept_idx, int32_t* d_status,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same selection for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no ws argument. Where tg_topk_select needs a workspace
+ * (max_n > 32768) this call uses a scratch array of
+ * TG_SELECT_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one per GPU for the life of the process, and calls no allocating routine.
+ * Arguments, outputs and results are those of tg_topk_select. Errors: as
+ * tg_topk_select, plus TG_ERR_WORKSPACE when
+ * tg_topk_select_workspace_size(B, T_in, max_n) exceeds the scratch size
+ * (nothing is enqueued then). Every call on a GPU shares that GPU's scratch,
+ * which keeps the last call's contents (each call clears what it must start
+ * from): calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller. */
+#define TG_SELECT_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+tg_status tg_topk_select_noalloc(const float* s, const uint8_t* keep_mask,
+                                 const int32_t* d_cu_in, const int32_t* d_cu_kept,
+                                 int B, int64_t T_in, int64_t T, int max_n,
+                                 int32_t* kept_idx, int32_t* d_status, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
  * Compaction — [TC] early token filtering: only the selected tokens go on

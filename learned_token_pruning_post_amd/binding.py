@@ -28,7 +28,7 @@ DEV_LEN_GT_MAX_N = 8
 ABI_FUNCTIONS = (
     "tg_status_string", "tg_abi_version",
     "tg_gate_score_workspace_size", "tg_gate_score",
-    "tg_topk_select_workspace_size", "tg_topk_select",
+    "tg_topk_select_workspace_size", "tg_topk_select", "tg_topk_select_noalloc",
     "tg_compact",
     "tg_gated_attn_workspace_size", "tg_gated_attn_fwd",
     "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
     L.tg_topk_select_workspace_size.restype = sz
     L.tg_topk_select.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp, sz, vp]
     L.tg_topk_select.restype = i32
+    L.tg_topk_select_noalloc.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp]
+    L.tg_topk_select_noalloc.restype = i32
     L.tg_compact.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp, vp, vp]
     L.tg_compact.restype = i32
     L.tg_gated_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -189,6 +191,19 @@ def topk_select(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, kept=None, sta
                                 max_n, _p(kept), _p(status), _p(ws) if need else None,
                                 ws.numel() if need else 0, _stream()),
            "tg_topk_select")
+    return kept, status
+
+
+SELECT_NOALLOC_SCRATCH_BYTES = 4 << 20  # TG_SELECT_NOALLOC_SCRATCH_BYTES
+
+
+def topk_select_noalloc(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, kept, status):
+    """tg_topk_select_noalloc: the selection on the library's own device scratch
+    (no workspace argument); the caller passes the outputs."""
+    B = cu_in.numel() - 1
+    _check(lib().tg_topk_select_noalloc(_p(s), _p(keep_mask), _p(cu_in), _p(cu_kept), B, s.numel(),
+                                        T, max_n, _p(kept), _p(status), _stream()),
+           "tg_topk_select_noalloc")
     return kept, status
 
 

@@ -66,6 +66,30 @@ tg_status layer_dims_supported(const tg_layer_dims* dm) {
 
 }  // namespace
 
+// Scratch of tg_topk_select_noalloc. Every GPU the library runs on holds its
+// own copy at its own address until the process ends; host code reaches it
+// only through the address hipGetSymbolAddress gives for the current device
+// (the array's name on the host is a stand-in, not a device address). Calls
+// that overlap on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[TG_SELECT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[64];  // device address of `scratch`, per device (idempotent cache)
+
+tg_status noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_LAUNCH;
+  if (dev < 0 || dev >= 64) return TG_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TG_ERR_LAUNCH;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return TG_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* tg_status_string(tg_status s) {
@@ -138,6 +162,23 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t
   if (a != TG_OK) return a;
   return launched(tg::launch_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, max_n, kept_idx,
                                          d_status, ws, stream));
+}
+
+tg_status tg_topk_select_noalloc(const float* s, const uint8_t* keep_mask, const int32_t* d_cu_in,
+                                 const int32_t* d_cu_kept, int B, int64_t T_in, int64_t T, int max_n,
+                                 int32_t* kept_idx, int32_t* d_status, hipStream_t stream) {
+  TG_CHECK(B >= 0 && T_in >= 0 && T >= 0 && max_n >= 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(T_in <= INT_MAX && T <= INT_MAX, TG_ERR_INVALID_ARG);
+  TG_CHECK(((int64_t)max_n + 4095) / 4096 * B <= INT_MAX, TG_ERR_INVALID_ARG);
+  const size_t need = B > 0 ? tg::topk_select_workspace_bytes(B, T_in, max_n) : 0;
+  TG_CHECK(need <= TG_SELECT_NOALLOC_SCRATCH_BYTES, TG_ERR_WORKSPACE);
+  void* ws = nullptr;
+  if (need > 0) {
+    const tg_status st = noalloc_scratch(&ws);
+    if (st != TG_OK) return st;
+  }
+  return tg_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx, d_status,
+                        ws, need, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -71,6 +71,20 @@ def test_topk_select_argument_errors(L):
     assert L.tg_topk_select_workspace_size(8, 1 << 17, 1 << 14) == 0
 
 
+def test_topk_select_noalloc_argument_errors(L):
+    """The allocation-free selection validates like tg_topk_select and refuses,
+    before touching a device, a call whose workspace would exceed its scratch."""
+    f = L.tg_topk_select_noalloc
+    assert f(FAKE, None, FAKE, FAKE, -1, 10, 5, 10, FAKE, None, None) == INVALID
+    assert f(FAKE, None, FAKE, FAKE, 1, 10, 11, 10, FAKE, None, None) == INVALID  # T > T_in
+    assert f(None, None, None, None, 0, 0, 0, 0, None, None, None) == OK  # B = 0
+    cap = tg.SELECT_NOALLOC_SCRATCH_BYTES
+    B = 200  # three 16 KB histograms per sequence: 9.6 MB > 4 MiB
+    assert L.tg_topk_select_workspace_size(B, B * 40000, 40000) > cap
+    assert f(FAKE, None, FAKE, FAKE, B, B * 40000, B * 100, 40000, FAKE, None, None) == WS
+    assert L.tg_topk_select_workspace_size(8, 8 * 40000, 40000) <= cap
+
+
 def test_topk_select_long_path_workspace(L):
     """Above 32768 tokens per sequence the selection needs scratch: three
     4096-bin histograms per sequence and a 32-byte record per 4096-token
