@@ -32,6 +32,10 @@
  *  - Dtypes: activations and weights are TG_BF16 (bf16 storage, fp32
  *    accumulation) or TG_F32. Scores, t, g, s_c and lse are always fp32;
  *    indices, positions and offsets are int32.
+ *  - Size limit (bf16): the kernels address every operand through 32-bit
+ *    buffer ranges, so each activation or weight matrix a bf16 call reads
+ *    (and one sequence's K or V) must be smaller than 4 GiB; larger calls
+ *    return TG_ERR_UNSUPPORTED before anything is enqueued.
  *  - Batches are packed ("varlen"): sequence b owns rows
  *    [cu_in[b], cu_in[b+1]) of the input and rows [cu_kept[b], cu_kept[b+1])
  *    of every kept-token tensor; K_b = cu_kept[b+1] - cu_kept[b].

@@ -35,6 +35,12 @@ tg_status check_arch() {
 
 inline tg_status launched(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH; }
 
+// The bf16 kernels address each operand through a buffer resource whose range
+// is a 32-bit byte count: every such operand must stay below 4 GiB.
+inline bool fits32(int64_t rows, int64_t row_elems, int64_t elt = 2) {
+  return rows >= 0 && row_elems >= 0 && rows * row_elems * elt < ((int64_t)1 << 32);
+}
+
 #define TG_CHECK(cond, code) \
   do {                       \
     if (!(cond)) return (code); \
@@ -121,6 +127,7 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1, const void* 
   if (T_in == 0) return TG_OK;
   TG_CHECK(h && W1 && b1 && w2 && b2 && s_out, TG_ERR_INVALID_ARG);
   if (dtype == TG_BF16) TG_CHECK(D % 64 == 0 && H1 % 4 == 0, TG_ERR_UNSUPPORTED);
+  if (dtype == TG_BF16) TG_CHECK(fits32(T_in, D) && fits32(H1, D), TG_ERR_UNSUPPORTED);
   const size_t need = tg_gate_score_workspace_size(T_in, D, H1, dtype);
   TG_CHECK(ws_bytes >= need && (need == 0 || ws), TG_ERR_WORKSPACE);
   tg_status a = check_arch();
@@ -218,6 +225,7 @@ static tg_status attn_args(int B, int max_k, int Hq, int Hkv, int d, tg_dtype dt
   if (dtype == TG_BF16) {
     const int G = Hq / Hkv;
     TG_CHECK(G == 1 || G == 2 || G == 4, TG_ERR_UNSUPPORTED);
+    TG_CHECK(fits32(max_k, (int64_t)Hkv * d), TG_ERR_UNSUPPORTED);  // one sequence's K or V
   }
   return TG_OK;
 }
@@ -300,6 +308,12 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   if (st != TG_OK) return st;
   if (T == 0 || B == 0) return TG_OK;
   TG_CHECK(max_k > 0, TG_ERR_INVALID_ARG);
+  if (dm->dtype == TG_BF16) {  // activations and weights of every GEMM, one sequence's K/V
+    const int64_t qd = (int64_t)dm->Hq * dm->d, kvd = (int64_t)dm->Hkv * dm->d;
+    TG_CHECK(fits32(T, dm->D) && fits32(T, qd) && fits32(T, dm->I) && fits32(qd, dm->D) &&
+                 fits32(dm->I, dm->D) && fits32(max_k, kvd),
+             TG_ERR_UNSUPPORTED);
+  }
   const bool fused = (dm->flags & TG_LAYER_NORMS_FOLDED) != 0;
   TG_CHECK(w->wq && w->wk && w->wv && w->wo && w->wg && w->wu && w->wd && w->t && w->g,
            TG_ERR_INVALID_ARG);

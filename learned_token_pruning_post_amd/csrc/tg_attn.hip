@@ -444,7 +444,7 @@ static hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, 
   const int n_qt = (max_k + BQ - 1) / BQ;
   // one query-tile pair per workgroup; single tiles while they fit one
   // workgroup per CU
-  const int single = (long)n_qt * Hkv * B <= 256;
+  const int single = (long)n_qt * Hkv * B <= device_cu_count();
   const long blocks = (long)(single ? n_qt : (n_qt + 1) / 2) * Hkv * B;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((attn_bf16_kernel<G, HD>), dim3((unsigned)blocks), dim3(512), lds, stream,

@@ -23,6 +23,24 @@ hipError_t ensure_dynamic_lds(int bytes) {
   return e;
 }
 
+// Compute units of the current device, cached per device (idempotent: a race
+// only repeats the query); 256 if the query fails.
+inline int device_cu_count() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  if (slot) cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Workspace of launch_topk_select (0 when max_n fits one workgroup's LDS).
 size_t topk_select_workspace_bytes(int B, int64_t T_in, int max_n);
 hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,

@@ -61,6 +61,21 @@ def test_gate_score_argument_errors(L):
     assert f(None, 0, 64, 32, None, None, None, None, 1, None, None, 0, None) == OK  # empty
 
 
+def test_bf16_operands_of_4_gib_are_refused(L):
+    """bf16 operands are addressed through 32-bit buffer ranges: a matrix of
+    4 GiB or more is refused up front instead of wrapping silently."""
+    f = L.tg_gate_score
+    assert f(FAKE, 1 << 20, 2048, 256, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, 0, None) == UNSUP
+    a = L.tg_gated_attn_fwd
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1 << 21, 16, 8, 128, 1, FAKE, None, None, 0,
+             None) == UNSUP
+    dims = tg.LayerDims(2048, 16, 8, 128, 6144, 1e6, 1e-6, 1, 0)
+    w = tg.LayerWeights(*([FAKE.value] * 11))
+    T = (1 << 32) // (2 * 6144) + 1  # the SwiGLU activation [T, I] reaches 4 GiB
+    assert L.tg_upper_layer_fwd(ctypes.byref(w), ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                T, 4096, FAKE, FAKE, FAKE, 1 << 62, None) == UNSUP
+
+
 def test_topk_select_argument_errors(L):
     f = L.tg_topk_select
     assert f(FAKE, None, FAKE, FAKE, -1, 10, 5, 10, FAKE, None, None, 0, None) == INVALID
