@@ -53,6 +53,8 @@ def parse():
                     help="skip the HIP-graph replay pass (ms_per_step_hip_graph)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only the whole step (no per-kernel events)")
+    ap.add_argument("--no-memory", action="store_true",
+                    help="skip the peak-memory comparison with the unpruned path")
     return ap.parse_args()
 
 
@@ -93,17 +95,52 @@ class HipEvents:
 
 
 CPU_LAYERS = 5  # upper layers the CPU baseline runs (about 10 s of fp64 work at K=4096)
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}  # atol, rtol of the parity tests
 
 
-def cpu_baseline(w, dw_host_gate, host_layers):
-    """The fp64 oracle timed on the host: scorer + selection + compaction on the
+def gpu_outputs_for_parity(torch, gp, n_layers):
+    """One more pass of the path's stages on the GPU, with the outputs the oracle
+    is compared against copied to the host: scores, selection, status, the
+    compacted rows, positions and scores, x after the first upper layer and
+    after `n_layers` of them."""
+    gp.score()
+    gp.select()
+    gp.compact()
+    torch.cuda.synchronize()
+    g = {"s": gp.s.cpu().numpy(), "kept": gp.kept.cpu().numpy(), "status": gp.status.cpu().numpy(),
+         "x_c": gp.x.clone(), "pos_c": gp.pos_c.cpu().numpy(), "s_c": gp.s_c.cpu().numpy()}
+    for l in range(n_layers):
+        gp.layer(l)
+        if l == 0:
+            torch.cuda.synchronize()
+            g["x_l0"] = gp.x.float().cpu().numpy()
+    torch.cuda.synchronize()
+    g["x_last"] = gp.x.float().cpu().numpy()
+    g["x_c_bits"] = g["x_c"].cpu().view(torch.int16 if g["x_c"].dtype == torch.bfloat16 else torch.int32).numpy()
+    g["x_c"] = g["x_c"].float().cpu().numpy().astype("float64")
+    return g
+
+
+def _excess(got, ref, atol, rtol):
+    import numpy as np
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    return float(err.max()) if err.size else 0.0, float((err - (atol + rtol * np.abs(ref))).max()) if err.size else -1.0
+
+
+def cpu_leg(w, gi, host_layers, g):
+    """The fp64 oracle on the host: times scorer + selection + compaction on the
     whole prompt and the first len(host_layers) upper layers (distinct seeded
-    weights) on all K kept tokens, the mean layer time scaled to the workload's
-    layer count."""
+    weights) on all K kept tokens, the mean layer time scaled to the
+    workload's layer count (the CPU baseline); and, with the GPU's outputs `g`
+    of the same workload, the parity figures: per-stage maxima (each oracle
+    stage fed the GPU's previous-stage output, as in the tests), selection
+    flips between the GPU's fp32 scores and the oracle's fp64 ones, and the
+    drift of x after len(host_layers) layers (reported, not gated)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import oracle as O
-    gi = dw_host_gate
     Ws = [{"wq": L.wq.value, "wk": L.wk.value, "wv": L.wv.value, "wo": L.wo.value,
            "wg": L.wg.value, "wu": L.wu.value, "wd": L.wd.value, "attn_norm": L.attn_norm.value,
            "ffn_norm": L.ffn_norm.value, "t": L.t, "g": L.g} for L in host_layers]
@@ -111,20 +148,23 @@ def cpu_baseline(w, dw_host_gate, host_layers):
     t0 = time.perf_counter()
     s = O.gate_score(gi.h.value, gi.W1.value, gi.b1.value, gi.w2.value, gi.b2.value)
     t1 = time.perf_counter()
-    kept, _ = O.topk_select(s, gi.keep_mask, gi.cu_in, gi.cu_kept)
+    kept_own, _ = O.topk_select(s, gi.keep_mask, gi.cu_in, gi.cu_kept)
     t2 = time.perf_counter()
-    hc, pc, sc = O.compact(gi.h.value, None, s, kept, gi.cu_in, gi.cu_kept)
+    O.compact(gi.h.value, None, s, kept_own, gi.cu_in, gi.cu_kept)
     t3 = time.perf_counter()
-    x = hc
-    for W in Ws:
-        x = O.upper_layer(x, pc, sc, W, w.dims, gi.cu_kept)["x2"]
+    x = g["x_c"]  # the GPU's compacted rows (exact values), so the drift below is the layers' own
+    x_l0 = None
+    for i, W in enumerate(Ws):
+        x = O.upper_layer(x, g["pos_c"], g["s_c"], W, w.dims, gi.cu_kept)["x2"]
+        if i == 0:
+            x_l0 = x
     t4 = time.perf_counter()
     t_est = (t3 - t0) + w.layers * (t4 - t3) / nl
     threads = 0
     for p in threadpool_info():
         if p.get("user_api") == "blas":
             threads = max(threads, int(p.get("num_threads", 0)))
-    return {
+    base = {
         "value": w.T_in / t_est, "unit": "tokens/s",
         "cores": threads or len(os.sched_getaffinity(0)),
         "kind": "oracle",
@@ -134,6 +174,67 @@ def cpu_baseline(w, dw_host_gate, host_layers):
         "host_cores": len(os.sched_getaffinity(0)),
         "seconds_measured": round(t4 - t0, 2),
     }
+    # ---- parity on the benchmarked workload ----
+    atol, rtol = TOL[w.dims.dtype]
+    s_err, s_exc = _excess(g["s"], s, atol, rtol)
+    ref_kept, ref_flags = O.topk_select(g["s"], gi.keep_mask, gi.cu_in, gi.cu_kept)
+    sel_exact = bool(np.array_equal(g["kept"], ref_kept.astype(np.int32)) and
+                     np.array_equal(g["status"], ref_flags.astype(np.int32)))
+    flips = int(np.setdiff1d(g["kept"], kept_own).size)
+    hc, pc, sc = O.compact(gi.h.value, None, g["s"], g["kept"].astype(np.int64), gi.cu_in, gi.cu_kept)
+    hbits = (np.ascontiguousarray(gi.h.bits[g["kept"]]).view(np.int16) if gi.h.bits is not None
+             else np.ascontiguousarray(hc, dtype=np.float32).view(np.int32))
+    comp_exact = bool(np.array_equal(g["x_c_bits"], hbits) and np.array_equal(g["pos_c"], pc) and
+                      np.array_equal(g["s_c"].view(np.int32), sc.astype(np.float32).view(np.int32)))
+    l0_err, l0_exc = _excess(g["x_l0"], x_l0, atol, rtol)
+    dr_err, dr_exc = _excess(g["x_last"], x, atol, rtol)
+    parity = {
+        "tolerance": {"atol": atol, "rtol": rtol},
+        "scores_max_abs_err": s_err, "scores_within_tol": s_exc <= 0,
+        "selection_bit_exact": sel_exact, "compaction_bit_exact": comp_exact,
+        "layer0_out_max_abs_err": l0_err, "layer0_out_within_tol": l0_exc <= 0,
+        "selection_flips_vs_fp64_scores": flips,
+        "selection_flips_note": "kept tokens chosen from the GPU's fp32 scores that the oracle's fp64 "
+                                "scores would not keep (of %d); reported, not gated" % w.T,
+        "drift_layers": nl,
+        "drift_max_abs_err": dr_err, "drift_max_excess_over_tol": dr_exc,
+        "drift_note": "x after %d stacked layers, GPU chain vs oracle chain from the same compacted "
+                      "rows (errors compound; reported, not gated)" % nl,
+    }
+    return base, parity
+
+
+def memory_vs_unpruned(torch, tg, w):
+    """Peak device memory of one pass of the path with one upper layer at the
+    workload's budgets and the same path with every token kept (K = N, the
+    unpruned layer), each measured from an empty allocator; and the K/V cache
+    of 27 upper layers at both budgets from the layer shapes."""
+    from learned_token_pruning_post_amd.pipeline import DeviceWorkload, GatedPrefill
+    from learned_token_pruning_post_amd.workloads import Workload
+    res = {}
+    for name, K in (("pruned", w.K), ("unpruned", w.N)):
+        wl = Workload(w.name, w.cfg_id, w.N, tuple(K), w.F, w.dims, 1, w.salient)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        dw = DeviceWorkload(wl, n_layers=1, norms_folded=True)
+        gp = GatedPrefill(dw)
+        gp.run()
+        torch.cuda.synchronize()
+        res[name] = (torch.cuda.max_memory_allocated() - base) / 1e9
+        del gp, dw
+    torch.cuda.empty_cache()
+    dm = w.dims
+    elt = 2 if dm.dtype == "bf16" else 4
+    kv = lambda toks: 27 * 2 * toks * dm.Hkv * dm.d * elt / 1e9
+    return {"peak_gb_one_layer_pruned": round(res["pruned"], 3),
+            "peak_gb_one_layer_unpruned": round(res["unpruned"], 3),
+            "peak_ratio_unpruned_over_pruned": round(res["unpruned"] / res["pruned"], 2),
+            "kv_cache_gb_27_layers_pruned": round(kv(w.T), 3),
+            "kv_cache_gb_27_layers_unpruned": round(kv(w.T_in), 3),
+            "note": "same N, scorer + select + compact + one upper layer; unpruned = every token kept "
+                    "(K = N); K/V of 27 upper layers from the shapes"}
 
 
 def attention_bias_ratio(tg, torch, w, dw, gp, stream, reps=20):
@@ -416,13 +517,19 @@ def main():
                                "traffic": traffic, "work_per_launch": kbytes[dom]}
         out["kernels"] = kern
         out["host_gaps"] = gaps
+    n_cpu_layers = min(CPU_LAYERS, w.layers)
+    g_out = gpu_outputs_for_parity(torch, gp, n_cpu_layers) if want_cpu else None
+    del gp, dw
+    torch.cuda.empty_cache()
+    if not args.no_memory:
+        print("[bench] peak memory against the unpruned path (K = N, one layer)", file=sys.stderr, flush=True)
+        out["memory"] = memory_vs_unpruned(torch, tg, w)
     if want_cpu:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle on a bounded sample; parity on this workload",
+              file=sys.stderr, flush=True)
         from learned_token_pruning_post_amd.workloads import gate_inputs, layer_weights
-        del gp, dw
-        torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(
-            w, gate_inputs(w), [layer_weights(w, l) for l in range(min(CPU_LAYERS, w.layers))])
+        out["cpu_baseline"], out["parity"] = cpu_leg(
+            w, gate_inputs(w), [layer_weights(w, l) for l in range(n_cpu_layers)], g_out)
     print(json.dumps(out), flush=True)
 
 

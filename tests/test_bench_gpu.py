@@ -15,8 +15,8 @@ pytestmark = pytest.mark.gpu
 
 def test_bench_json_line_small_workload():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "qwen8k", "--steps", "3",
-           "--warmup", "1", "--no-cpu-baseline"]
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=110)
+           "--warmup", "1"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=170)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.strip().splitlines() if l.startswith("{")]
     assert len(lines) == 1, r.stdout
@@ -39,6 +39,16 @@ def test_bench_json_line_small_workload():
     span = d["ms_per_step_with_kernel_events"]
     assert gaps["in_step_ms_per_step"] >= -1e-3 and gaps["between_steps_ms_per_step"] >= -1e-3
     assert abs(total + gaps["in_step_ms_per_step"] - span) < 0.01 * span + 1e-3
+    # the oracle leg: CPU baseline and parity of this very workload
+    cb, par = d["cpu_baseline"], d["parity"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert par["selection_bit_exact"] and par["compaction_bit_exact"]
+    assert par["scores_within_tol"] and par["layer0_out_within_tol"]
+    assert 0 <= par["selection_flips_vs_fp64_scores"] <= 1024
+    # peak memory against the unpruned path (K = N) at the same N
+    mem = d["memory"]
+    assert mem["peak_gb_one_layer_unpruned"] > mem["peak_gb_one_layer_pruned"] > 0
+    assert mem["kv_cache_gb_27_layers_unpruned"] == pytest.approx(8 * mem["kv_cache_gb_27_layers_pruned"], rel=1e-2)
     # the graph replay of the same step takes about as long as the eager step
     g = d["ms_per_step_hip_graph"]
     assert g is not None and 0.5 * d["ms_per_step"] < g < 1.5 * d["ms_per_step"]
