@@ -104,8 +104,7 @@ def gpu_outputs_for_parity(torch, gp, n_layers):
     compacted rows, positions and scores, x after the first upper layer and
     after `n_layers` of them."""
     gp.score()
-    gp.select()
-    gp.compact()
+    gp.select_compact()
     torch.cuda.synchronize()
     g = {"s": gp.s.cpu().numpy(), "kept": gp.kept.cpu().numpy(), "status": gp.status.cpu().numpy(),
          "x_c": gp.x.clone(), "pos_c": gp.pos_c.cpu().numpy(), "s_c": gp.s_c.cpu().numpy()}
@@ -308,7 +307,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.reset_peak_memory_stats()
 
-    per_step = 4 + L * (tg.LAYER_STAGES + 1)
+    per_step = 3 + L * (tg.LAYER_STAGES + 1)
     use_ev = not args.no_kernel_events
     EV0 = 6  # events 0-1: timed region, 2-3: per-kernel pass, 4-5: graph replays
     ev = HipEvents(EV0 + (per_step * args.steps if use_ev else 0))
@@ -321,14 +320,12 @@ def main():
         ev.record(base + 0, stream)
         gp.score()
         ev.record(base + 1, stream)
-        gp.select()
+        gp.select_compact()
         ev.record(base + 2, stream)
-        gp.compact()
-        ev.record(base + 3, stream)
         for l in range(L):
             tg.upper_layer_fwd(dw.layers[l], dw.dims, gp.x, gp.pos_c, gp.s_c, dw.cu_kept, w.max_k,
                                x_out=gp.x, kcache=gp.kcache[l], vcache=gp.vcache[l], ws=gp.ws,
-                               events=ev.sub(base + 4 + l * (tg.LAYER_STAGES + 1), tg.LAYER_STAGES + 1),
+                               events=ev.sub(base + 3 + l * (tg.LAYER_STAGES + 1), tg.LAYER_STAGES + 1),
                                rope_ready=l > 0, norms_folded=dw.norms_folded,
                                input_ssq=dw.norms_folded and l > 0)
 
@@ -403,8 +400,9 @@ def main():
     }
     kbytes = {
         "gate_score": w.T_in * D * elt + 4.0 * w.T_in + H1 * D * elt,
-        "topk_select": 5.0 * w.T_in + 4.0 * T,
-        "compact": 4.0 * T + 2.0 * T * D * elt + 4.0 * T + 8.0 * T,
+        # selection (scores, mask, kept indices out) + compaction (rows in and
+        # out, positions and scores out; the kept indices are not read back)
+        "select_compact": 5.0 * w.T_in + 4.0 * T + 4.0 * T + 2.0 * T * D * elt + 4.0 * T + 8.0 * T,
         "rope_table": 4.0 * T + 4.0 * T * d,
     }
     if not dw.norms_folded:  # fused: stage 1 is x_in's sums of squares (first layer), stage 5 empty
@@ -422,16 +420,16 @@ def main():
             # covers are host-side hops (compaction end -> first layer, layer ->
             # layer), where the GPU waits for Python to marshal the next call
             span = ev.ms(base, base + last)
-            covered = ev.ms(base, base + 3)
+            covered = ev.ms(base, base + 2)
             for l in range(L):
-                lb = base + 4 + l * (tg.LAYER_STAGES + 1)
+                lb = base + 3 + l * (tg.LAYER_STAGES + 1)
                 covered += ev.ms(lb, lb + tg.LAYER_STAGES)
             spans.append(span)
             in_step_gaps.append(span - covered)
-            for name, a in (("gate_score", 0), ("topk_select", 1), ("compact", 2)):
+            for name, a in (("gate_score", 0), ("select_compact", 1)):
                 acc.setdefault(name, []).append(ev.ms(base + a, base + a + 1))
             for l in range(L):
-                lb = base + 4 + l * (tg.LAYER_STAGES + 1)
+                lb = base + 3 + l * (tg.LAYER_STAGES + 1)
                 for j, name in enumerate(tg.LAYER_STAGE_NAMES):
                     # stages that launch nothing in this layer (the RoPE table and,
                     # with fused norms, the sums of squares after the first layer;
@@ -498,8 +496,8 @@ def main():
         out["attn_tflops"] = a["tflops"]
         out["attn_frac_mfma_peak"] = a["frac_mfma_peak"]
         out["attn_bias_vs_g0"] = attn_bias
-        sc_us = kern["topk_select"]["avg_us"] + kern["compact"]["avg_us"]
-        sc_bytes = kbytes["topk_select"] + kbytes["compact"]
+        sc_us = kern["select_compact"]["avg_us"]
+        sc_bytes = kbytes["select_compact"]
         out["select_compact"] = {"us": round(sc_us, 2), "bytes": sc_bytes,
                                  "gbs": round(sc_bytes / (sc_us * 1e-6) / 1e9, 1),
                                  "frac_hbm": round(sc_bytes / (sc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}

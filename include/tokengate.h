@@ -105,21 +105,23 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1,
  *  keep_mask [T_in]   uint8, 1 = unprunable; NULL = nothing forced
  *  d_cu_in   [B+1]    int32 device, prefix sums of N_b (d_cu_in[0] = 0, d_cu_in[B] = T_in)
  *  d_cu_kept [B+1]    int32 device, prefix sums of K_b (d_cu_kept[B] = T)
- *  max_n              an upper bound of every N_b. Up to 32768 one workgroup
- *                     per sequence holds its keys in LDS (no workspace); above,
- *                     every sequence is searched by workgroups of 4096 tokens
- *                     in a chain of short kernels, with a workspace of
- *                     tg_topk_select_workspace_size bytes (256-byte aligned).
- *                     A sequence longer than max_n gets TG_DEV_LEN_GT_MAX_N
- *                     and -1 slots.
+ *  max_n              an upper bound of every N_b, at most 1048576 (else
+ *                     TG_ERR_UNSUPPORTED). A sequence longer than max_n gets
+ *                     TG_DEV_LEN_GT_MAX_N and -1 slots.
  *  kept_idx  [T]      int32 out: GLOBAL row indices into s/h, ascending inside
  *                     each sequence, at that sequence's cu_kept offsets
  *  d_status  [B]      int32 device out, TG_DEV_* flags of each sequence
  *                     (overwritten, 0 when fine); may be NULL
- *  ws, ws_bytes       scratch for max_n > 32768 (three 4096-bin histograms
- *                     per sequence, a 32-byte record per 4096-token chunk:
- *                     about B * 48 KB + T_in / 128 bytes); NULL / 0 otherwise.
- *                     Too small: TG_ERR_WORKSPACE; misaligned: TG_ERR_INVALID_ARG.
+ *  ws, ws_bytes       scratch of tg_topk_select_workspace_size(B, T_in, max_n)
+ *                     bytes, 256-byte aligned, contents irrelevant (about 8
+ *                     bytes per input token: per chunk of the sequences a
+ *                     record, a list of its score bins and its keys sorted by
+ *                     bin). Too small or NULL: TG_ERR_WORKSPACE; misaligned:
+ *                     TG_ERR_INVALID_ARG.
+ * Two kernels: per chunk of up to 4096 tokens a summary (forced count, NaN
+ * flag, key range, the non-empty bins of the keys' top 16 bits, the keys
+ * sorted by bin); then workgroups that share the output rows derive the
+ * threshold key from the summaries and emit their rows.
  * ------------------------------------------------------------------------- */
 size_t tg_topk_select_workspace_size(int B, int64_t T_in, int max_n);
 tg_status tg_topk_select(const float* s, const uint8_t* keep_mask,
@@ -128,19 +130,38 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask,
                          int32_t* kept_idx, int32_t* d_status,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Selection and compaction in one pass — [TC] early token filtering: only the
+ * selected tokens go on above the gate. Exactly tg_topk_select followed by
+ * tg_compact on the same arguments (same outputs, bit for bit), but the
+ * workgroups that emit a share of the kept indices copy those rows, positions
+ * and scores at once, so the row gather is spread over the whole GPU and the
+ * kept indices are not read back.
+ *  h [T_in, D] dtype, pos [T_in] int32 or NULL (then a token's position is its
+ *  index inside its sequence); h_out [T, D] dtype, pos_out [T] int32,
+ *  s_out [T] fp32 or NULL; the rest as tg_topk_select (same workspace). Rows
+ *  of a rejected sequence are zeros, its positions -1 and its scores 0.
+ * ------------------------------------------------------------------------- */
+tg_status tg_select_compact(const float* s, const uint8_t* keep_mask,
+                            const int32_t* d_cu_in, const int32_t* d_cu_kept,
+                            int B, int64_t T_in, int64_t T, int max_n,
+                            const void* h, const int32_t* pos, int D, tg_dtype dtype,
+                            int32_t* kept_idx, int32_t* d_status,
+                            void* h_out, int32_t* pos_out, float* s_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* The same selection for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): no ws argument. Where tg_topk_select needs a workspace
- * (max_n > 32768) this call uses a scratch array of
- * TG_SELECT_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
- * one per GPU for the life of the process, and calls no allocating routine.
+ * hipMalloc): no ws argument. In place of the workspace this call uses a
+ * scratch array of TG_SELECT_NOALLOC_SCRATCH_BYTES that the library holds in
+ * device memory, one per GPU for the life of the process, and calls no
+ * allocating routine (about half a million input tokens per call).
  * Arguments, outputs and results are those of tg_topk_select. Errors: as
  * tg_topk_select, plus TG_ERR_WORKSPACE when
  * tg_topk_select_workspace_size(B, T_in, max_n) exceeds the scratch size
  * (nothing is enqueued then). Every call on a GPU shares that GPU's scratch,
- * which keeps the last call's contents (each call clears what it must start
- * from): calls that overlap on one GPU (other streams, other host threads)
- * race and must be serialised by the caller. */
+ * which keeps the last call's contents (each call writes everything it reads
+ * before reading it): calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller. */
 #define TG_SELECT_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 tg_status tg_topk_select_noalloc(const float* s, const uint8_t* keep_mask,
                                  const int32_t* d_cu_in, const int32_t* d_cu_kept,
@@ -305,16 +326,17 @@ tg_status tg_upper_layer_stack_fwd(const tg_layer_weights* w, int n_layers,
  * One gated prefill step above layer L, the whole path in one call — [FW]
  * the method: score after layer L, keep K tokens, run the layers above on
  * them; [TC] early token filtering. In order on `stream`: tg_gate_score on h,
- * tg_topk_select, tg_compact (pos NULL: a token's position is its index in
- * its sequence), tg_upper_layer_stack_fwd on the compacted rows.
+ * tg_select_compact (pos NULL: a token's position is its index in its
+ * sequence), tg_upper_layer_stack_fwd on the compacted rows.
  *  h [T_in, D] dtype (D = dims->D); gate: the scorer's weights (W1 [H1, D],
  *  b1 [H1], w2 [H1], b2 [1], dtype); layers [n_layers], dims as for the
  *  stack (flags 0 or TG_LAYER_NORMS_FOLDED).
  *  Outputs: s [T_in] fp32, kept_idx [T] int32, d_status [B] int32 (may be
  *  NULL), x [T, D] dtype (the compacted rows, then the last layer's output),
  *  pos_c [T] int32, s_c [T] fp32, kcache / vcache [n_layers, T, Hkv, d].
- * Workspace: tg_gated_prefill_workspace_size() (the larger of the scorer's
- * and one layer's). The first failing stage's status is returned; stages
+ * Workspace: tg_gated_prefill_workspace_size() (the largest of the
+ * scorer's, the selection's for any max_n and one layer's). The first
+ * failing stage's status is returned; stages
  * before it have been enqueued.
  * ------------------------------------------------------------------------- */
 typedef struct tg_gate_weights {

@@ -29,7 +29,7 @@ ABI_FUNCTIONS = (
     "tg_status_string", "tg_abi_version",
     "tg_gate_score_workspace_size", "tg_gate_score",
     "tg_topk_select_workspace_size", "tg_topk_select", "tg_topk_select_noalloc",
-    "tg_compact",
+    "tg_compact", "tg_select_compact",
     "tg_gated_attn_workspace_size", "tg_gated_attn_fwd",
     "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
     "tg_upper_layer_fwd_timed", "tg_fold_norm_weights", "tg_upper_layer_stack_fwd",
@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.tg_topk_select_noalloc.restype = i32
     L.tg_compact.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp, vp, vp]
     L.tg_compact.restype = i32
+    L.tg_select_compact.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp,
+                                    vp, vp, sz, vp]
+    L.tg_select_compact.restype = i32
     L.tg_gated_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.tg_gated_attn_workspace_size.restype = sz
     L.tg_gated_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -185,11 +188,10 @@ def topk_select(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, kept=None, sta
     if status is None:
         status = torch.empty(max(B, 1), dtype=torch.int32, device=s.device)
     need = lib().tg_topk_select_workspace_size(max(B, 0), s.numel(), max_n)
-    if need and (ws is None or ws.numel() < need):
+    if ws is None or ws.numel() < need:
         ws = _empty_ws(need, s.device)
     _check(lib().tg_topk_select(_p(s), _p(keep_mask), _p(cu_in), _p(cu_kept), B, s.numel(), T,
-                                max_n, _p(kept), _p(status), _p(ws) if need else None,
-                                ws.numel() if need else 0, _stream()),
+                                max_n, _p(kept), _p(status), _p(ws), ws.numel(), _stream()),
            "tg_topk_select")
     return kept, status
 
@@ -221,6 +223,33 @@ def compact(h, pos, s, kept, cu_in, cu_kept, h_out=None, pos_out=None, s_out=Non
                             dtype_code(h.dtype), _p(h_out), _p(pos_out), _p(s_out), _stream()),
            "tg_compact")
     return h_out, pos_out, s_out
+
+
+def select_compact(s, keep_mask, cu_in, cu_kept, T: int, max_n: int, h, pos=None, kept=None,
+                   status=None, h_out=None, pos_out=None, s_out=None, ws=None):
+    """tg_select_compact: the selection and the compaction of the kept rows in
+    one pass (outputs as topk_select followed by compact)."""
+    B = cu_in.numel() - 1
+    dev = s.device
+    D = h.shape[1]
+    if kept is None:
+        kept = torch.empty(max(T, 0), dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    if h_out is None:
+        h_out = torch.empty((T, D), dtype=h.dtype, device=dev)
+    if pos_out is None:
+        pos_out = torch.empty(T, dtype=torch.int32, device=dev)
+    if s_out is None:
+        s_out = torch.empty(T, dtype=torch.float32, device=dev)
+    need = lib().tg_topk_select_workspace_size(max(B, 0), s.numel(), max_n)
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(need, dev)
+    _check(lib().tg_select_compact(_p(s), _p(keep_mask), _p(cu_in), _p(cu_kept), B, s.numel(), T, max_n,
+                                   _p(h), _p(pos), D, dtype_code(h.dtype), _p(kept), _p(status),
+                                   _p(h_out), _p(pos_out), _p(s_out), _p(ws), ws.numel(), _stream()),
+           "tg_select_compact")
+    return kept, status, h_out, pos_out, s_out
 
 
 def gated_attn_fwd(q, k, v, s_c, t, g, cu_kept, max_k: int, o=None, lse=None, want_lse=False):

@@ -145,14 +145,14 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1, const void* 
 
 // ---------------------------------------------------------------------------
 size_t tg_topk_select_workspace_size(int B, int64_t T_in, int max_n) {
-  if (B < 0 || T_in < 0) return 0;
-  return tg::topk_select_workspace_bytes(B, T_in, max_n);
+  if (B <= 0 || T_in < 0 || max_n < 0 || !tg::select_supported(max_n)) return 0;
+  return tg::select_workspace_bytes(B, T_in, max_n);
 }
 
-tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t* d_cu_in,
-                         const int32_t* d_cu_kept, int B, int64_t T_in, int64_t T, int max_n,
-                         int32_t* kept_idx, int32_t* d_status, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+// Arguments shared by the selection entry points (checked before any HIP call).
+static tg_status select_args(const float* s, const int32_t* d_cu_in, const int32_t* d_cu_kept, int B,
+                             int64_t T_in, int64_t T, int max_n, const int32_t* kept_idx, void* ws,
+                             size_t ws_bytes) {
   TG_CHECK(B >= 0 && T_in >= 0 && T >= 0 && max_n >= 0, TG_ERR_INVALID_ARG);
   TG_CHECK(T_in <= INT_MAX && T <= INT_MAX, TG_ERR_INVALID_ARG);
   TG_CHECK(T <= T_in, TG_ERR_INVALID_ARG);  // K_b <= N_b summed over the batch
@@ -160,30 +160,59 @@ tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t
   TG_CHECK(d_cu_in && d_cu_kept, TG_ERR_INVALID_ARG);
   TG_CHECK(T_in == 0 || s, TG_ERR_INVALID_ARG);
   TG_CHECK(T == 0 || kept_idx, TG_ERR_INVALID_ARG);
-  // one workgroup per (sequence, 4096-token chunk) on the long-sequence path
-  TG_CHECK(((int64_t)max_n + 4095) / 4096 * B <= INT_MAX, TG_ERR_INVALID_ARG);
-  const size_t need = tg::topk_select_workspace_bytes(B, T_in, max_n);
-  TG_CHECK(need == 0 || (ws && ws_bytes >= need), TG_ERR_WORKSPACE);
-  TG_CHECK(need == 0 || ((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(tg::select_supported(max_n), TG_ERR_UNSUPPORTED);
+  // one workgroup per (sequence, chunk of at least 256 tokens)
+  TG_CHECK(((int64_t)max_n + 255) / 256 * B <= INT_MAX, TG_ERR_INVALID_ARG);
+  const size_t need = tg::select_workspace_bytes(B, T_in, max_n);
+  TG_CHECK(ws && ws_bytes >= need, TG_ERR_WORKSPACE);
+  TG_CHECK(((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);
+  return TG_OK;
+}
+
+tg_status tg_topk_select(const float* s, const uint8_t* keep_mask, const int32_t* d_cu_in,
+                         const int32_t* d_cu_kept, int B, int64_t T_in, int64_t T, int max_n,
+                         int32_t* kept_idx, int32_t* d_status, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  const tg_status st = select_args(s, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx, ws, ws_bytes);
+  if (st != TG_OK || B == 0) return st;
   tg_status a = check_arch();
   if (a != TG_OK) return a;
-  return launched(tg::launch_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, max_n, kept_idx,
-                                         d_status, ws, stream));
+  return launched(tg::launch_select_compact(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n,
+                                            kept_idx, d_status, ws, nullptr, nullptr, 0, nullptr,
+                                            nullptr, nullptr, stream));
+}
+
+tg_status tg_select_compact(const float* s, const uint8_t* keep_mask, const int32_t* d_cu_in,
+                            const int32_t* d_cu_kept, int B, int64_t T_in, int64_t T, int max_n,
+                            const void* h, const int32_t* pos, int D, tg_dtype dtype,
+                            int32_t* kept_idx, int32_t* d_status, void* h_out, int32_t* pos_out,
+                            float* s_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  TG_CHECK(D > 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(dtype_ok(dtype), TG_ERR_UNSUPPORTED);
+  const tg_status st = select_args(s, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx, ws, ws_bytes);
+  if (st != TG_OK || B == 0) return st;
+  TG_CHECK(T == 0 || (h && h_out && pos_out), TG_ERR_INVALID_ARG);
+  TG_CHECK((int64_t)D * (int64_t)elt_size(dtype) < ((int64_t)1 << 31), TG_ERR_UNSUPPORTED);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+  return launched(tg::launch_select_compact(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n,
+                                            kept_idx, d_status, ws, h, pos,
+                                            (size_t)D * elt_size(dtype), T > 0 ? h_out : nullptr,
+                                            pos_out, s_out, stream));
 }
 
 tg_status tg_topk_select_noalloc(const float* s, const uint8_t* keep_mask, const int32_t* d_cu_in,
                                  const int32_t* d_cu_kept, int B, int64_t T_in, int64_t T, int max_n,
                                  int32_t* kept_idx, int32_t* d_status, hipStream_t stream) {
-  TG_CHECK(B >= 0 && T_in >= 0 && T >= 0 && max_n >= 0, TG_ERR_INVALID_ARG);
-  TG_CHECK(T_in <= INT_MAX && T <= INT_MAX, TG_ERR_INVALID_ARG);
-  TG_CHECK(((int64_t)max_n + 4095) / 4096 * B <= INT_MAX, TG_ERR_INVALID_ARG);
-  const size_t need = B > 0 ? tg::topk_select_workspace_bytes(B, T_in, max_n) : 0;
-  TG_CHECK(need <= TG_SELECT_NOALLOC_SCRATCH_BYTES, TG_ERR_WORKSPACE);
+  // every argument check before the first HIP call, with the scratch standing
+  // in for the workspace (its size; any 256-aligned address)
+  const tg_status chk = select_args(s, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx,
+                                    reinterpret_cast<void*>(256), TG_SELECT_NOALLOC_SCRATCH_BYTES);
+  if (chk != TG_OK || B == 0) return chk;
+  const size_t need = tg::select_workspace_bytes(B, T_in, max_n);
   void* ws = nullptr;
-  if (need > 0) {
-    const tg_status st = noalloc_scratch(&ws);
-    if (st != TG_OK) return st;
-  }
+  const tg_status st = noalloc_scratch(&ws);
+  if (st != TG_OK) return st;
   return tg_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx, d_status,
                         ws, need, stream);
 }
@@ -446,7 +475,7 @@ size_t tg_gated_prefill_workspace_size(const tg_layer_dims* dm, int H1, int64_t 
   tg_layer_dims base = *dm;
   base.flags &= TG_LAYER_NORMS_FOLDED;
   const size_t b = tg_upper_layer_workspace_size(&base, T, B, max_k);
-  const size_t c = tg_topk_select_workspace_size(B, T_in, INT_MAX);
+  const size_t c = B > 0 && T_in >= 0 ? tg::select_workspace_bound(B, T_in) : 0;
   const size_t ab = a > b ? a : b;
   return ab > c ? ab : c;
 }
@@ -462,11 +491,8 @@ tg_status tg_gated_prefill(const void* h, const int32_t* pos, const uint8_t* kee
   tg_status st = tg_gate_score(h, T_in, dm->D, gate->H1, gate->W1, gate->b1, gate->w2, gate->b2,
                                dm->dtype, s, ws, ws_bytes, stream);
   if (st != TG_OK) return st;
-  st = tg_topk_select(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n, kept_idx, d_status,
-                      ws, ws_bytes, stream);
-  if (st != TG_OK) return st;
-  st = tg_compact(h, pos, s, kept_idx, d_cu_in, d_cu_kept, B, T, dm->D, dm->dtype, x, pos_c, s_c,
-                  stream);
+  st = tg_select_compact(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n, h, pos, dm->D,
+                         dm->dtype, kept_idx, d_status, x, pos_c, s_c, ws, ws_bytes, stream);
   if (st != TG_OK) return st;
   return tg_upper_layer_stack_fwd(layers, n_layers, dm, x, pos_c, s_c, d_cu_kept, B, T, max_k,
                                   kcache, vcache, ws, ws_bytes, stream);

@@ -41,11 +41,16 @@ inline int device_cu_count() {
   return n;
 }
 
-// Workspace of launch_topk_select (0 when max_n fits one workgroup's LDS).
-size_t topk_select_workspace_bytes(int B, int64_t T_in, int max_n);
-hipError_t launch_topk_select(const float* s, const uint8_t* mask, const int32_t* cu_in,
-                              const int32_t* cu_kept, int B, int max_n, int32_t* kept,
-                              int32_t* status, void* ws, hipStream_t stream);
+// Top-K selection with forced keep (and, with h_out, the compaction of the
+// kept rows in the same pass). Supported for max_n up to 1M tokens per sequence.
+bool select_supported(int max_n);
+size_t select_workspace_bytes(int B, int64_t T_in, int max_n);
+size_t select_workspace_bound(int B, int64_t T_in);  // over every max_n <= T_in
+hipError_t launch_select_compact(const float* s, const uint8_t* mask, const int32_t* cu_in,
+                                 const int32_t* cu_kept, int B, int64_t T_in, int64_t T, int max_n,
+                                 int32_t* kept, int32_t* status, void* ws, const void* h,
+                                 const int32_t* pos, size_t row_bytes, void* h_out,
+                                 int32_t* pos_out, float* s_out, hipStream_t stream);
 
 hipError_t launch_compact(const void* h, const int32_t* pos, const float* s, const int32_t* kept,
                           const int32_t* cu_in, const int32_t* cu_kept, int B, int64_t T,

@@ -110,6 +110,14 @@ class GatedPrefill:
         tg.compact(d.h, None, self.s, self.kept, d.cu_in, d.cu_kept,
                    h_out=self.x, pos_out=self.pos_c, s_out=self.s_c)
 
+    def select_compact(self):
+        """Selection and compaction in one pass (tg_select_compact): the same
+        outputs as select() then compact(), as the whole-step call runs them."""
+        d = self.dw
+        tg.select_compact(self.s, d.keep_mask, d.cu_in, d.cu_kept, d.w.T, d.w.max_n, d.h,
+                          kept=self.kept, status=self.status, h_out=self.x, pos_out=self.pos_c,
+                          s_out=self.s_c, ws=self.ws)
+
     def layer(self, l: int):
         d = self.dw
         # layers after the first reuse the RoPE table the first one left in the
@@ -122,7 +130,7 @@ class GatedPrefill:
 
     def run(self):
         """One step in one native call (tg_gated_prefill): the same kernels as
-        score(), select(), compact() and layer(l) for every l, in that order."""
+        score(), select_compact() and layer(l) for every l, in that order."""
         d = self.dw
         tg.gated_prefill(d.h, d.keep_mask, d.cu_in, d.cu_kept, d.w.T, d.w.max_n, d.w.max_k,
                          d.W1, d.b1, d.w2, d.b2, d.layers, d.dims, self.s, self.kept, self.status,

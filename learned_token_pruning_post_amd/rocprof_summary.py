@@ -32,6 +32,7 @@ COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 _SHARED = ["tg_common.hpp", "tg_internal.hpp"]
 STAGE_SOURCES = {
     "gate_score": ["tg_gemm.hip"] + _SHARED,
+    "select_compact": ["tg_select.hip"] + _SHARED,
     "topk_select": ["tg_select.hip"] + _SHARED,
     "compact": ["tg_rowops.hip"] + _SHARED,
     "rmsnorm_attn": ["tg_rowops.hip"] + _SHARED,

@@ -83,7 +83,6 @@ def test_topk_select_argument_errors(L):
     assert f(FAKE, None, None, FAKE, 1, 10, 5, 10, FAKE, None, None, 0, None) == INVALID
     assert f(FAKE, None, FAKE, FAKE, 1, 10, 5, 10, None, None, None, 0, None) == INVALID
     assert f(None, None, None, None, 0, 0, 0, 0, None, None, None, 0, None) == OK  # B = 0
-    assert L.tg_topk_select_workspace_size(8, 1 << 17, 1 << 14) == 0
 
 
 def test_topk_select_noalloc_argument_errors(L):
@@ -94,27 +93,53 @@ def test_topk_select_noalloc_argument_errors(L):
     assert f(FAKE, None, FAKE, FAKE, 1, 10, 11, 10, FAKE, None, None) == INVALID  # T > T_in
     assert f(None, None, None, None, 0, 0, 0, 0, None, None, None) == OK  # B = 0
     cap = tg.SELECT_NOALLOC_SCRATCH_BYTES
-    B = 200  # three 16 KB histograms per sequence: 9.6 MB > 4 MiB
+    B = 200  # about 8 bytes of scratch per token: 64 MB > 4 MiB
     assert L.tg_topk_select_workspace_size(B, B * 40000, 40000) > cap
     assert f(FAKE, None, FAKE, FAKE, B, B * 40000, B * 100, 40000, FAKE, None, None) == WS
     assert L.tg_topk_select_workspace_size(8, 8 * 40000, 40000) <= cap
 
 
-def test_topk_select_long_path_workspace(L):
-    """Above 32768 tokens per sequence the selection needs scratch: three
-    4096-bin histograms per sequence and a 32-byte record per 4096-token
-    chunk slot, each block 256-byte aligned."""
-    B, T_in, max_n = 3, 200000, 100000
+def test_topk_select_workspace(L):
+    """The selection's scratch: per chunk slot (T_in / CH + B + 1 of them) a
+    32-byte record, two bin lists and a key array of CH words each, each block
+    256-byte aligned; CH = 256 tokens per chunk, doubled until a sequence of
+    max_n tokens has at most 256 chunks (at most 4096)."""
     a = lambda x: (x + 255) // 256 * 256
+    for B, T_in, max_n, CH in ((3, 200000, 100000, 512), (1, 32768, 32768, 256),
+                               (8, 131072, 16384, 256), (2, 1 << 21, 1 << 20, 4096)):
+        slots = T_in // CH + B + 1
+        need = L.tg_topk_select_workspace_size(B, T_in, max_n)
+        assert need == a(slots * 32) + 3 * a(slots * CH * 4), (B, T_in, max_n)
+    assert L.tg_topk_select_workspace_size(0, 10, 10) == 0
+    assert L.tg_topk_select_workspace_size(1, 1 << 23, (1 << 20) + 1) == 0  # unsupported length
+    B, T_in, max_n = 3, 200000, 100000
     need = L.tg_topk_select_workspace_size(B, T_in, max_n)
-    assert need == a(B * 3 * 4096 * 4) + a((T_in // 4096 + B + 1) * 32)
-    assert L.tg_topk_select_workspace_size(B, T_in, 32768) == 0
-    assert L.tg_topk_select_workspace_size(B, T_in, 32769) == need
     f = L.tg_topk_select
     assert f(FAKE, None, FAKE, FAKE, B, T_in, 5, max_n, FAKE, None, None, 0, None) == WS
     assert f(FAKE, None, FAKE, FAKE, B, T_in, 5, max_n, FAKE, None, FAKE, need - 1, None) == WS
     odd = ctypes.c_void_p(0x100000 + 16)
     assert f(FAKE, None, FAKE, FAKE, B, T_in, 5, max_n, FAKE, None, odd, need, None) == INVALID
+    assert f(FAKE, None, FAKE, FAKE, 1, 1 << 23, 5, (1 << 20) + 1, FAKE, None, FAKE, 1 << 30, None) == UNSUP
+
+
+def test_select_compact_argument_errors(L):
+    """The fused selection + compaction validates like tg_topk_select plus the
+    row arguments of tg_compact."""
+    f = L.tg_select_compact
+    B, T_in, T, max_n = 1, 1000, 100, 1000
+    need = L.tg_topk_select_workspace_size(B, T_in, max_n)
+    args = lambda **k: [k.get("s", FAKE), None, FAKE, FAKE, B, T_in, k.get("T", T), max_n,
+                        k.get("h", FAKE), None, k.get("D", 64), k.get("dt", 1), FAKE, None,
+                        k.get("h_out", FAKE), k.get("pos_out", FAKE), None, k.get("ws", FAKE),
+                        k.get("wsb", need), None]
+    assert f(*args(D=0)) == INVALID
+    assert f(*args(dt=5)) == UNSUP
+    assert f(*args(h=None)) == INVALID
+    assert f(*args(h_out=None)) == INVALID
+    assert f(*args(pos_out=None)) == INVALID
+    assert f(*args(T=T_in + 1)) == INVALID
+    assert f(*args(wsb=need - 1)) == WS
+    assert f(*args(ws=None)) == WS
 
 
 def test_compact_argument_errors(L):

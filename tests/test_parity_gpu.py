@@ -47,23 +47,30 @@ def _stage_parity(w, score_rows=None, layer_rows_per_seq=None, seed=0, norms_fol
     e = assert_close(s[rows], ref, dt, "scores")
     say("  scorer max err", e)
 
-    # ---- select: bit exact on the same fp32 scores ----
-    gp.select()
-    torch.cuda.synchronize()
-    kept = gp.kept.cpu().numpy()
+    # ---- select + compact: bit exact on the same fp32 scores ----
     ref_kept, flags = O.topk_select(s, gi.keep_mask, gi.cu_in, gi.cu_kept)
-    assert np.array_equal(gp.status.cpu().numpy(), flags.astype(np.int32))
-    assert np.array_equal(kept, ref_kept.astype(np.int32))
-    say("  select bit-exact", len(kept))
-
-    # ---- compact: bit exact ----
-    gp.compact()
-    torch.cuda.synchronize()
     hc_ref, pc_ref, sc_ref = O.compact(gi.h.device_array, None, s, ref_kept, gi.cu_in, gi.cu_kept)
-    assert np.array_equal(bits(gp.x), np.ascontiguousarray(hc_ref).view(bits(gp.x).dtype))
-    assert np.array_equal(gp.pos_c.cpu().numpy(), pc_ref.astype(np.int32))
-    assert np.array_equal(gp.s_c.cpu().numpy().view(np.int32), sc_ref.astype(np.float32).view(np.int32))
-    say("  compact bit-exact")
+
+    def check_selected(what):
+        torch.cuda.synchronize()
+        assert np.array_equal(gp.status.cpu().numpy(), flags.astype(np.int32)), what
+        assert np.array_equal(gp.kept.cpu().numpy(), ref_kept.astype(np.int32)), what
+        assert np.array_equal(bits(gp.x), np.ascontiguousarray(hc_ref).view(bits(gp.x).dtype)), what
+        assert np.array_equal(gp.pos_c.cpu().numpy(), pc_ref.astype(np.int32)), what
+        assert np.array_equal(gp.s_c.cpu().numpy().view(np.int32),
+                              sc_ref.astype(np.float32).view(np.int32)), what
+
+    for buf in (gp.kept, gp.status, gp.pos_c):
+        buf.fill_(-5)
+    gp.select()   # the two calls one after the other
+    gp.compact()
+    check_selected("tg_topk_select + tg_compact")
+    for buf in (gp.kept, gp.status, gp.pos_c):
+        buf.fill_(-5)
+    gp.x.zero_()
+    gp.select_compact()  # the fused pass the whole step runs (last: the layer reads its output)
+    check_selected("tg_select_compact")
+    say("  select + compact bit-exact", len(ref_kept), "(separate calls and fused)")
 
     # ---- one upper layer, stage by stage ----
     x_in = f64(gp.x)
