@@ -334,6 +334,94 @@ def upper_layer(x, pos_c, s_c, W: Dict[str, np.ndarray], dims, cu_kept,
             "x1": x1, "n2": n2, "act": act, "x2": x2}
 
 
+def attention_half(x, pos, s, W: Dict[str, np.ndarray], dims, cu, t=None, g=None):
+    """The attention half of a decoder layer, up to the post-attention residual:
+    n1 = RMSNorm(x) * attn_norm; q, k, v projections; RoPE at ``pos``;
+    attention with temperature ``t`` and gain ``g`` (default: W's; pass
+    t = 1, g = 0 for plain causal attention); x1 = x + o Wo^T.
+
+    [TC] early token filtering and [AI] mechanism design: the gate scorer
+    reads this residual of layer L, after its attention and before its FFN.
+    Returns {"x1", "k", "v"}.
+    """
+    x = _f64(x)
+    _, q, k, v = qkv_rope(x, pos, W, dims)
+    tt = W["t"] if t is None else t
+    gg = W["g"] if g is None else g
+    o, _ = gated_attention(q, k, v, s, tt, gg, cu)
+    return {"x1": o_proj(x, o, W["wo"]), "k": k, "v": v}
+
+
+def ffn_half(x1, W: Dict[str, np.ndarray], dims):
+    """The FFN half of a decoder layer: x2 = x1 + SwiGLU(RMSNorm(x1) * ffn_norm) Wd^T."""
+    _, act = swiglu_act(x1, W, dims.rms_eps)
+    return down_proj(x1, act, W["wd"])
+
+
+def plain_layer(x, pos, W: Dict[str, np.ndarray], dims, cu):
+    """A layer below the gate: both halves, plain causal attention (t = 1,
+    g = 0; the gate's bias only exists above it). Returns {"x2", "k", "v"}."""
+    a = attention_half(x, pos, np.zeros(_f64(x).shape[0]), W, dims, cu,
+                       t=np.ones(dims.Hq), g=np.zeros(dims.Hq))
+    return {"x2": ffn_half(a["x1"], W, dims), "k": a["k"], "v": a["v"]}
+
+
+def local_positions(cu_in):
+    """Each token's index inside its own sequence (the original positions)."""
+    cu_in = np.asarray(cu_in, dtype=np.int64)
+    return np.concatenate([np.arange(int(cu_in[b + 1] - cu_in[b])) for b in range(len(cu_in) - 1)]
+                          or [np.zeros(0, dtype=np.int64)])
+
+
+def full_prefill(h, gate, below, gate_layer, above, keep_mask, cu_in, cu_kept, dims):
+    """The three-stage forward with the gate at layer L = len(below).
+
+    [FW] the method and [AI] mechanism design: the forward splits in three;
+    [TC] early token filtering: all prompt tokens go through the layers below
+    the gate and through layer L's attention (full-prompt KV there, [TC]
+    engineering section); the scorer reads layer L's post-attention residual
+    and the selector keeps K tokens; only those go on into layer L's FFN and
+    the layers above, whose attention is gated.
+      h: [T_in, D] the rows entering layer 0; gate: (W1, b1, w2, b2);
+      below: L layer dicts; gate_layer: layer L's dict; above: layer dicts.
+    Selection runs on the oracle's own scores.
+    """
+    pos = local_positions(cu_in)
+    x = _f64(h)
+    kv_below = []
+    for W in below:
+        r = plain_layer(x, pos, W, dims, cu_in)
+        kv_below.append((r["k"], r["v"]))
+        x = r["x2"]
+    x_below = x
+    a = attention_half(x, pos, np.zeros(x.shape[0]), gate_layer, dims, cu_in,
+                       t=np.ones(dims.Hq), g=np.zeros(dims.Hq))
+    kv_below.append((a["k"], a["v"]))
+    x1 = a["x1"]
+    s = gate_score(x1, *gate)
+    kept, flags = topk_select(s, keep_mask, cu_in, cu_kept)
+    x1c, pos_c, s_c = compact(x1, pos, s, kept, cu_in, cu_kept)
+    xk = ffn_half(x1c, gate_layer, dims)
+    x_gate = xk
+    kv_above = []
+    for W in above:
+        r = upper_layer(xk, pos_c, s_c, W, dims, cu_kept)
+        kv_above.append((r["k"], r["v"]))
+        xk = r["x2"]
+    return {"x_below": x_below, "x1": x1, "s": s, "kept": kept, "flags": flags, "pos_c": pos_c,
+            "s_c": s_c, "x_gate": x_gate, "x": xk, "kv_below": kv_below, "kv_above": kv_above}
+
+
+def unpruned_prefill(h, layers, cu_in, dims):
+    """The same model without the gate: every layer on every token with plain
+    attention (the baseline the pages' prefill speedups are measured against)."""
+    pos = local_positions(cu_in)
+    x = _f64(h)
+    for W in layers:
+        x = plain_layer(x, pos, W, dims, cu_in)["x2"]
+    return x
+
+
 # ----------------------------------------------------------------------------
 # The whole gated prefill above layer L's attention
 # ----------------------------------------------------------------------------

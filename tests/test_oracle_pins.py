@@ -519,3 +519,103 @@ def test_pipeline_forced_always_kept_on_workload():
     kept, flags = O.topk_select(s.astype(np.float32), gi.keep_mask, gi.cu_in, gi.cu_kept)
     assert len(kept) == 128 and np.all(flags == 0)
     assert set(range(512 - 32, 512)) <= set(kept.tolist())
+
+
+# ----------------------------------------------------------------------------
+# the below-gate path: three-stage forward
+# ----------------------------------------------------------------------------
+
+def _torch_layer(X, W, pos, dm):
+    """Textbook pre-norm decoder layer (plain causal attention) in torch fp64:
+    returns (x1, x2), the post-attention residual and the layer output."""
+    T = X.shape[0]
+    tw = {k_: torch.from_numpy(np.asarray(v_)) for k_, v_ in W.items()}
+    n1 = F.rms_norm(X, (dm.D,), tw["attn_norm"], eps=dm.rms_eps)
+    q = _torch_rope(F.linear(n1, tw["wq"]).view(T, dm.Hq, dm.d), pos, dm.rope_base)
+    k = _torch_rope(F.linear(n1, tw["wk"]).view(T, dm.Hkv, dm.d), pos, dm.rope_base)
+    v = F.linear(n1, tw["wv"]).view(T, dm.Hkv, dm.d)
+    a = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
+                                       v.transpose(0, 1)[None], is_causal=True, enable_gqa=True)
+    x1 = X + F.linear(a[0].transpose(0, 1).reshape(T, dm.Hq * dm.d), tw["wo"])
+    n2 = F.rms_norm(x1, (dm.D,), tw["ffn_norm"], eps=dm.rms_eps)
+    x2 = x1 + F.linear(F.silu(F.linear(n2, tw["wg"])) * F.linear(n2, tw["wu"]), tw["wd"])
+    return x1, x2
+
+
+def test_layer_halves_match_textbook_layer():
+    """attention_half gives the textbook layer's post-attention residual (with
+    t = 1, g = 0), ffn_half turns that into the layer output, and plain_layer
+    is the two in a row."""
+    dm = SMALL
+    rng = np.random.default_rng(21)
+    T = 19
+    x = rng.standard_normal((T, dm.D))
+    pos = np.arange(T)
+    W = _layer_w(5, dm)  # its own t and g are not used below the gate
+    x1_ref, x2_ref = _torch_layer(torch.from_numpy(x), W, torch.from_numpy(pos), dm)
+    a = O.attention_half(x, pos, rng.random(T), W, dm, np.array([0, T]), t=np.ones(dm.Hq),
+                         g=np.zeros(dm.Hq))
+    np.testing.assert_allclose(a["x1"], x1_ref.numpy(), atol=1e-11)
+    np.testing.assert_allclose(O.ffn_half(x1_ref.numpy(), W, dm), x2_ref.numpy(), atol=1e-11)
+    np.testing.assert_allclose(O.plain_layer(x, pos, W, dm, np.array([0, T]))["x2"], x2_ref.numpy(),
+                               atol=1e-11)
+
+
+def _prefill_case(seed, N, K, F):
+    dm = SMALL
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((sum(N), dm.D))
+    cu_in = np.concatenate([[0], np.cumsum(N)])
+    cu_k = np.concatenate([[0], np.cumsum(K)])
+    mask = np.zeros(sum(N), np.uint8)
+    for b in range(len(N)):
+        mask[cu_in[b + 1] - F:cu_in[b + 1]] = 1
+    gate = (rng.standard_normal((dm.H1, dm.D)) * 0.5, rng.standard_normal(dm.H1) * 0.1,
+            rng.standard_normal(dm.H1), rng.standard_normal(1) * 0.1)
+    return dm, h, cu_in, cu_k, mask, gate
+
+
+def test_full_prefill_keep_all_is_the_unpruned_model():
+    """K = N with g = 0, t = 1 above the gate: the three-stage forward is the
+    plain decoder stack over every token (textbook layers in torch), and so is
+    unpruned_prefill; layer L's K/V are the textbook layer's."""
+    dm, h, cu_in, cu_k, mask, gate = _prefill_case(22, [17], [17], 3)
+    Ws = [_layer_w(30 + i, dm) for i in range(3)]  # layer 0 below, layer 1 the gate, layer 2 above
+    for W in Ws:
+        W["t"] = np.ones(dm.Hq)
+        W["g"] = np.zeros(dm.Hq)
+    r = O.full_prefill(h, gate, Ws[:1], Ws[1], Ws[2:], mask, cu_in, cu_k, dm)
+    assert r["kept"].tolist() == list(range(17))
+    X = torch.from_numpy(h)
+    P = torch.arange(17)
+    for W in Ws:
+        X = _torch_layer(X, W, P, dm)[1]
+    np.testing.assert_allclose(r["x"], X.numpy(), atol=1e-10)
+    np.testing.assert_allclose(O.unpruned_prefill(h, Ws, cu_in, dm), X.numpy(), atol=1e-10)
+
+
+def test_full_prefill_scores_read_layer_L_post_attention_residual():
+    """The scores are the scorer on layer L's post-attention residual (textbook
+    layers below, then layer L's attention); neither layer L's input nor its
+    output gives the same scores, so a misplaced scorer fails here."""
+    dm, h, cu_in, cu_k, mask, gate = _prefill_case(23, [15, 12], [6, 5], 2)
+    Ws = [_layer_w(40 + i, dm) for i in range(3)]
+    r = O.full_prefill(h, gate, Ws[:1], Ws[1], Ws[2:], mask, cu_in, cu_k, dm)
+    xin, x1, x2 = [], [], []
+    for b, n in enumerate((15, 12)):
+        X = torch.from_numpy(h[cu_in[b]:cu_in[b + 1]])
+        P = torch.arange(n)
+        X = _torch_layer(X, Ws[0], P, dm)[1]
+        a, o = _torch_layer(X, Ws[1], P, dm)
+        xin.append(X.numpy())
+        x1.append(a.numpy())
+        x2.append(o.numpy())
+    want = O.gate_score(np.concatenate(x1), *gate)
+    np.testing.assert_allclose(r["s"], want, atol=1e-12)
+    np.testing.assert_allclose(r["x1"], np.concatenate(x1), atol=1e-11)
+    for other in (xin, x2):
+        assert np.max(np.abs(O.gate_score(np.concatenate(other), *gate) - want)) > 1e-3
+    # the kept rows are exactly those rows of x1 (then layer L's FFN on them)
+    np.testing.assert_allclose(r["x_gate"], O.ffn_half(np.concatenate(x1)[r["kept"]], Ws[1], dm), atol=1e-11)
+    assert r["kv_above"][0][0].shape[0] == 11 and r["kv_below"][1][0].shape[0] == 27
+    assert np.array_equal(r["pos_c"], O.local_positions(cu_in)[r["kept"]])
