@@ -55,6 +55,9 @@ def parse():
                     help="time only the whole step (no per-kernel events)")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the peak-memory comparison with the unpruned path")
+    ap.add_argument("--no-prefill-time", action="store_true",
+                    help="skip the whole-model prefill (all layers from layer 0) against the "
+                         "same model run unpruned")
     return ap.parse_args()
 
 
@@ -95,6 +98,8 @@ class HipEvents:
 
 
 CPU_LAYERS = 5  # upper layers the CPU baseline runs (about 10 s of fp64 work at K=4096)
+MODEL_LAYERS = 28  # decoder layers of Qwen3-1.7B, the model of the prefill-time comparison
+GATE_LAYER = 1     # the gate position of the pages' main experiments
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}  # atol, rtol of the parity tests
 
 
@@ -234,6 +239,60 @@ def memory_vs_unpruned(torch, tg, w):
             "kv_cache_gb_27_layers_unpruned": round(kv(w.T_in), 3),
             "note": "same N, scorer + select + compact + one upper layer; unpruned = every token kept "
                     "(K = N); K/V of 27 upper layers from the shapes"}
+
+
+def prefill_vs_unpruned(torch, tg, dw, reps=3):
+    """The whole prefill of a MODEL_LAYERS-layer model with the gate at layer
+    GATE_LAYER (layers below it and its attention on all N tokens, its FFN and
+    the layers above on the K kept ones; one tg_full_prefill call) against the
+    same layers run unpruned (every layer on every token, plain attention; one
+    tg_upper_layer_stack_fwd call): GPU time of each with HIP events on the
+    launch stream (mean of `reps` after one warmup), and the peak device
+    memory each one's buffers and run add to the resident weights. Layers
+    beyond the workload's own are generated from the same seeds; the input
+    rows are the workload's, standing in for layer 0's input."""
+    from learned_token_pruning_post_amd.pipeline import FullPrefill, UnprunedPrefill
+    w = dw.w
+    if len(dw.layers) < MODEL_LAYERS:
+        print("[bench] uploading layers %d..%d for the whole-model prefill"
+              % (len(dw.layers), MODEL_LAYERS - 1), file=sys.stderr, flush=True)
+        dw.extend_layers(MODEL_LAYERS)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2 * reps)
+    res = {}
+    makers = (("pruned", lambda: FullPrefill(dw, n_below=GATE_LAYER)),
+              ("unpruned", lambda: UnprunedPrefill(dw)))
+    for name, make in makers:
+        print("[bench] whole-model prefill, %s: 1 warmup + %d timed" % (name, reps),
+              file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        run = make()
+        run.run()
+        torch.cuda.synchronize()
+        peak = (torch.cuda.max_memory_allocated() - base) / 1e9
+        for i in range(reps):
+            ev.record(2 * i, stream)
+            run.run()
+            ev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        ms = [ev.ms(2 * i, 2 * i + 1) for i in range(reps)]
+        res[name] = (sum(ms) / reps, peak)
+        del run
+    ev.close()
+    torch.cuda.empty_cache()
+    (tp, mp), (tu, mu) = res["pruned"], res["unpruned"]
+    return {"layers": MODEL_LAYERS, "gate_layer": GATE_LAYER, "n_prompt_tokens": w.T_in, "n_kept_tokens": w.T,
+            "pruned_ms": round(tp, 3), "unpruned_ms": round(tu, 3), "speedup": round(tu / tp, 2),
+            "pruned_tokens_per_s": round(w.T_in / (tp / 1e3), 1),
+            "unpruned_tokens_per_s": round(w.T_in / (tu / 1e3), 1),
+            "peak_gb_pruned": round(mp, 3), "peak_gb_unpruned": round(mu, 3),
+            "peak_ratio_unpruned_over_pruned": round(mu / mp, 2),
+            "note": "GPU time of the decoder layers' prefill (no embedding, LM head or sampling); "
+                    "peak = buffers and run on top of the resident weights (K/V of every layer "
+                    "included); mean of %d runs after one warmup" % reps}
 
 
 def attention_bias_ratio(tg, torch, w, dw, gp, stream, reps=20):
@@ -517,7 +576,11 @@ def main():
         out["host_gaps"] = gaps
     n_cpu_layers = min(CPU_LAYERS, w.layers)
     g_out = gpu_outputs_for_parity(torch, gp, n_cpu_layers) if want_cpu else None
-    del gp, dw
+    del gp
+    torch.cuda.empty_cache()
+    if not args.no_prefill_time:
+        out["prefill_vs_unpruned"] = prefill_vs_unpruned(torch, tg, dw)
+    del dw
     torch.cuda.empty_cache()
     if not args.no_memory:
         print("[bench] peak memory against the unpruned path (K = N, one layer)", file=sys.stderr, flush=True)

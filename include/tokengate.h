@@ -274,6 +274,19 @@ typedef struct tg_layer_dims {
  * TG_LAYER_NORMS_FOLDED the call returns TG_ERR_INVALID_ARG. */
 #define TG_LAYER_INPUT_SSQ 4
 
+/* tg_layer_dims.flags: one half of the layer only, for a gate layer L whose
+ * FFN runs on the kept tokens alone ([TC] early token filtering: pruned
+ * tokens skip layer L's FFN; the scorer reads layer L's post-attention
+ * residual). TG_LAYER_ATTN_ONLY runs stages 0-4: x_out receives the
+ * post-attention residual x1 = x_in + o Wo^T (x_out may alias x_in).
+ * TG_LAYER_FFN_ONLY runs stages 5-7 on x_in as that residual:
+ * x_out = x_in + SwiGLU(...) Wd^T; pos_c, s_c, d_cu_kept, kcache and vcache
+ * are not used and may be NULL, and with TG_LAYER_NORMS_FOLDED the row sums
+ * of squares of x_in are computed by the call. Both at once:
+ * TG_ERR_INVALID_ARG. */
+#define TG_LAYER_ATTN_ONLY 8
+#define TG_LAYER_FFN_ONLY 16
+
 /* Fold an RMSNorm weight into a projection for TG_LAYER_NORMS_FOLDED, in
  * place on the stream: W[r, c] = W[r, c] * norm_w[c], the product taken in
  * fp32 and rounded to the dtype (nearest even). W [rows, cols] and
@@ -357,6 +370,49 @@ tg_status tg_gated_prefill(const void* h, const int32_t* pos, const uint8_t* kee
                            float* s, int32_t* kept_idx, int32_t* d_status,
                            void* x, int32_t* pos_c, float* s_c, void* kcache, void* vcache,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * The whole three-stage prefill with the gate at layer L = n_below — [FW]
+ * the method: the forward splits in three; [TC] early token filtering: all
+ * prompt tokens run through the layers below the gate and through layer L's
+ * attention, with the full prompt's K/V kept there ([TC] engineering
+ * section); the scorer reads layer L's post-attention residual, the selector
+ * keeps K_b tokens per sequence, and only those go on into layer L's FFN and
+ * the layers above (token-gated attention). In order on `stream`:
+ *   below[l], l < n_below: whole layers on all T_in rows, plain causal
+ *     attention (t = 1, g = 0: their t and g are not read);
+ *   gate_layer: attention half on all T_in rows (plain), x_full = x1;
+ *   tg_gate_score on x_full -> s; tg_select_compact of x_full's rows -> x,
+ *   pos_c, s_c; gate_layer's FFN half on x; tg_upper_layer_stack_fwd of
+ *   above[] on x.
+ *  h [T_in, D] dtype: the rows entering layer 0 (not modified);
+ *  pos [T_in] int32: every token's original position (its index in its
+ *  sequence for a plain prompt);
+ *  x_full [T_in, D] dtype out: layer L's post-attention residual;
+ *  kcache_full / vcache_full [n_below + 1, T_in, Hkv, d] out: K/V of every
+ *  token in layers 0 .. L; max_n bounds the N_b (the attention and selection
+ *  of the full rows), max_k the K_b;
+ *  s, kept_idx, d_status, x, pos_c, s_c, kcache, vcache [n_above, T, Hkv, d]:
+ *  as tg_gated_prefill; with T = 0 (nothing kept) kept_idx, x, pos_c, s_c,
+ *  kcache and vcache may be NULL and the call ends after the selection.
+ *  dims->flags: 0 or TG_LAYER_NORMS_FOLDED.
+ * Workspace: tg_full_prefill_workspace_size(). The first failing stage's
+ * status is returned; stages before it have been enqueued.
+ * ------------------------------------------------------------------------- */
+size_t tg_full_prefill_workspace_size(const tg_layer_dims* dims, int H1, int64_t T_in, int64_t T,
+                                      int B, int max_n, int max_k);
+tg_status tg_full_prefill(const void* h, const int32_t* pos, const uint8_t* keep_mask,
+                          const int32_t* d_cu_in, const int32_t* d_cu_kept, int B,
+                          int64_t T_in, int64_t T, int max_n, int max_k,
+                          const tg_gate_weights* gate,
+                          const tg_layer_weights* below, int n_below,
+                          const tg_layer_weights* gate_layer,
+                          const tg_layer_weights* above, int n_above,
+                          const tg_layer_dims* dims,
+                          void* x_full, void* kcache_full, void* vcache_full,
+                          float* s, int32_t* kept_idx, int32_t* d_status,
+                          void* x, int32_t* pos_c, float* s_c, void* kcache, void* vcache,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Instrumentation: exactly tg_upper_layer_fwd, and in addition records
  * events[i] on `stream` right before stage i of the layer and

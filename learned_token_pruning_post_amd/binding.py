@@ -34,6 +34,7 @@ ABI_FUNCTIONS = (
     "tg_upper_layer_ws_layout", "tg_upper_layer_workspace_size", "tg_upper_layer_fwd",
     "tg_upper_layer_fwd_timed", "tg_fold_norm_weights", "tg_upper_layer_stack_fwd",
     "tg_gated_prefill_workspace_size", "tg_gated_prefill",
+    "tg_full_prefill_workspace_size", "tg_full_prefill",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -64,6 +65,8 @@ class LayerDims(ctypes.Structure):
 LAYER_ROPE_READY = 1  # tg_layer_dims.flags: the workspace already holds this RoPE table
 LAYER_NORMS_FOLDED = 2  # norm weights folded into wq/wk/wv and wg/wu: RMSNorms fused into the GEMMs
 LAYER_INPUT_SSQ = 4  # with NORMS_FOLDED: the workspace holds x_in's row sums of squares
+LAYER_ATTN_ONLY = 8  # the attention half only: x_out = the post-attention residual
+LAYER_FFN_ONLY = 16  # the FFN half only: x_in is the post-attention residual
 
 
 class LayerWsLayout(ctypes.Structure):
@@ -125,6 +128,13 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tg_gated_prefill.restype = i32
+    L.tg_full_prefill_workspace_size.argtypes = [ctypes.POINTER(LayerDims), i32, i64, i64, i32, i32, i32]
+    L.tg_full_prefill_workspace_size.restype = sz
+    L.tg_full_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, ctypes.POINTER(GateWeights),
+                                  ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerWeights),
+                                  ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
+                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tg_full_prefill.restype = i32
     L.tg_fold_norm_weights.argtypes = [vp, vp, i64, i32, i32, vp]
     L.tg_fold_norm_weights.restype = i32
     _lib = L
@@ -330,6 +340,35 @@ def gated_prefill(h, keep_mask, cu_in, cu_kept, T: int, max_n: int, max_k: int, 
     return x
 
 
+def full_prefill(h, pos, keep_mask, cu_in, cu_kept, T: int, max_n: int, max_k: int, W1, b1, w2, b2,
+                 below, gate_layer, above, dims: LayerDims, x_full, kcache_full, vcache_full, s, kept,
+                 status, x, pos_c, s_c, kcache, vcache, ws=None, norms_folded=False):
+    """The three-stage prefill in one native call (tg_full_prefill): the layers
+    ``below`` and ``gate_layer``'s attention on every row of h, the scorer on
+    that residual, selection with compaction, ``gate_layer``'s FFN and the
+    layers ``above`` on the kept rows. All outputs are caller-allocated; returns x."""
+    B = cu_in.numel() - 1
+    T_in = h.shape[0]
+    if norms_folded:
+        dims = LayerDims(*[getattr(dims, f) for f, _ in LayerDims._fields_])
+        dims.flags |= LAYER_NORMS_FOLDED
+    H1 = W1.shape[0]
+    need = lib().tg_full_prefill_workspace_size(ctypes.byref(dims), H1, T_in, T, B, max_n, max_k)
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(need, h.device)
+    gate = GateWeights(_p(W1), _p(b1), _p(w2), _p(b2), H1)
+    nb, na = len(below), len(above)
+    arr_b = (LayerWeights * max(nb, 1))(*[l.c for l in below])
+    arr_a = (LayerWeights * max(na, 1))(*[l.c for l in above])
+    gl = gate_layer.c
+    _check(lib().tg_full_prefill(_p(h), _p(pos), _p(keep_mask), _p(cu_in), _p(cu_kept), B, T_in, T, max_n,
+                                 max_k, ctypes.byref(gate), arr_b, nb, ctypes.byref(gl), arr_a, na,
+                                 ctypes.byref(dims), _p(x_full), _p(kcache_full), _p(vcache_full), _p(s),
+                                 _p(kept), _p(status), _p(x), _p(pos_c), _p(s_c), _p(kcache), _p(vcache),
+                                 _p(ws), ws.numel(), _stream()), "tg_full_prefill")
+    return x
+
+
 def fold_norm_weights(norm_w: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
     """W[r, c] *= norm_w[c] in place (fp32 product rounded to W's dtype); returns W."""
     if W.dim() != 2 or norm_w.numel() != W.shape[1] or norm_w.dtype != W.dtype:
@@ -341,16 +380,20 @@ def fold_norm_weights(norm_w: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
 
 def upper_layer_fwd(w: UpperLayerWeights, dims: LayerDims, x_in, pos_c, s_c, cu_kept, max_k: int,
                     x_out=None, kcache=None, vcache=None, ws=None, events=None, rope_ready=False,
-                    norms_folded=False, input_ssq=False):
+                    norms_folded=False, input_ssq=False, attn_only=False, ffn_only=False):
     """One upper layer. ``events``: optional ctypes array of LAYER_STAGES + 1
     hipEvent_t handles; when given, the instrumented entry point records them
     between the layer's stages. ``rope_ready``: ``ws`` already holds the RoPE
     table of these positions (an earlier layer of the same stack ran on it).
     ``norms_folded``: the weights went through fold_norm_weights and the RMSNorms
     run fused into the GEMMs; ``input_ssq``: ``ws`` holds x_in's row sums of
-    squares from the previous folded layer of the stack."""
+    squares from the previous folded layer of the stack. ``attn_only``: the
+    attention half only (x_out = the post-attention residual); ``ffn_only``:
+    the FFN half only (x_in is that residual; no K/V, positions or scores are
+    read and none of kcache / vcache is written)."""
     flags = (LAYER_ROPE_READY if rope_ready else 0) | (LAYER_NORMS_FOLDED if norms_folded else 0) | \
-        (LAYER_INPUT_SSQ if input_ssq else 0)
+        (LAYER_INPUT_SSQ if input_ssq else 0) | (LAYER_ATTN_ONLY if attn_only else 0) | \
+        (LAYER_FFN_ONLY if ffn_only else 0)
     if (rope_ready or input_ssq) and ws is None:
         raise ValueError("rope_ready / input_ssq need the workspace that holds the table / sums")
     if flags:
@@ -361,9 +404,9 @@ def upper_layer_fwd(w: UpperLayerWeights, dims: LayerDims, x_in, pos_c, s_c, cu_
     dev = x_in.device
     if x_out is None:
         x_out = torch.empty_like(x_in)
-    if kcache is None:
+    if kcache is None and not ffn_only:
         kcache = torch.empty((T, dims.Hkv, dims.d), dtype=x_in.dtype, device=dev)
-    if vcache is None:
+    if vcache is None and not ffn_only:
         vcache = torch.empty((T, dims.Hkv, dims.d), dtype=x_in.dtype, device=dev)
     need = lib().tg_upper_layer_workspace_size(ctypes.byref(dims), T, B, max_k)
     if ws is None or ws.numel() < need:

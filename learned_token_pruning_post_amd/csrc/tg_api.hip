@@ -1,6 +1,7 @@
 // C ABI of libtokengate: host-side validation, workspace carving and kernel
 // launches. Arguments are checked before any HIP call, so argument errors
 // come back synchronously with nothing enqueued.
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstring>
@@ -52,9 +53,12 @@ inline bool fits32(int64_t rows, int64_t row_elems, int64_t elt = 2) {
   } while (0)
 
 bool layer_dims_ok(const tg_layer_dims* dm) {
+  constexpr int known = TG_LAYER_ROPE_READY | TG_LAYER_NORMS_FOLDED | TG_LAYER_INPUT_SSQ |
+                        TG_LAYER_ATTN_ONLY | TG_LAYER_FFN_ONLY;
+  const bool halves = (dm->flags & TG_LAYER_ATTN_ONLY) && (dm->flags & TG_LAYER_FFN_ONLY);
   return dm->D > 0 && dm->Hq > 0 && dm->Hkv > 0 && dm->d > 0 && dm->I > 0 &&
          dm->Hq % dm->Hkv == 0 && dm->rms_eps >= 0.f && dm->rope_base > 0.f &&
-         (dm->flags & ~(TG_LAYER_ROPE_READY | TG_LAYER_NORMS_FOLDED | TG_LAYER_INPUT_SSQ)) == 0 &&
+         (dm->flags & ~known) == 0 && !halves &&
          (!(dm->flags & TG_LAYER_INPUT_SSQ) || (dm->flags & TG_LAYER_NORMS_FOLDED));
 }
 
@@ -336,18 +340,21 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   tg_status st = layer_dims_supported(dm);
   if (st != TG_OK) return st;
   if (T == 0 || B == 0) return TG_OK;
-  TG_CHECK(max_k > 0, TG_ERR_INVALID_ARG);
+  const bool fused = (dm->flags & TG_LAYER_NORMS_FOLDED) != 0;
+  const bool attn_half = !(dm->flags & TG_LAYER_FFN_ONLY);  // stages 0-4
+  const bool ffn_half = !(dm->flags & TG_LAYER_ATTN_ONLY);  // stages 5-7
+  TG_CHECK(!attn_half || max_k > 0, TG_ERR_INVALID_ARG);
   if (dm->dtype == TG_BF16) {  // activations and weights of every GEMM, one sequence's K/V
     const int64_t qd = (int64_t)dm->Hq * dm->d, kvd = (int64_t)dm->Hkv * dm->d;
     TG_CHECK(fits32(T, dm->D) && fits32(T, qd) && fits32(T, dm->I) && fits32(qd, dm->D) &&
                  fits32(dm->I, dm->D) && fits32(max_k, kvd),
              TG_ERR_UNSUPPORTED);
   }
-  const bool fused = (dm->flags & TG_LAYER_NORMS_FOLDED) != 0;
-  TG_CHECK(w->wq && w->wk && w->wv && w->wo && w->wg && w->wu && w->wd && w->t && w->g,
-           TG_ERR_INVALID_ARG);
-  TG_CHECK(fused || (w->attn_norm && w->ffn_norm), TG_ERR_INVALID_ARG);
-  TG_CHECK(x_in && x_out && pos_c && s_c && d_cu_kept && kcache && vcache, TG_ERR_INVALID_ARG);
+  TG_CHECK(!attn_half || (w->wq && w->wk && w->wv && w->wo && w->t && w->g), TG_ERR_INVALID_ARG);
+  TG_CHECK(!ffn_half || (w->wg && w->wu && w->wd), TG_ERR_INVALID_ARG);
+  TG_CHECK(fused || ((!attn_half || w->attn_norm) && (!ffn_half || w->ffn_norm)), TG_ERR_INVALID_ARG);
+  TG_CHECK(x_in && x_out, TG_ERR_INVALID_ARG);
+  TG_CHECK(!attn_half || (pos_c && s_c && d_cu_kept && kcache && vcache), TG_ERR_INVALID_ARG);
   tg_layer_ws_layout L;
   st = tg_upper_layer_ws_layout(dm, T, &L);
   if (st != TG_OK) return st;
@@ -359,54 +366,70 @@ static tg_status upper_layer_impl(const tg_layer_weights* w, const tg_layer_dims
   void* norm = base + L.norm;
   void* qb = base + L.q;
   void* attn = base + L.attn;
-  void* x1 = base + L.x1;
   void* act = base + L.act;
   float* rope = (float*)(base + L.rope);
   float* ssq_x = (float*)(base + L.ssq);                   // x_in, then x_out
   float* ssq_x1 = ssq_x + (size_t)T * (size_t)(dm->D / 64);  // x1
+  // the post-attention residual: the workspace's x1 for a whole layer, the
+  // output of an attention half, the input of an FFN half
+  void* x1 = attn_half ? (ffn_half ? (void*)(base + L.x1) : x_out) : const_cast<void*>(x_in);
   const int M = (int)T;
   const int D = dm->D, Hq = dm->Hq, Hkv = dm->Hkv, d = dm->d, I = dm->I;
   const bool bf = dm->dtype == TG_BF16;
 
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
-  TG_LAUNCH(mark(0));
-  if (!(dm->flags & TG_LAYER_ROPE_READY))
-    TG_LAUNCH(tg::launch_rope_table(pos_c, T, d, dm->rope_base, rope, stream));
-  TG_LAUNCH(mark(1));
-  if (!fused)
-    TG_LAUNCH(tg::launch_rmsnorm(x_in, w->attn_norm, norm, T, D, dm->rms_eps, bf, stream));
-  else if (!(dm->flags & TG_LAYER_INPUT_SSQ))
-    TG_LAUNCH(tg::launch_row_ssq(x_in, ssq_x, T, D, stream));
-  TG_LAUNCH(mark(2));
-  if (bf) {
-    tg::QkvOut qo{(bf16*)qb, (bf16*)kcache, (bf16*)vcache, rope, Hq, Hkv, d};
-    TG_LAUNCH(tg::gemm_bf16_qkv((const bf16*)(fused ? x_in : norm), (const bf16*)w->wq,
-                                (const bf16*)w->wk, (const bf16*)w->wv, qo, M, D, stream,
-                                fused ? ssq_x : nullptr, dm->rms_eps));
+  if (attn_half) {
+    TG_LAUNCH(mark(0));
+    if (!(dm->flags & TG_LAYER_ROPE_READY))
+      TG_LAUNCH(tg::launch_rope_table(pos_c, T, d, dm->rope_base, rope, stream));
+    TG_LAUNCH(mark(1));
+    if (!fused)
+      TG_LAUNCH(tg::launch_rmsnorm(x_in, w->attn_norm, norm, T, D, dm->rms_eps, bf, stream));
+    else if (!(dm->flags & TG_LAYER_INPUT_SSQ))
+      TG_LAUNCH(tg::launch_row_ssq(x_in, ssq_x, T, D, stream));
+    TG_LAUNCH(mark(2));
+    if (bf) {
+      tg::QkvOut qo{(bf16*)qb, (bf16*)kcache, (bf16*)vcache, rope, Hq, Hkv, d};
+      TG_LAUNCH(tg::gemm_bf16_qkv((const bf16*)(fused ? x_in : norm), (const bf16*)w->wq,
+                                  (const bf16*)w->wk, (const bf16*)w->wv, qo, M, D, stream,
+                                  fused ? ssq_x : nullptr, dm->rms_eps));
+    } else {
+      float* raw = (float*)(base + L.rope + align_up((size_t)T * d * sizeof(float)));
+      const int ldr = (Hq + 2 * Hkv) * d;
+      TG_LAUNCH(tg::gemm_f32((const float*)norm, (const float*)w->wq, nullptr, raw, M, Hq * d, D, ldr, stream));
+      TG_LAUNCH(tg::gemm_f32((const float*)norm, (const float*)w->wk, nullptr, raw + Hq * d, M,
+                             Hkv * d, D, ldr, stream));
+      TG_LAUNCH(tg::gemm_f32((const float*)norm, (const float*)w->wv, nullptr,
+                             raw + (Hq + Hkv) * d, M, Hkv * d, D, ldr, stream));
+      TG_LAUNCH(tg::qkv_split_rope_f32(raw, rope, (float*)qb, (float*)kcache, (float*)vcache, T, Hq,
+                                       Hkv, d, stream));
+    }
+    TG_LAUNCH(mark(3));
+    TG_LAUNCH(tg::attn_fwd(qb, kcache, vcache, s_c, w->t, w->g, d_cu_kept, B, max_k, Hq, Hkv, d, bf,
+                           attn, nullptr, stream));
+    TG_LAUNCH(mark(4));
+    // the residual is read and the output written element by element by the
+    // same thread, so x1 may be x_in (an attention half in place)
+    if (bf) {
+      TG_LAUNCH(tg::gemm_bf16_plain((const bf16*)attn, (const bf16*)w->wo, (const bf16*)x_in,
+                                    (bf16*)x1, M, D, Hq * d, stream,
+                                    fused && ffn_half ? ssq_x1 : nullptr));
+    } else {
+      TG_LAUNCH(tg::gemm_f32((const float*)attn, (const float*)w->wo, (const float*)x_in, (float*)x1,
+                             M, D, Hq * d, D, stream));
+    }
   } else {
-    float* raw = (float*)(base + L.rope + align_up((size_t)T * d * sizeof(float)));
-    const int ldr = (Hq + 2 * Hkv) * d;
-    TG_LAUNCH(tg::gemm_f32((const float*)norm, (const float*)w->wq, nullptr, raw, M, Hq * d, D, ldr, stream));
-    TG_LAUNCH(tg::gemm_f32((const float*)norm, (const float*)w->wk, nullptr, raw + Hq * d, M,
-                           Hkv * d, D, ldr, stream));
-    TG_LAUNCH(tg::gemm_f32((const float*)norm, (const float*)w->wv, nullptr,
-                           raw + (Hq + Hkv) * d, M, Hkv * d, D, ldr, stream));
-    TG_LAUNCH(tg::qkv_split_rope_f32(raw, rope, (float*)qb, (float*)kcache, (float*)vcache, T, Hq,
-                                     Hkv, d, stream));
-  }
-  TG_LAUNCH(mark(3));
-  TG_LAUNCH(tg::attn_fwd(qb, kcache, vcache, s_c, w->t, w->g, d_cu_kept, B, max_k, Hq, Hkv, d, bf,
-                         attn, nullptr, stream));
-  TG_LAUNCH(mark(4));
-  if (bf) {
-    TG_LAUNCH(tg::gemm_bf16_plain((const bf16*)attn, (const bf16*)w->wo, (const bf16*)x_in,
-                                  (bf16*)x1, M, D, Hq * d, stream, fused ? ssq_x1 : nullptr));
-  } else {
-    TG_LAUNCH(tg::gemm_f32((const float*)attn, (const float*)w->wo, (const float*)x_in, (float*)x1,
-                           M, D, Hq * d, D, stream));
+    for (int i = 0; i <= 4; ++i) TG_LAUNCH(mark(i));
   }
   TG_LAUNCH(mark(5));
-  if (!fused) TG_LAUNCH(tg::launch_rmsnorm(x1, w->ffn_norm, norm, T, D, dm->rms_eps, bf, stream));
+  if (!ffn_half) {
+    for (int i = 6; i <= 8; ++i) TG_LAUNCH(mark(i));
+    return TG_OK;
+  }
+  if (!fused)
+    TG_LAUNCH(tg::launch_rmsnorm(x1, w->ffn_norm, norm, T, D, dm->rms_eps, bf, stream));
+  else if (!attn_half)  // an FFN half: its input's sums of squares
+    TG_LAUNCH(tg::launch_row_ssq(x1, ssq_x1, T, D, stream));
   TG_LAUNCH(mark(6));
   if (bf) {
     TG_LAUNCH(tg::gemm_bf16_swiglu((const bf16*)(fused ? x1 : norm), (const bf16*)w->wg,
@@ -496,6 +519,111 @@ tg_status tg_gated_prefill(const void* h, const int32_t* pos, const uint8_t* kee
   if (st != TG_OK) return st;
   return tg_upper_layer_stack_fwd(layers, n_layers, dm, x, pos_c, s_c, d_cu_kept, B, T, max_k,
                                   kcache, vcache, ws, ws_bytes, stream);
+}
+
+size_t tg_full_prefill_workspace_size(const tg_layer_dims* dm, int H1, int64_t T_in, int64_t T,
+                                      int B, int max_n, int max_k) {
+  if (!dm || T_in < 0 || T < 0 || B < 0) return 0;
+  tg_layer_dims base = *dm;
+  base.flags &= TG_LAYER_NORMS_FOLDED;
+  size_t m = tg_gate_score_workspace_size(T_in, dm->D, H1, dm->dtype);
+  m = std::max(m, tg_upper_layer_workspace_size(&base, T_in, B, max_n));
+  m = std::max(m, tg_upper_layer_workspace_size(&base, T, B, max_k));
+  m = std::max(m, tg_topk_select_workspace_size(B, T_in, max_n));
+  // plus the plain-attention constants: t = 1 and g = 0 per head, zero scores per token
+  return align_up(m) + align_up(((size_t)2 * (size_t)std::max(dm->Hq, 0) + (size_t)T_in) * sizeof(float));
+}
+
+tg_status tg_full_prefill(const void* h, const int32_t* pos, const uint8_t* keep_mask,
+                          const int32_t* d_cu_in, const int32_t* d_cu_kept, int B, int64_t T_in,
+                          int64_t T, int max_n, int max_k, const tg_gate_weights* gate,
+                          const tg_layer_weights* below, int n_below,
+                          const tg_layer_weights* gate_layer, const tg_layer_weights* above,
+                          int n_above, const tg_layer_dims* dm, void* x_full, void* kcache_full,
+                          void* vcache_full, float* s, int32_t* kept_idx, int32_t* d_status, void* x,
+                          int32_t* pos_c, float* s_c, void* kcache, void* vcache, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  TG_CHECK(gate && dm && gate_layer && n_below >= 0 && n_above >= 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(n_below == 0 || below, TG_ERR_INVALID_ARG);
+  TG_CHECK(n_above == 0 || above, TG_ERR_INVALID_ARG);
+  TG_CHECK((dm->flags & ~TG_LAYER_NORMS_FOLDED) == 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(B >= 0 && T_in >= 0 && T_in <= INT_MAX && T >= 0 && T <= T_in && max_n >= 0 && max_k >= 0,
+           TG_ERR_INVALID_ARG);
+  if (B == 0 || T_in == 0) return TG_OK;
+  TG_CHECK(h && pos && x_full && kcache_full && vcache_full && s, TG_ERR_INVALID_ARG);
+  TG_CHECK(T == 0 || (kept_idx && x && pos_c && s_c), TG_ERR_INVALID_ARG);
+  TG_CHECK(n_above == 0 || T == 0 || (kcache && vcache), TG_ERR_INVALID_ARG);
+  const size_t need = tg_full_prefill_workspace_size(dm, gate->H1, T_in, T, B, max_n, max_k);
+  TG_CHECK(ws && ws_bytes >= need, TG_ERR_WORKSPACE);
+  TG_CHECK(dtype_ok(dm->dtype), TG_ERR_UNSUPPORTED);
+  // every layer's weights before the first launch
+  auto weights_ok = [&](const tg_layer_weights& wl) {
+    return wl.wq && wl.wk && wl.wv && wl.wo && wl.wg && wl.wu && wl.wd &&
+           ((dm->flags & TG_LAYER_NORMS_FOLDED) || (wl.attn_norm && wl.ffn_norm));
+  };
+  for (int l = 0; l < n_below; ++l) TG_CHECK(weights_ok(below[l]), TG_ERR_INVALID_ARG);
+  TG_CHECK(weights_ok(*gate_layer), TG_ERR_INVALID_ARG);
+  for (int l = 0; l < n_above; ++l) TG_CHECK(weights_ok(above[l]) && above[l].t && above[l].g, TG_ERR_INVALID_ARG);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+
+  // plain attention below the gate and in layer L: t = 1, g = 0 (the layers'
+  // own t and g are not used), zero scores; kept at the end of the workspace,
+  // past what every stage uses
+  const size_t stage_ws = need - align_up(((size_t)2 * dm->Hq + (size_t)T_in) * sizeof(float));
+  float* plain = (float*)((char*)ws + stage_ws);
+  TG_LAUNCH(tg::launch_fill_f32(plain, dm->Hq, 1.f, stream));
+  TG_LAUNCH(tg::launch_fill_f32(plain + dm->Hq, (int64_t)dm->Hq + T_in, 0.f, stream));
+  auto plain_weights = [&](const tg_layer_weights& wl) {
+    tg_layer_weights p = wl;
+    p.t = plain;
+    p.g = plain + dm->Hq;
+    return p;
+  };
+  const float* zero_s = plain + 2 * dm->Hq;
+  const bool fused = (dm->flags & TG_LAYER_NORMS_FOLDED) != 0;
+  const size_t elt = elt_size(dm->dtype);
+  const size_t cache_full = (size_t)T_in * (size_t)dm->Hkv * (size_t)dm->d * elt;
+  // ---- layers below the gate on every token ----
+  for (int l = 0; l < n_below; ++l) {
+    tg_layer_dims dl = *dm;
+    if (l > 0) dl.flags |= TG_LAYER_ROPE_READY | (fused ? TG_LAYER_INPUT_SSQ : 0);
+    const tg_layer_weights wl = plain_weights(below[l]);
+    tg_status st = upper_layer_impl(&wl, &dl, l == 0 ? h : x_full, x_full, pos, zero_s, d_cu_in, B,
+                                    T_in, max_n, (char*)kcache_full + l * cache_full,
+                                    (char*)vcache_full + l * cache_full, ws, stage_ws, stream, nullptr);
+    if (st != TG_OK) return st;
+  }
+  // ---- layer L's attention on every token: x_full = its post-attention residual ----
+  {
+    tg_layer_dims dl = *dm;
+    dl.flags |= TG_LAYER_ATTN_ONLY;
+    if (n_below > 0) dl.flags |= TG_LAYER_ROPE_READY | (fused ? TG_LAYER_INPUT_SSQ : 0);
+    const tg_layer_weights wl = plain_weights(*gate_layer);
+    tg_status st = upper_layer_impl(&wl, &dl, n_below > 0 ? x_full : h, x_full, pos, zero_s, d_cu_in,
+                                    B, T_in, max_n, (char*)kcache_full + n_below * cache_full,
+                                    (char*)vcache_full + n_below * cache_full, ws, stage_ws, stream,
+                                    nullptr);
+    if (st != TG_OK) return st;
+  }
+  // ---- the gate: scores, selection, compaction of the residual rows ----
+  tg_status st = tg_gate_score(x_full, T_in, dm->D, gate->H1, gate->W1, gate->b1, gate->w2, gate->b2,
+                               dm->dtype, s, ws, stage_ws, stream);
+  if (st != TG_OK) return st;
+  st = tg_select_compact(s, keep_mask, d_cu_in, d_cu_kept, B, T_in, T, max_n, x_full, pos, dm->D,
+                         dm->dtype, kept_idx, d_status, x, pos_c, s_c, ws, stage_ws, stream);
+  if (st != TG_OK) return st;
+  if (T == 0) return TG_OK;
+  // ---- layer L's FFN on the kept rows, then the layers above ----
+  {
+    tg_layer_dims dl = *dm;
+    dl.flags |= TG_LAYER_FFN_ONLY;
+    st = upper_layer_impl(gate_layer, &dl, x, x, pos_c, s_c, d_cu_kept, B, T, max_k, nullptr, nullptr,
+                          ws, stage_ws, stream, nullptr);
+    if (st != TG_OK) return st;
+  }
+  return tg_upper_layer_stack_fwd(above, n_above, dm, x, pos_c, s_c, d_cu_kept, B, T, max_k, kcache,
+                                  vcache, ws, stage_ws, stream);
 }
 
 tg_status tg_upper_layer_fwd_timed(const tg_layer_weights* w, const tg_layer_dims* dm,

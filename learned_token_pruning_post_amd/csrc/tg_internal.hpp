@@ -68,6 +68,9 @@ hipError_t launch_row_ssq(const void* x, float* ssq, int64_t rows, int D, hipStr
 hipError_t launch_fold_norm(const void* w, void* W, int64_t rows, int cols, bool is_bf16,
                             hipStream_t stream);
 
+// p[i] = v for i < n
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+
 // cos/sin table [T, d] fp32: [.., i] = cos(pos*base^(-2i/d)), [.., d/2 + i] = sin(..)
 hipError_t launch_rope_table(const int32_t* pos, int64_t T, int d, float base, float* table,
                              hipStream_t stream);

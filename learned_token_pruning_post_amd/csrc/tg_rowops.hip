@@ -1,4 +1,6 @@
 // Row-parallel HBM-bound kernels: compaction gather, RMSNorm, RoPE table.
+#include <algorithm>
+
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
 
@@ -320,6 +322,20 @@ hipError_t launch_fold_norm(const void* w, void* W, int64_t rows, int cols, bool
   else
     hipLaunchKernelGGL(fold_norm_kernel<float>, grid, dim3(256), 0, stream, (const float*)w,
                        (float*)W, n, cols);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// p[i] = v for i < n (workspace constants; a kernel, so it captures into a graph)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, v);
   return hipGetLastError();
 }
 

@@ -236,9 +236,12 @@ def test_layer_layout_and_errors(L):
     assert f(*args(_dims(Hq=6, Hkv=4), 1 << 40)) == INVALID
     assert f(*args(_dims(D=200), 1 << 40)) == UNSUP  # bf16 needs D % 64 == 0
     bad_flags = _dims()
-    bad_flags.flags = 8  # TG_LAYER_ROPE_READY | NORMS_FOLDED | INPUT_SSQ are the defined bits
+    bad_flags.flags = 32  # bits 1, 2, 4, 8 and 16 are the defined ones
     assert f(*args(bad_flags, 1 << 40)) == INVALID
     assert L.tg_upper_layer_ws_layout(ctypes.byref(bad_flags), 1000, ctypes.byref(lay)) == INVALID
+    both_halves = _dims()
+    both_halves.flags = tg.LAYER_ATTN_ONLY | tg.LAYER_FFN_ONLY
+    assert f(*args(both_halves, 1 << 40)) == INVALID
     ssq_alone = _dims()
     ssq_alone.flags = tg.LAYER_INPUT_SSQ  # needs NORMS_FOLDED
     assert f(*args(ssq_alone, 1 << 40)) == INVALID
@@ -258,3 +261,35 @@ def test_layer_layout_and_errors(L):
     lay32 = tg.LayerWsLayout()
     assert L.tg_upper_layer_ws_layout(ctypes.byref(_dims(dtype=0)), 1000, ctypes.byref(lay32)) == OK
     assert lay32.total > lay32.rope + 1000 * 64 * 4
+
+
+def test_full_prefill_argument_errors(L):
+    """The three-stage prefill validates every stage's arguments before the
+    first launch (FAKE pointers are never dereferenced)."""
+    dm = _dims()
+    w = tg.LayerWeights(*([0x100000] * 11))
+    gate = tg.GateWeights(FAKE, FAKE, FAKE, FAKE, 64)
+    arr = (tg.LayerWeights * 1)(w)
+    need = L.tg_full_prefill_workspace_size(ctypes.byref(dm), 64, 1000, 100, 1, 1000, 100)
+    assert need >= L.tg_upper_layer_workspace_size(ctypes.byref(dm), 1000, 1, 1000)
+    f = L.tg_full_prefill
+
+    def call(**k):
+        return f(FAKE, k.get("pos", FAKE), None, FAKE, FAKE, 1, 1000, k.get("T", 100), 1000, 100,
+                 ctypes.byref(gate), arr, k.get("nb", 1), ctypes.byref(w), arr, 1, ctypes.byref(k.get("dm", dm)),
+                 FAKE, FAKE, FAKE, FAKE, FAKE, None, k.get("x", FAKE), FAKE, FAKE, FAKE, FAKE,
+                 k.get("ws", FAKE), k.get("wsb", need), None)
+    assert call(T=1001) == INVALID        # more kept than tokens
+    assert call(x=None) == INVALID        # kept rows need an output
+    assert call(pos=None) == INVALID      # positions are required
+    assert call(nb=-1) == INVALID
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == WS
+    bad = _dims()
+    bad.flags = tg.LAYER_ROPE_READY       # only NORMS_FOLDED may be set
+    assert call(dm=bad) == INVALID
+    nul = tg.LayerWeights(*([0x100000] * 6), None, *([0x100000] * 4))  # wg missing
+    arr_bad = (tg.LayerWeights * 1)(nul)
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 1, 1000, 100, 1000, 100, ctypes.byref(gate), arr_bad, 1,
+             ctypes.byref(w), arr, 1, ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+             FAKE, FAKE, FAKE, FAKE, need, None) == INVALID

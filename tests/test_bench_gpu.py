@@ -49,6 +49,10 @@ def test_bench_json_line_small_workload():
     mem = d["memory"]
     assert mem["peak_gb_one_layer_unpruned"] > mem["peak_gb_one_layer_pruned"] > 0
     assert mem["kv_cache_gb_27_layers_unpruned"] == pytest.approx(8 * mem["kv_cache_gb_27_layers_pruned"], rel=1e-2)
+    # the whole-model prefill against the same model run unpruned
+    pf = d["prefill_vs_unpruned"]
+    assert pf["layers"] == 28 and pf["gate_layer"] == 1 and pf["n_kept_tokens"] == 1024
+    assert pf["pruned_ms"] > 0 and pf["speedup"] > 1 and pf["peak_gb_unpruned"] > pf["peak_gb_pruned"] > 0
     # the graph replay of the same step takes about as long as the eager step
     g = d["ms_per_step_hip_graph"]
     assert g is not None and 0.5 * d["ms_per_step"] < g < 1.5 * d["ms_per_step"]
