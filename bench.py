@@ -459,9 +459,10 @@ def main():
     }
     kbytes = {
         "gate_score": w.T_in * D * elt + 4.0 * w.T_in + H1 * D * elt,
-        # selection (scores, mask, kept indices out) + compaction (rows in and
-        # out, positions and scores out; the kept indices are not read back)
-        "select_compact": 5.0 * w.T_in + 4.0 * T + 4.0 * T + 2.0 * T * D * elt + 4.0 * T + 8.0 * T,
+        # selection (scores and mask bytes in, kept indices out) + compaction (rows
+        # in and out, positions out, scores gathered in and out; the kept indices
+        # are not read back)
+        "select_compact": 5.0 * w.T_in + 4.0 * T + 2.0 * T * D * elt + 4.0 * T + 8.0 * T,
         "rope_table": 4.0 * T + 4.0 * T * d,
     }
     if not dw.norms_folded:  # fused: stage 1 is x_in's sums of squares (first layer), stage 5 empty

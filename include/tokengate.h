@@ -64,7 +64,12 @@ typedef int tg_status;
 #define TG_DEV_NAN_SCORE        4 /* a score of b is NaN (informational; NaN ranks lowest) */
 #define TG_DEV_LEN_GT_MAX_N     8 /* N_b > max_n passed by the host: kept slots of b are -1 */
 
-typedef enum tg_dtype { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+/* Element type of activations and weights. A plain 32-bit integer (not an
+ * enum) so that any value a caller passes is well defined inside the library,
+ * which refuses codes other than these with TG_ERR_UNSUPPORTED. */
+typedef int32_t tg_dtype;
+#define TG_F32  0
+#define TG_BF16 1
 
 /* Text for a status code (static storage; never NULL). */
 const char* tg_status_string(tg_status s);

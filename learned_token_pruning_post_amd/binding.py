@@ -15,7 +15,9 @@ from typing import Dict, Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtokengate.so")
+# TG_LIBRARY names another build of the same library to load instead (the
+# host-side sanitizer build of build.py --sanitize); by default the in-tree one
+LIB_PATH = os.environ.get("TG_LIBRARY") or os.path.join(_HERE, "libtokengate.so")
 
 TG_F32 = 0
 TG_BF16 = 1

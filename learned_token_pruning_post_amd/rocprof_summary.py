@@ -111,8 +111,22 @@ def _per_dispatch(pmc_csv, counter, match, largest=False):
 
 
 def traffic(fetch_csv, write_csv, kernel, copy_bytes, stage=None):
-    f_kib, f_n, name = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
-    w_kib, w_n, _ = _per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    """`kernel`: one name substring, or a list of them for a stage made of
+    several kernels (their per-dispatch figures are summed: one pass of the
+    stage launches each of them once)."""
+    kernels = [kernel] if isinstance(kernel, str) else list(kernel)
+    f_kib = w_kib = 0.0
+    f_n, w_n, names = [], [], []
+    for k in kernels:
+        fk, fn, name = _per_dispatch(fetch_csv, "FETCH_SIZE", k)
+        wk, wn, _ = _per_dispatch(write_csv, "WRITE_SIZE", k)
+        f_kib += fk
+        w_kib += wk
+        f_n.append(fn)
+        w_n.append(wn)
+        names.append(name)
+    name = " + ".join(names)
+    kernel = "+".join(kernels)
     cf_kib, _, _ = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL, largest=True)
     cw_kib, _, _ = _per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL, largest=True)
     f_factor = cf_kib * 1024.0 / copy_bytes   # counter KiB per true KiB
@@ -120,7 +134,8 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, stage=None):
     fetch_b = f_kib * 1024.0 / f_factor
     write_b = w_kib * 1024.0 / w_factor
     return {
-        "kernel_match": kernel, "kernel_name": name, "dispatches": [f_n, w_n],
+        "kernel_match": kernel, "kernel_name": name,
+        "dispatches": [f_n[0], w_n[0]] if len(kernels) == 1 else [f_n, w_n],
         "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
         "copy_bytes": copy_bytes, "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
         "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
@@ -139,7 +154,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, action="append",
+                   help="kernel name substring; repeat for a stage made of several kernels")
     t.add_argument("--stage", required=True, help="bench.py stage name of the kernel")
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--cmd", required=True, help="the two commands, separated by ' ; '")
@@ -148,7 +164,7 @@ def main(argv=None):
     if a.cmd_name == "stats":
         print("# %s\n\nCommand:\n\n```\n%s\n```\n\n%s" % (a.title, a.cmd, stats_table(a.csv)))
         return
-    res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes, a.stage)
+    res = traffic(a.fetch, a.write, a.kernel if len(a.kernel) > 1 else a.kernel[0], a.copy_bytes, a.stage)
     res["stage"] = a.stage
     res["command"] = a.cmd
     with open(a.out + ".json", "w") as fh:

@@ -46,6 +46,21 @@ def test_traffic_scales_by_the_calibration_copy(tmp_path):
     assert R.source_hash("gated_attn") != R.source_hash("gate_up_swiglu") != R.source_hash()
 
 
+def test_traffic_of_a_stage_sums_its_kernels(tmp_path):
+    copy = 1 << 20
+    fetch = [("__amd_rocclr_copyBuffer", copy / 1024 * 0.5), ("chunk_k<4>", 10.0), ("chunk_k<4>", 30.0),
+             ("emit_k<4, true>", 100.0), ("emit_k<4, true>", 100.0)]
+    write = [("__amd_rocclr_copyBuffer", copy / 1024 * 1.0), ("chunk_k<4>", 5.0), ("chunk_k<4>", 5.0),
+             ("emit_k<4, true>", 50.0), ("emit_k<4, true>", 70.0)]
+    _pmc(str(tmp_path / "f"), "FETCH_SIZE", fetch)
+    _pmc(str(tmp_path / "w"), "WRITE_SIZE", write)
+    res = R.traffic(str(tmp_path / "f"), str(tmp_path / "w"), ["chunk_k", "emit_k"], copy, "select_compact")
+    assert res["fetch_kib_per_dispatch"] == pytest.approx(20.0 + 100.0)
+    assert res["write_kib_per_dispatch"] == pytest.approx(5.0 + 60.0)
+    assert res["fetch_bytes"] == round(120.0 * 1024 / 0.5) and res["write_bytes"] == round(65.0 * 1024)
+    assert res["dispatches"] == [[2, 2], [2, 2]] and res["kernel_match"] == "chunk_k+emit_k"
+
+
 def test_stats_table_orders_by_total(tmp_path):
     p = tmp_path / "run_kernel_stats.csv"
     with open(p, "w", newline="") as fh:
