@@ -265,6 +265,52 @@ def gated_attention(q, k, v, s_c, t, g, cu_kept, rows: Optional[Sequence[int]] =
     return o, lse
 
 
+def decode_attention(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g):
+    """One new token per sequence attending to its pruned K/V cache.
+
+    [TC] engineering section: once prefill has fixed the gate bias, decoding
+    can fold it into the attention mask and run ordinary attention over the
+    cache; [TC] early token filtering: tokens generated while decoding are
+    never gated out, so each one joins the cache. The keys of sequence b are
+    its kept prompt tokens (rows cuA[b] .. cuA[b+1]-1 of kA / vA, scores sA)
+    followed by its first lenB[b] generated tokens (rows 0 .. lenB[b]-1 of
+    kB[b] / vB[b], scores sB[b]); every one of them precedes the query, so
+    there is no causal mask. Same logit as the prefill's gated attention:
+        L_j = t_h * (q_h . k_j,h') / sqrt(d) + g_h * s_j,  h' = h // (Hq / Hkv).
+    q: [B, Hq, d]; kA, vA: [rows, Hkv, d]; kB, vB: [B, cap, Hkv, d];
+    sB: [B, cap]. Returns o [B, Hq, d] and lse [B, Hq] (natural log); a
+    sequence with no keys gives o = 0 and lse = -inf.
+    """
+    q = _f64(q)
+    kA, vA, sA = _f64(kA), _f64(vA), _f64(sA)
+    kB, vB, sB = _f64(kB), _f64(vB), _f64(sB)
+    t, g = _f64(t), _f64(g)
+    B, Hq, d = q.shape
+    Hkv = kA.shape[1] if kA.ndim == 3 else kB.shape[2]
+    grp = Hq // Hkv
+    cuA = np.asarray(cuA, dtype=np.int64)
+    lenB = np.asarray(lenB, dtype=np.int64)
+    o = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        a0, a1 = int(cuA[b]), int(cuA[b + 1])
+        nb = int(lenB[b])
+        keys = np.concatenate([kA[a0:a1], kB[b, :nb]], axis=0)      # [L, Hkv, d]
+        vals = np.concatenate([vA[a0:a1], vB[b, :nb]], axis=0)
+        s = np.concatenate([sA[a0:a1], sB[b, :nb]])
+        if keys.shape[0] == 0:
+            continue
+        for h in range(Hq):
+            hk = h // grp
+            logits = t[h] * (keys[:, hk, :] @ q[b, h]) / math.sqrt(d) + g[h] * s
+            m = logits.max()
+            p = np.exp(logits - m)
+            den = p.sum()
+            o[b, h] = (p @ vals[:, hk, :]) / den
+            lse[b, h] = m + math.log(den)
+    return o, lse
+
+
 def silu(x):
     x = _f64(x)
     return x / (1.0 + np.exp(-x))

@@ -339,6 +339,105 @@ def test_attention_large_gain_is_one_hot():
     np.testing.assert_allclose(o[7:, 0], np.broadcast_to(v[7, 0], (23, 8)), atol=1e-12)
 
 
+# ----------------------------------------------------------------------------
+# decode attention over the pruned cache
+# ----------------------------------------------------------------------------
+
+def _split_cache(k, v, s, cu, splits, cap):
+    """Put the first splits[b] keys of each sequence of a packed batch into
+    segment A (packed) and the rest into segment B ([B, cap, ...])."""
+    B = len(cu) - 1
+    Hkv, d = k.shape[1], k.shape[2]
+    rowsA = [np.arange(cu[b], cu[b] + splits[b]) for b in range(B)]
+    cuA = np.concatenate([[0], np.cumsum([len(r) for r in rowsA])])
+    idxA = np.concatenate(rowsA) if B else np.zeros(0, np.int64)
+    kB = np.zeros((B, cap, Hkv, d))
+    vB = np.zeros((B, cap, Hkv, d))
+    sB = np.zeros((B, cap))
+    lenB = np.zeros(B, np.int64)
+    for b in range(B):
+        rest = np.arange(cu[b] + splits[b], cu[b + 1])
+        lenB[b] = len(rest)
+        kB[b, :len(rest)], vB[b, :len(rest)], sB[b, :len(rest)] = k[rest], v[rest], s[rest]
+    return k[idxA], v[idxA], s[idxA], cuA, kB, vB, sB, lenB
+
+
+def test_decode_is_the_last_row_of_prefill_attention():
+    # the newest token of a sequence sees every earlier key: its decode output is
+    # the last row of the causal gated attention over the same keys, wherever the
+    # keys sit between the two cache segments
+    cu = np.array([0, 17, 18, 40, 47])
+    q, k, v, s = _qkv(21, 47, 4, 2, 8)
+    t = np.array([0.8, 1.1, 0.95, 1.2])
+    g = np.array([0.0, 1.5, 0.3, 2.0])
+    o_pf, lse_pf = O.gated_attention(q, k, v, s, t, g, cu)
+    last = cu[1:] - 1
+    n = np.diff(cu)
+    for splits in (n, np.zeros_like(n), np.array([5, 0, 22, 3]), np.array([16, 1, 1, 6])):
+        cache = _split_cache(k, v, s, cu, splits, cap=int(n.max()) + 3)
+        o, lse = O.decode_attention(q[last], *cache, t, g)
+        np.testing.assert_allclose(o, o_pf[last], atol=1e-12)
+        np.testing.assert_allclose(lse, lse_pf[:, last].T, atol=1e-12)
+
+
+def test_decode_matches_sdpa_with_additive_bias():
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, d = 3, 6, 2, 16
+    lens = [9, 1, 30]
+    cuA = np.concatenate([[0], np.cumsum(lens)])
+    kA = rng.standard_normal((cuA[-1], Hkv, d))
+    vA = rng.standard_normal((cuA[-1], Hkv, d))
+    sA = rng.random(cuA[-1])
+    kB = rng.standard_normal((B, 4, Hkv, d))
+    vB = rng.standard_normal((B, 4, Hkv, d))
+    sB = rng.random((B, 4))
+    lenB = np.array([2, 4, 0])
+    q = rng.standard_normal((B, Hq, d))
+    t = rng.uniform(0.8, 1.2, Hq)
+    g = rng.uniform(0, 2, Hq)
+    o, _ = O.decode_attention(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g)
+    grp = Hq // Hkv
+    for b in range(B):
+        kk = np.concatenate([kA[cuA[b]:cuA[b + 1]], kB[b, :lenB[b]]])
+        vv = np.concatenate([vA[cuA[b]:cuA[b + 1]], vB[b, :lenB[b]]])
+        ss = np.concatenate([sA[cuA[b]:cuA[b + 1]], sB[b, :lenB[b]]])
+        for h in range(Hq):
+            r = F.scaled_dot_product_attention(
+                torch.from_numpy(q[b, h][None, None, None]), torch.from_numpy(kk[:, h // grp][None, None]),
+                torch.from_numpy(vv[:, h // grp][None, None]),
+                attn_mask=torch.from_numpy(g[h] * ss)[None, None, None], scale=float(t[h]) / math.sqrt(d))
+            np.testing.assert_allclose(o[b, h], r[0, 0, 0].numpy(), atol=1e-12)
+
+
+def test_decode_closed_forms():
+    rng = np.random.default_rng(23)
+    Hq, Hkv, d = 2, 1, 4
+    q = rng.standard_normal((3, Hq, d))
+    kA = rng.standard_normal((1, Hkv, d))
+    vA = rng.standard_normal((1, Hkv, d))
+    kB = rng.standard_normal((3, 5, Hkv, d))
+    vB = np.broadcast_to(rng.standard_normal((1, 1, Hkv, d)), (3, 5, Hkv, d)).copy()
+    t, g = np.array([0.9, 1.3]), np.array([0.5, 1.5])
+    sA, sB = np.array([0.4]), rng.random((3, 5))
+    # b=0: one key (lse = its logit, o = its value); b=1: no keys (o = 0, lse = -inf);
+    # b=2: five keys with equal values (o = that value whatever the weights)
+    o, lse = O.decode_attention(q, kA, vA, sA, np.array([0, 1, 1, 1]), kB, vB, sB, np.array([0, 0, 5]), t, g)
+    for h in range(Hq):
+        assert np.array_equal(o[0, h], vA[0, 0])
+        assert abs(lse[0, h] - (t[h] * float(q[0, h] @ kA[0, 0]) / 2.0 + g[h] * 0.4)) < 1e-12
+        assert np.all(o[1, h] == 0) and lse[1, h] == -np.inf
+        np.testing.assert_allclose(o[2, h], vB[2, 0, 0], atol=1e-12)
+    # a constant added to every score cancels; a huge gain selects the highest-scored key
+    o1, _ = O.decode_attention(q, kA, vA, sA + 0.3, np.array([0, 1, 1, 1]), kB, vB, sB + 0.3,
+                               np.array([0, 0, 5]), t, g)
+    np.testing.assert_allclose(o1, o, atol=1e-12)
+    vB2 = rng.standard_normal((3, 5, Hkv, d))
+    o2, _ = O.decode_attention(q * 1e-3, kA, vA, sA, np.array([0, 1, 1, 1]), kB, vB2, sB, np.array([0, 0, 5]),
+                               np.ones(Hq), np.full(Hq, 2000.0))
+    j = int(np.argmax(sB[2]))
+    np.testing.assert_allclose(o2[2], np.broadcast_to(vB2[2, j, 0], (Hq, d)), atol=1e-12)
+
+
 def test_attention_rows_subset_matches_full():
     cu = np.array([0, 40, 64])
     q, k, v, s = _qkv(13, 64, 4, 2, 8)
