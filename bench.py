@@ -55,6 +55,8 @@ def parse():
                     help="time only the whole step (no per-kernel events)")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the peak-memory comparison with the unpruned path")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-attention comparison over the pruned and the full cache")
     ap.add_argument("--no-prefill-time", action="store_true",
                     help="skip the whole-model prefill (all layers from layer 0) against the "
                          "same model run unpruned")
@@ -293,6 +295,65 @@ def prefill_vs_unpruned(torch, tg, dw, reps=3):
             "note": "GPU time of the decoder layers' prefill (no embedding, LM head or sampling); "
                     "peak = buffers and run on top of the resident weights (K/V of every layer "
                     "included); mean of %d runs after one warmup" % reps}
+
+
+DECODE_BATCH = 16  # sequences per decode step
+DECODE_GEN = 128   # tokens each has generated so far (segment B of its cache)
+
+
+def decode_vs_unpruned(torch, tg, w, reps=20):
+    """Decode attention of one layer for one step of DECODE_BATCH sequences:
+    each has the workload's K kept prompt tokens plus DECODE_GEN generated
+    tokens cached (tg_decode_attn_fwd, two cache segments), against the same
+    batch with all N prompt tokens cached (no pruning). Seeded random cache
+    and queries at the model's head shapes; HIP events on the launch stream
+    around `reps` calls after two warm-up calls. Bytes: K and V rows of every
+    cached key and kv head, one score per key, q in and o out."""
+    dm = w.dims
+    dt = torch.bfloat16 if dm.dtype == "bf16" else torch.float32
+    elt = 2 if dm.dtype == "bf16" else 4
+    B, Hq, Hkv, d, G = DECODE_BATCH, dm.Hq, dm.Hkv, dm.d, DECODE_GEN
+    gen = torch.Generator(device="cuda").manual_seed(1000 + w.cfg_id)
+    rnd = lambda shape: torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(dt)
+    uni = lambda shape: torch.rand(shape, generator=gen, device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+    res = {}
+    for name, n in (("pruned", w.K[0]), ("unpruned", w.N[0])):
+        kA, vA, sA = rnd((B * n, Hkv, d)), rnd((B * n, Hkv, d)), uni(B * n)
+        kB, vB, sB = rnd((B, G, Hkv, d)), rnd((B, G, Hkv, d)), uni((B, G))
+        q, t, g = rnd((B, Hq, d)), 0.8 + 0.4 * uni(Hq), 2.0 * uni(Hq)
+        cuA = torch.arange(0, B * n + 1, n, dtype=torch.int32, device="cuda")
+        lenB = torch.full((B,), G, dtype=torch.int32, device="cuda")
+        o = torch.empty_like(q)
+        status = torch.empty(B, dtype=torch.int32, device="cuda")
+        need = tg.lib().tg_decode_attn_workspace_size(B, n + G, Hq, Hkv, d, tg.dtype_code(dt))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        call = lambda: tg.decode_attn_fwd(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g, n + G, o=o,
+                                          status=status, ws=ws)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        ev.record(0, stream)
+        for _ in range(reps):
+            call()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        assert not status.any().item(), "decode status flags"
+        us = ev.ms(0, 1) / reps * 1e3
+        nbytes = 2.0 * B * (n + G) * Hkv * d * elt + 4.0 * B * (n + G) + 2.0 * B * Hq * d * elt
+        res[name] = (us, nbytes)
+        del kA, vA, sA, kB, vB, sB, q, o, ws
+    ev.close()
+    torch.cuda.empty_cache()
+    (tp, bp), (tu, bu) = res["pruned"], res["unpruned"]
+    return {"batch": B, "kept_prompt_keys": w.K[0], "prompt_keys_unpruned": w.N[0], "generated_keys": G,
+            "heads": "%d/%d x %d" % (Hq, Hkv, d), "pruned_us": round(tp, 2), "unpruned_us": round(tu, 2),
+            "speedup": round(tu / tp, 2), "pruned_bytes": bp,
+            "pruned_gbs": round(bp / (tp * 1e-6) / 1e9, 1),
+            "pruned_frac_hbm": round(bp / (tp * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "unpruned_gbs": round(bu / (tu * 1e-6) / 1e9, 1),
+            "note": "attention of one layer for one decode step; mean of %d calls after two warm-ups" % reps}
 
 
 def attention_bias_ratio(tg, torch, w, dw, gp, stream, reps=20):
@@ -586,6 +647,9 @@ def main():
     if not args.no_memory:
         print("[bench] peak memory against the unpruned path (K = N, one layer)", file=sys.stderr, flush=True)
         out["memory"] = memory_vs_unpruned(torch, tg, w)
+    if not args.no_decode:
+        print("[bench] decode attention over the pruned and the full cache", file=sys.stderr, flush=True)
+        out["decode_vs_unpruned"] = decode_vs_unpruned(torch, tg, w)
     if want_cpu:
         print("[bench] timing the CPU oracle on a bounded sample; parity on this workload",
               file=sys.stderr, flush=True)

@@ -419,6 +419,46 @@ tg_status tg_full_prefill(const void* h, const int32_t* pos, const uint8_t* keep
                           void* x, int32_t* pos_c, float* s_c, void* kcache, void* vcache,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* -------------------------------------------------------------------------
+ * Decode attention over the pruned K/V cache — [TC] engineering section:
+ * once prefill has fixed the gate bias, decoding folds it into the attention
+ * mask and runs ordinary attention over the cache; [TC] early token
+ * filtering: generated tokens are never gated out and join the cache. One
+ * new token per sequence attends to every cached key of its sequence (all of
+ * them precede it, so no causal mask) with the prefill's logit
+ *   L_j = t_h * (q_h . k_j,h') / sqrt(d) + g_h * s_j,  h' = h / (Hq / Hkv).
+ * The cache has two segments per sequence:
+ *  A: the kept prompt tokens where the prefill wrote them: kA, vA
+ *     [rows, Hkv, d] dtype (post-RoPE), sA [rows] fp32 their scores, d_cuA
+ *     [B+1] int32 (device) sequence b's rows cuA[b] .. cuA[b+1]-1 (the
+ *     prefill's d_cu_kept, kcache, vcache and s_c). Required even when empty.
+ *  B: the generated tokens: kB, vB [B, capB, Hkv, d] dtype, sB [B, capB]
+ *     fp32, d_lenB [B] int32 (device): sequence b uses rows 0 .. lenB[b]-1 of
+ *     its capB (the caller appends each new token's k, v and score before the
+ *     call that attends from it). May be NULL when capB == 0.
+ * The key scores are the caller's: the library reads sA / sB as given (the
+ * tests and the benchmark give a generated token its own scorer score, as a
+ * forced prompt token keeps its own).
+ *  q [B, Hq, d] dtype (post-RoPE at the new token's position); t, g [Hq]
+ *  fp32; max_len (host) bounds (cuA[b+1]-cuA[b]) + lenB[b] over b;
+ *  o [B, Hq, d] dtype out; lse [B, Hq] fp32 out (natural log; optional);
+ *  d_status [B] int32 out (optional): TG_DEV_LEN_GT_MAX_N when a sequence's
+ *  segment lengths are negative, lenB[b] > capB, or the total exceeds
+ *  max_len; that sequence's o and lse are then NaN. A sequence with no keys
+ *  gets o = 0, lse = -inf.
+ * Supported: d in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q, k, v and o 16-byte
+ * aligned. Workspace: tg_decode_attn_workspace_size() bytes (0 when every
+ * sequence fits one key chunk), 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t tg_decode_attn_workspace_size(int B, int max_len, int Hq, int Hkv, int d, tg_dtype dtype);
+tg_status tg_decode_attn_fwd(const void* q, const void* kA, const void* vA, const float* sA,
+                             const int32_t* d_cuA, const void* kB, const void* vB,
+                             const float* sB, const int32_t* d_lenB, int capB,
+                             const float* t, const float* g, int B, int max_len,
+                             int Hq, int Hkv, int d, tg_dtype dtype,
+                             void* o, float* lse, int32_t* d_status,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Instrumentation: exactly tg_upper_layer_fwd, and in addition records
  * events[i] on `stream` right before stage i of the layer and
  * events[TG_LAYER_STAGES] after the last one, so hipEventElapsedTime gives each

@@ -37,6 +37,7 @@ ABI_FUNCTIONS = (
     "tg_upper_layer_fwd_timed", "tg_fold_norm_weights", "tg_upper_layer_stack_fwd",
     "tg_gated_prefill_workspace_size", "tg_gated_prefill",
     "tg_full_prefill_workspace_size", "tg_full_prefill",
+    "tg_decode_attn_workspace_size", "tg_decode_attn_fwd",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -137,6 +138,11 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tg_full_prefill.restype = i32
+    L.tg_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.tg_decode_attn_workspace_size.restype = sz
+    L.tg_decode_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, vp, vp, vp, vp, sz, vp]
+    L.tg_decode_attn_fwd.restype = i32
     L.tg_fold_norm_weights.argtypes = [vp, vp, i64, i32, i32, vp]
     L.tg_fold_norm_weights.restype = i32
     _lib = L
@@ -276,6 +282,33 @@ def gated_attn_fwd(q, k, v, s_c, t, g, cu_kept, max_k: int, o=None, lse=None, wa
                                    max_k, Hq, Hkv, d, dtype_code(q.dtype), _p(o), _p(lse), None, 0,
                                    _stream()), "tg_gated_attn_fwd")
     return o, lse
+
+
+def decode_attn_fwd(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g, max_len: int, o=None, lse=None,
+                    status=None, ws=None, want_lse=False):
+    """tg_decode_attn_fwd: q [B, Hq, d]; segment A = the prefill's kept-token
+    cache (kA, vA [rows, Hkv, d], sA [rows], cuA [B+1]); segment B = generated
+    tokens (kB, vB [B, capB, Hkv, d], sB [B, capB], lenB [B]; capB may be 0).
+    Returns (o, lse, status)."""
+    B, Hq, d = q.shape
+    Hkv = kA.shape[1]
+    capB = kB.shape[1] if kB is not None else 0
+    dev = q.device
+    if o is None:
+        o = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    code = dtype_code(q.dtype)
+    need = lib().tg_decode_attn_workspace_size(B, max_len, Hq, Hkv, d, code)
+    if need and (ws is None or ws.numel() < need):
+        ws = _empty_ws(need, dev)
+    _check(lib().tg_decode_attn_fwd(_p(q), _p(kA), _p(vA), _p(sA), _p(cuA), _p(kB), _p(vB), _p(sB), _p(lenB),
+                                    capB, _p(t), _p(g), B, max_len, Hq, Hkv, d, code, _p(o), _p(lse),
+                                    _p(status), _p(ws) if need else None, ws.numel() if need else 0,
+                                    _stream()), "tg_decode_attn_fwd")
+    return o, lse, status
 
 
 def layer_dims(D, Hq, Hkv, d, I, dtype: torch.dtype, rope_base=1.0e6, rms_eps=1.0e-6) -> LayerDims:

@@ -280,6 +280,41 @@ tg_status tg_gated_attn_fwd(const void* q, const void* k, const void* v, const f
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// decode attention over the pruned cache
+// ---------------------------------------------------------------------------
+
+size_t tg_decode_attn_workspace_size(int B, int max_len, int Hq, int Hkv, int d, tg_dtype dtype) {
+  if (!dtype_ok(dtype) || B <= 0 || max_len < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+  return tg::decode_workspace_bytes(B, max_len, Hq, Hkv, d);
+}
+
+tg_status tg_decode_attn_fwd(const void* q, const void* kA, const void* vA, const float* sA,
+                             const int32_t* d_cuA, const void* kB, const void* vB, const float* sB,
+                             const int32_t* d_lenB, int capB, const float* t, const float* g, int B,
+                             int max_len, int Hq, int Hkv, int d, tg_dtype dtype, void* o, float* lse,
+                             int32_t* d_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  TG_CHECK(B >= 0 && max_len >= 0 && capB >= 0 && Hq > 0 && Hkv > 0 && d > 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(Hq % Hkv == 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(dtype_ok(dtype), TG_ERR_UNSUPPORTED);
+  TG_CHECK(tg::decode_supported(Hq, Hkv, d), TG_ERR_UNSUPPORTED);
+  // one workgroup per (sequence, kv head, chunk of at least 128 keys)
+  TG_CHECK((int64_t)B * Hkv * (((int64_t)max_len + 127) / 128) <= INT_MAX, TG_ERR_UNSUPPORTED);
+  if (B == 0) return TG_OK;
+  TG_CHECK(q && kA && vA && sA && d_cuA && d_lenB && t && g && o, TG_ERR_INVALID_ARG);
+  TG_CHECK(capB == 0 || (kB && vB && sB), TG_ERR_INVALID_ARG);
+  auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
+  TG_CHECK(a16(q) && a16(kA) && a16(vA) && a16(kB) && a16(vB) && a16(o), TG_ERR_INVALID_ARG);
+  const size_t need = tg::decode_workspace_bytes(B, max_len, Hq, Hkv, d);
+  TG_CHECK(need == 0 || (ws && ws_bytes >= need), TG_ERR_WORKSPACE);
+  TG_CHECK(need == 0 || ((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+  return launched(tg::launch_decode_attn(q, kA, vA, sA, d_cuA, kB, vB, sB, d_lenB, capB, t, g, B,
+                                         max_len, Hq, Hkv, d, dtype == TG_BF16, o, lse, d_status,
+                                         ws, stream));
+}
+
 tg_status tg_fold_norm_weights(const void* norm_w, void* W, int64_t rows, int cols,
                                tg_dtype dtype, hipStream_t stream) {
   TG_CHECK(rows >= 0 && cols >= 0, TG_ERR_INVALID_ARG);

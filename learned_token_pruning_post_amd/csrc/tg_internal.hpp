@@ -116,4 +116,13 @@ hipError_t attn_fwd(const void* q, const void* k, const void* v, const float* s_
                     const float* g, const int32_t* cu_kept, int B, int max_k, int Hq, int Hkv,
                     int d, bool is_bf16, void* o, float* lse, hipStream_t stream);
 
+// ---- decode attention over the pruned cache (two segments per sequence) ----
+bool decode_supported(int Hq, int Hkv, int d);
+size_t decode_workspace_bytes(int B, int max_len, int Hq, int Hkv, int d);
+hipError_t launch_decode_attn(const void* q, const void* kA, const void* vA, const float* sA,
+                              const int32_t* cuA, const void* kB, const void* vB, const float* sB,
+                              const int32_t* lenB, int capB, const float* t, const float* g, int B,
+                              int max_len, int Hq, int Hkv, int d, bool is_bf16, void* o, float* lse,
+                              int32_t* status, void* ws, hipStream_t stream);
+
 }  // namespace tg

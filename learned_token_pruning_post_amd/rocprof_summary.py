@@ -28,13 +28,15 @@ ROOT = os.path.dirname(PKG)
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 
 
-# the files that define each stage's kernel: its own source plus the shared device headers
-_SHARED = ["tg_common.hpp", "tg_internal.hpp"]
+# the files that define each stage's kernel: its own source plus the shared device
+# helpers (tg_internal.hpp only declares host launchers, so it is not part of a kernel)
+_SHARED = ["tg_common.hpp"]
 STAGE_SOURCES = {
     "gate_score": ["tg_gemm.hip"] + _SHARED,
     "select_compact": ["tg_select.hip"] + _SHARED,
     "topk_select": ["tg_select.hip"] + _SHARED,
     "compact": ["tg_rowops.hip"] + _SHARED,
+    "decode_attn": ["tg_decode.hip"] + _SHARED,
     "rmsnorm_attn": ["tg_rowops.hip"] + _SHARED,
     "rmsnorm_ffn": ["tg_rowops.hip"] + _SHARED,
     "rope_table": ["tg_rowops.hip"] + _SHARED,

@@ -163,6 +163,34 @@ def test_attention_argument_errors(L):
     assert f(FAKE, FAKE, None, *([FAKE] * 4), 1, 64, 8, 4, 128, 1, FAKE, None, None, 0, None) == INVALID
 
 
+def test_decode_attention_argument_errors(L):
+    """Every check fails before any launch (FAKE pointers are never dereferenced)."""
+    ws = L.tg_decode_attn_workspace_size
+    assert ws(1, 100, 16, 8, 128, 1) == 0            # one key chunk per sequence: no workspace
+    big = ws(64, 4224, 16, 8, 128, 1)
+    assert big >= 64 * 16 * 5 * (128 + 2) * 4        # partial outputs and (max, sum) per chunk
+    assert ws(64, 4224, 16, 8, 128, 7) == 0 and ws(0, 4224, 16, 8, 128, 1) == 0
+    f = L.tg_decode_attn_fwd
+
+    def call(q=FAKE, kA=FAKE, kB=FAKE, capB=8, B=64, max_len=4224, Hq=16, Hkv=8, d=128, dt=1, o=FAKE,
+             w=None, wsb=0):
+        return f(q, kA, FAKE, FAKE, FAKE, kB, FAKE, FAKE, FAKE, capB, FAKE, FAKE, B, max_len, Hq, Hkv, d, dt,
+                 o, None, None, w, wsb, None)
+    assert call(Hq=12) == INVALID                  # Hq % Hkv
+    assert call(d=96) == UNSUP                     # head dim
+    assert call(Hq=32, Hkv=2) == UNSUP             # group of 16
+    assert call(dt=7) == UNSUP                     # dtype code
+    assert call(max_len=-1) == INVALID
+    assert call(q=None) == INVALID
+    assert call(kA=None) == INVALID                # segment A is required even when empty
+    assert call(kB=None) == INVALID                # capB > 0 needs segment B
+    assert call(q=ctypes.c_void_p(0x100008)) == INVALID  # 16-byte alignment
+    assert call() == WS                            # split over chunks: workspace needed
+    assert call(w=FAKE, wsb=big - 1) == WS
+    assert call(w=ctypes.c_void_p(0x100010), wsb=big) == INVALID  # workspace alignment
+    assert call(B=0) == OK                         # nothing to do
+
+
 def test_layer_stack_argument_errors(L):
     f = L.tg_upper_layer_stack_fwd
     dm = _dims()

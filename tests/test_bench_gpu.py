@@ -53,6 +53,10 @@ def test_bench_json_line_small_workload():
     pf = d["prefill_vs_unpruned"]
     assert pf["layers"] == 28 and pf["gate_layer"] == 1 and pf["n_kept_tokens"] == 1024
     assert pf["pruned_ms"] > 0 and pf["speedup"] > 1 and pf["peak_gb_unpruned"] > pf["peak_gb_pruned"] > 0
+    # decode attention over the pruned cache against the full one
+    dec = d["decode_vs_unpruned"]
+    assert dec["kept_prompt_keys"] == 1024 and dec["prompt_keys_unpruned"] == 8192
+    assert dec["pruned_us"] > 0 and dec["speedup"] > 1 and 0 < dec["pruned_frac_hbm"] < 1
     # the graph replay of the same step takes about as long as the eager step
     g = d["ms_per_step_hip_graph"]
     assert g is not None and 0.5 * d["ms_per_step"] < g < 1.5 * d["ms_per_step"]

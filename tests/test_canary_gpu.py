@@ -209,3 +209,32 @@ def test_whole_step_and_three_stage_outputs_stay_inside_their_buffers(dtype, N, 
     assert torch.equal(o["s"], fp.s) and torch.equal(o["kept"], fp.kept) and torch.equal(o["x"], fp.x)
     if T:
         assert torch.equal(o["k"], fp.kcache[:na])
+
+
+@pytest.mark.parametrize("lens", [([37, 0, 100], [3, 1, 0]), ([3000, 0, 1, 700], [5, 0, 16, 16])])
+def test_decode_outputs_stay_inside_their_buffers(lens):
+    """Decode attention, single-chunk and split paths: o, lse, status and the
+    workspace between guard bands; outputs equal to an unguarded call."""
+    lenA, lenB = lens
+    B, Hq, Hkv, d, capB = len(lenA), 16, 8, 128, 16
+    say("canaries, decode:", lenA, lenB)
+    rows = max(sum(lenA), 1)
+    act = lambda o, shape: to_device(activations(64, o, shape, "bf16"))
+    q, kA, vA = act(1, (B, Hq, d)), act(2, (rows, Hkv, d)), act(3, (rows, Hkv, d))
+    kB, vB = act(4, (B, capB, Hkv, d)), act(5, (B, capB, Hkv, d))
+    gen = torch.Generator().manual_seed(64)
+    sA, sB = torch.rand(rows, generator=gen).cuda(), torch.rand((B, capB), generator=gen).cuda()
+    t, g = torch.rand(Hq, generator=gen).cuda() + 0.5, torch.rand(Hq, generator=gen).cuda()
+    cuA = torch.tensor([0] + list(np.cumsum(lenA)), dtype=torch.int32, device="cuda")
+    lB = torch.tensor(lenB, dtype=torch.int32, device="cuda")
+    max_len = max(a + b for a, b in zip(lenA, lenB))
+    o_ref, lse_ref, st_ref = tg.decode_attn_fwd(q, kA, vA, sA, cuA, kB, vB, sB, lB, t, g, max_len, want_lse=True)
+    lib = tg.lib()
+    o, lse = Guarded("o", (B, Hq, d), torch.bfloat16), Guarded("lse", (B, Hq), torch.float32)
+    st = Guarded("status", (B,), torch.int32)
+    ws = _ws("decode ws", lib.tg_decode_attn_workspace_size(B, max_len, Hq, Hkv, d, 1))
+    tg.decode_attn_fwd(q, kA, vA, sA, cuA, kB, vB, sB, lB, t, g, max_len, o=o.t, lse=lse.t, status=st.t,
+                       ws=ws.t if ws.nbytes else None)
+    _check_all(o, lse, st, ws)
+    assert torch.equal(o.t, o_ref) and torch.equal(lse.t, lse_ref) and torch.equal(st.t, st_ref[:B])
+
