@@ -311,6 +311,99 @@ def decode_attention(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g):
     return o, lse
 
 
+# ----------------------------------------------------------------------------
+# Backward: the gradient path from the upper attention to the scorer
+# ----------------------------------------------------------------------------
+
+def gated_attention_backward(q, k, v, s_c, t, g, cu_kept, do):
+    """Gradients of the token-gated attention with respect to q, k, v, the
+    kept tokens' scores and the per-head temperature and gain.
+
+    [TC] gradient-path section: because the scores enter the upper layers'
+    attention logits, the loss reaches the scorer through them, and the
+    per-head gain and temperature are learned with it. With the forward of
+    gated_attention (L_ij = t_h q_i.k_j / sqrt(d) + g_h s_j for j <= i,
+    P = softmax_j L, o_i = sum_j P_ij v_j) and an upstream gradient dO:
+        dv_j   = sum_i P_ij dO_i
+        dP_ij  = dO_i . v_j
+        dL_ij  = P_ij (dP_ij - sum_k P_ik dP_ik)      (softmax Jacobian)
+        dq_i   = t_h / sqrt(d) sum_j dL_ij k_j
+        dk_j   = t_h / sqrt(d) sum_i dL_ij q_i
+        ds_j   = sum_h g_h sum_i dL_ij
+        dg_h   = sum_ij dL_ij s_j,   dt_h = sum_ij dL_ij q_i.k_j / sqrt(d)
+    For GQA, dk and dv of a kv head add up over the query heads of its group.
+    Returns {"dq" [T,Hq,d], "dk" [T,Hkv,d], "dv" [T,Hkv,d], "ds" [T], "dt" [Hq], "dg" [Hq]}.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    s_c, t, g = _f64(s_c), _f64(t), _f64(g)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    grp = Hq // Hkv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    ds, dt, dg = np.zeros(T), np.zeros(Hq), np.zeros(Hq)
+    cu = np.asarray(cu_kept, dtype=np.int64)
+    rd = 1.0 / math.sqrt(d)
+    for b in range(len(cu) - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        n = hi - lo
+        if n <= 0:
+            continue
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(Hq):
+            hk = h // grp
+            qq, kk, vv, dd = q[lo:hi, h], k[lo:hi, hk], v[lo:hi, hk], do[lo:hi, h]
+            qk = qq @ kk.T * rd
+            L = np.where(causal, t[h] * qk + g[h] * s_c[lo:hi][None, :], -np.inf)
+            P = np.exp(L - L.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dv[lo:hi, hk] += P.T @ dd
+            dP = dd @ vv.T
+            dL = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[lo:hi, h] = t[h] * rd * (dL @ kk)
+            dk[lo:hi, hk] += t[h] * rd * (dL.T @ qq)
+            ds[lo:hi] += g[h] * dL.sum(axis=0)
+            dg[h] += float((dL * s_c[lo:hi][None, :]).sum())
+            dt[h] += float((dL * qk).sum())
+    return {"dq": dq, "dk": dk, "dv": dv, "ds": ds, "dt": dt, "dg": dg}
+
+
+def gelu_grad(z):
+    """d GELU(z) / dz = Phi(z) + z phi(z) for the exact (erf) GELU."""
+    z = _f64(z)
+    return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def gate_score_backward(h, W1, b1, w2, b2, ds):
+    """Gradients of the scorer s = sigmoid(w2 . GELU(W1 h + b1) + b2) given ds
+    per token ([TC] gradient-path section: the gate gives the scoring network
+    a gradient path, so it trains with the model):
+        z = W1 h + b1, a = GELU(z), u = w2.a + b2, s = sigmoid(u)
+        du = ds s (1 - s);  dw2 = sum_t du_t a_t;  db2 = sum_t du_t
+        dz = du w2 GELU'(z); dW1 = sum_t dz_t h_t^T; db1 = sum_t dz_t; dh = dz W1
+    Returns {"dh" [T,D], "dW1" [H1,D], "db1" [H1], "dw2" [H1], "db2" scalar}.
+    """
+    h, W1, b1, w2 = _f64(h), _f64(W1), _f64(b1), _f64(w2)
+    b2v = float(_f64(b2).reshape(-1)[0])
+    ds = _f64(ds)
+    z = h @ W1.T + b1[None, :]
+    a = gelu(z)
+    sv = sigmoid(a @ w2 + b2v)
+    du = ds * sv * (1.0 - sv)
+    dz = du[:, None] * w2[None, :] * gelu_grad(z)
+    return {"dh": dz @ W1, "dW1": dz.T @ h, "db1": dz.sum(axis=0), "dw2": a.T @ du,
+            "db2": float(du.sum())}
+
+
+def compact_backward(ds_c, kept_idx, T_in):
+    """Gradient of the prompt scores through the compaction: compacted row r
+    is prompt row kept_idx[r], so it carries ds_c[r] back there; a pruned
+    token's score gets none ([TC] early token filtering: pruned tokens stop
+    at layer L and never reach the layers whose attention reads the scores)."""
+    ds = np.zeros(int(T_in))
+    np.add.at(ds, np.asarray(kept_idx, dtype=np.int64), _f64(ds_c))
+    return ds
+
+
 def silu(x):
     x = _f64(x)
     return x / (1.0 + np.exp(-x))

@@ -718,3 +718,110 @@ def test_full_prefill_scores_read_layer_L_post_attention_residual():
     np.testing.assert_allclose(r["x_gate"], O.ffn_half(np.concatenate(x1)[r["kept"]], Ws[1], dm), atol=1e-11)
     assert r["kv_above"][0][0].shape[0] == 11 and r["kv_below"][1][0].shape[0] == 27
     assert np.array_equal(r["pos_c"], O.local_positions(cu_in)[r["kept"]])
+
+
+# ----------------------------------------------------------------------------
+# backward: the gradient path from the upper attention to the scorer
+# ----------------------------------------------------------------------------
+
+def _torch_gated_attention(q, k, v, s, t, g, cu):
+    """The gated attention as plain torch ops (fp64, autograd-able): GQA by
+    repeating kv heads, causal mask inside each sequence."""
+    T, Hq, d = q.shape
+    grp = Hq // k.shape[1]
+    outs = []
+    for b in range(len(cu) - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        kk = k[lo:hi].repeat_interleave(grp, dim=1).transpose(0, 1)     # [Hq, n, d]
+        vv = v[lo:hi].repeat_interleave(grp, dim=1).transpose(0, 1)
+        qq = q[lo:hi].transpose(0, 1)
+        logits = t[:, None, None] * (qq @ kk.transpose(1, 2)) / math.sqrt(d) + g[:, None, None] * s[lo:hi][None, None, :]
+        mask = torch.ones(n, n, dtype=torch.bool).tril()
+        logits = logits.masked_fill(~mask, float("-inf"))
+        outs.append((torch.softmax(logits, dim=-1) @ vv).transpose(0, 1))
+    return torch.cat(outs, dim=0)
+
+
+def _attn_bwd_case(seed, cu, Hq, Hkv, d):
+    rng = np.random.default_rng(seed)
+    T = int(cu[-1])
+    q, k, v = rng.standard_normal((T, Hq, d)), rng.standard_normal((T, Hkv, d)), rng.standard_normal((T, Hkv, d))
+    s, do = rng.random(T), rng.standard_normal((T, Hq, d))
+    t, g = rng.uniform(0.8, 1.2, Hq), rng.uniform(0.0, 2.0, Hq)
+    return q, k, v, s, t, g, do
+
+
+def test_attention_backward_matches_autograd():
+    cu = np.array([0, 23, 24, 24, 61])       # ragged, a one-token and an empty sequence
+    q, k, v, s, t, g, do = _attn_bwd_case(31, cu, 6, 2, 8)
+    r = O.gated_attention_backward(q, k, v, s, t, g, cu, do)
+    tt = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+          for n, a in (("q", q), ("k", k), ("v", v), ("s", s), ("t", t), ("g", g))}
+    o = _torch_gated_attention(tt["q"], tt["k"], tt["v"], tt["s"], tt["t"], tt["g"], cu)
+    (o * torch.from_numpy(do)).sum().backward()
+    for mine, name in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("ds", "s"), ("dt", "t"), ("dg", "g")):
+        np.testing.assert_allclose(r[mine], tt[name].grad.numpy(), atol=1e-10, err_msg=mine)
+    # the forward it differentiates is the oracle's own
+    np.testing.assert_allclose(o.detach().numpy(), O.gated_attention(q, k, v, s, t, g, cu)[0], atol=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    cu = np.array([0, 5, 9])
+    q, k, v, s, t, g, do = _attn_bwd_case(32, cu, 2, 1, 4)
+    r = O.gated_attention_backward(q, k, v, s, t, g, cu, do)
+    loss = lambda q_, k_, v_, s_, t_, g_: float((O.gated_attention(q_, k_, v_, s_, t_, g_, cu)[0] * do).sum())
+    eps = 1e-6
+
+    def fd(arr, idx, pos):
+        a1, a0 = [x.copy() for x in (q, k, v, s, t, g)], [x.copy() for x in (q, k, v, s, t, g)]
+        a1[pos][idx] += eps
+        a0[pos][idx] -= eps
+        return (loss(*a1) - loss(*a0)) / (2 * eps)
+    for name, pos, idx in (("dq", 0, (6, 1, 2)), ("dk", 1, (3, 0, 1)), ("dv", 2, (7, 0, 3)), ("ds", 3, (2,)),
+                           ("ds", 3, (8,)), ("dt", 4, (1,)), ("dg", 5, (0,))):
+        assert abs(r[name][idx] - fd(None, idx, pos)) < 1e-7, (name, idx)
+
+
+def test_scorer_backward_matches_autograd_and_differences():
+    rng = np.random.default_rng(33)
+    T, D, H1 = 19, 12, 7
+    h = rng.standard_normal((T, D))
+    W1, b1, w2, b2 = rng.standard_normal((H1, D)) * 0.5, rng.standard_normal(H1) * 0.5, rng.standard_normal(H1), \
+        rng.standard_normal(1)
+    ds = rng.standard_normal(T)
+    r = O.gate_score_backward(h, W1, b1, w2, b2, ds)
+    tt = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+          for n, a in (("h", h), ("W1", W1), ("b1", b1), ("w2", w2), ("b2", b2))}
+    z = tt["h"] @ tt["W1"].T + tt["b1"]
+    sc = torch.sigmoid(F.gelu(z, approximate="none") @ tt["w2"] + tt["b2"])
+    np.testing.assert_allclose(sc.detach().numpy(), O.gate_score(h, W1, b1, w2, b2), atol=1e-13)
+    (sc * torch.from_numpy(ds)).sum().backward()
+    for mine, name in (("dh", "h"), ("dW1", "W1"), ("db1", "b1"), ("dw2", "w2"), ("db2", "b2")):
+        np.testing.assert_allclose(np.asarray(r[mine]).reshape(tt[name].grad.shape), tt[name].grad.numpy(),
+                                   atol=1e-12, err_msg=mine)
+    # GELU' against central differences of the oracle's own GELU (catches a tanh-form derivative)
+    zz = np.linspace(-4, 4, 33)
+    np.testing.assert_allclose(O.gelu_grad(zz), (O.gelu(zz + 1e-6) - O.gelu(zz - 1e-6)) / 2e-6, atol=1e-8)
+
+
+def test_gradient_path_through_the_compaction():
+    # loss -> gated attention over the kept rows -> their scores -> the prompt scores:
+    # compact_backward of the attention's ds equals autograd through the gather
+    rng = np.random.default_rng(34)
+    cu_in, cu_k = np.array([0, 30, 50]), np.array([0, 12, 20])
+    s = rng.random(50)
+    kept, _ = O.topk_select(s, None, cu_in, cu_k)
+    q, k, v = rng.standard_normal((20, 4, 8)), rng.standard_normal((20, 2, 8)), rng.standard_normal((20, 2, 8))
+    t, g, do = rng.uniform(0.8, 1.2, 4), rng.uniform(0, 2, 4), rng.standard_normal((20, 4, 8))
+    st = torch.tensor(s, requires_grad=True)
+    o = _torch_gated_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                               st[torch.from_numpy(kept.astype(np.int64))], torch.from_numpy(t), torch.from_numpy(g), cu_k)
+    (o * torch.from_numpy(do)).sum().backward()
+    ds_c = O.gated_attention_backward(q, k, v, s[kept], t, g, cu_k, do)["ds"]
+    ds = O.compact_backward(ds_c, kept, 50)
+    np.testing.assert_allclose(ds, st.grad.numpy(), atol=1e-12)
+    pruned = np.setdiff1d(np.arange(50), kept)
+    assert np.all(ds[pruned] == 0) and np.all(ds[kept] == ds_c)
