@@ -55,6 +55,8 @@ def parse():
                     help="time only the whole step (no per-kernel events)")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the peak-memory comparison with the unpruned path")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward of the gated attention and of the scorer")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-attention comparison over the pruned and the full cache")
     ap.add_argument("--no-prefill-time", action="store_true",
@@ -295,6 +297,67 @@ def prefill_vs_unpruned(torch, tg, dw, reps=3):
             "note": "GPU time of the decoder layers' prefill (no embedding, LM head or sampling); "
                     "peak = buffers and run on top of the resident weights (K/V of every layer "
                     "included); mean of %d runs after one warmup" % reps}
+
+
+def backward_timing(torch, tg, w, reps=5):
+    """The gate's gradient path at the workload's shapes: the gated attention's
+    backward (tg_gated_attn_bwd) over one sequence of the kept-token count,
+    next to its forward, and the scorer's backward (tg_gate_score_bwd) over
+    the whole prompt. Seeded random operands; HIP events on the launch stream,
+    mean of `reps` calls after a warm-up. Algorithmic work: attention backward
+    = 2.5x the forward's matmul flops (S recomputed, dP, dV, dK, dQ); scorer
+    backward = the three products W1 h, dz W1 and dz^T h (2 T D H1 each)."""
+    dm = w.dims
+    if dm.dtype != "bf16":
+        return None
+    gen = torch.Generator(device="cuda").manual_seed(2000 + w.cfg_id)
+    rnd = lambda shape, sc=1.0: (sc * torch.randn(shape, generator=gen, device="cuda")).to(torch.bfloat16)
+    uni = lambda shape: torch.rand(shape, generator=gen, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev.record(0, stream)
+        for _ in range(reps):
+            fn()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        return ev.ms(0, 1) / reps * 1e3
+
+    K, Hq, Hkv, d = w.K[0], dm.Hq, dm.Hkv, dm.d
+    q, k, v, dO = rnd((K, Hq, d)), rnd((K, Hkv, d)), rnd((K, Hkv, d)), rnd((K, Hq, d))
+    s_c, t, g = uni(K), 0.8 + 0.4 * uni(Hq), 2.0 * uni(Hq)
+    cu = torch.tensor([0, K], dtype=torch.int32, device="cuda")
+    o, lse = tg.gated_attn_fwd(q, k, v, s_c, t, g, cu, K, want_lse=True)
+    ws = torch.empty(max(tg.lib().tg_gated_attn_bwd_workspace_size(1, K, K, Hq, Hkv, d, 1), 1), dtype=torch.uint8,
+                     device="cuda")
+    fwd_us = timed(lambda: tg.gated_attn_fwd(q, k, v, s_c, t, g, cu, K, o=o, lse=lse, want_lse=True))
+    bwd_us = timed(lambda: tg.gated_attn_bwd(q, k, v, s_c, t, g, cu, K, o, lse, dO, ws=ws))
+    attn_flop = 2.0 * d * Hq * K * (K + 1)
+    del q, k, v, dO, o, lse, ws
+    N, D, H1 = w.N[0], dm.D, dm.H1
+    h, W1, b1, w2, b2 = rnd((N, D)), rnd((H1, D), 0.02), rnd((H1,), 0.02), rnd((H1,), 0.02), rnd((1,), 0.02)
+    s = tg.gate_score(h, W1, b1, w2, b2)
+    ds = torch.randn(N, generator=gen, device="cuda")
+    ws = torch.empty(max(tg.lib().tg_gate_score_bwd_workspace_size(N, D, H1, 1), 1), dtype=torch.uint8,
+                     device="cuda")
+    sc_us = timed(lambda: tg.gate_score_bwd(h, W1, b1, w2, s, ds, ws=ws))
+    sc_flop = 3 * 2.0 * N * D * H1
+    del h, W1, ws
+    ev.close()
+    torch.cuda.empty_cache()
+    bt = 2.5 * attn_flop / (bwd_us * 1e-6) / 1e12
+    st = sc_flop / (sc_us * 1e-6) / 1e12
+    return {"attn_bwd_us": round(bwd_us, 1), "attn_fwd_us": round(fwd_us, 1),
+            "attn_bwd_over_fwd": round(bwd_us / fwd_us, 2), "attn_bwd_tflops": round(bt, 1),
+            "attn_bwd_frac_mfma_peak": round(bt / PEAK_BF16_TFLOPS, 4),
+            "scorer_bwd_us": round(sc_us, 1), "scorer_bwd_tflops": round(st, 1),
+            "scorer_bwd_frac_mfma_peak": round(st / PEAK_BF16_TFLOPS, 4),
+            "shapes": "attention: 1 sequence of %d kept tokens, %d/%d heads x %d; scorer: %d tokens, %d -> %d"
+                      % (K, Hq, Hkv, d, N, D, H1),
+            "note": "mean of %d calls after a warm-up; attention backward work = 2.5x the forward's" % reps}
 
 
 DECODE_BATCH = 16  # sequences per decode step
@@ -647,6 +710,9 @@ def main():
     if not args.no_memory:
         print("[bench] peak memory against the unpruned path (K = N, one layer)", file=sys.stderr, flush=True)
         out["memory"] = memory_vs_unpruned(torch, tg, w)
+    if not args.no_backward:
+        print("[bench] backward of the gated attention and of the scorer", file=sys.stderr, flush=True)
+        out["backward"] = backward_timing(torch, tg, w)
     if not args.no_decode:
         print("[bench] decode attention over the pruned and the full cache", file=sys.stderr, flush=True)
         out["decode_vs_unpruned"] = decode_vs_unpruned(torch, tg, w)

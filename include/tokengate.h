@@ -420,6 +420,68 @@ tg_status tg_full_prefill(const void* h, const int32_t* pos, const uint8_t* keep
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Backward of the token-gated attention — [TC] gradient-path section: the
+ * kept tokens' scores enter the upper layers' attention logits, so the loss
+ * reaches the scorer through them, and the per-head gain and temperature are
+ * learned. For the forward of tg_gated_attn_fwd and an upstream gradient dO:
+ *   dv_j = sum_i P_ij dO_i;  dL_ij = P_ij (dO_i.v_j - dO_i.o_i);
+ *   dq_i = t_h/sqrt(d) sum_j dL_ij k_j;  dk_j = t_h/sqrt(d) sum_i dL_ij q_i;
+ *   ds_j = sum_h g_h sum_i dL_ij;  dg_h = sum_ij dL_ij s_c[j];
+ *   dt_h = sum_ij dL_ij q_i.k_j / sqrt(d)
+ * (dk, dv of a kv head sum over the query heads of its group). P is
+ * recomputed from the forward's log-sum-exp.
+ *  q [T, Hq, d], k, v [T, Hkv, d], o [T, Hq, d] (the forward's output), dO
+ *  [T, Hq, d]: bf16; s_c [T], t, g [Hq], lse [Hq, T] (the forward's, natural
+ *  log): fp32; d_cu_kept [B+1] (device); T = cu_kept[B] (host); max_k bounds
+ *  the K_b.
+ *  Outputs, fp32: dq [T, Hq, d], dk, dv [T, Hkv, d], ds [T] (gradient of the
+ *  kept tokens' scores), dt, dg [Hq]. Every element is written (none is
+ *  accumulated into), and the results do not depend on timing.
+ * Supported: bf16, d in {64, 128}, Hq / Hkv in {1, 2, 4}; q, k, v, o, dO,
+ * dq, dk, dv 16-byte aligned. Workspace: tg_gated_attn_bwd_workspace_size()
+ * bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t tg_gated_attn_bwd_workspace_size(int B, int64_t T, int max_k, int Hq, int Hkv, int d,
+                                        tg_dtype dtype);
+tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const float* s_c,
+                            const float* t, const float* g, const int32_t* d_cu_kept, int B,
+                            int64_t T, int max_k, int Hq, int Hkv, int d, tg_dtype dtype,
+                            const void* o, const float* lse, const void* dO,
+                            float* dq, float* dk, float* dv, float* ds, float* dt, float* dg,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Backward of the gate scorer — [TC] gradient-path section: the gate gives
+ * the scoring network a gradient path, so it trains with the model. For
+ * s = sigmoid(w2 . GELU(W1 h + b1) + b2) (tg_gate_score) and ds per token:
+ *   du = ds s (1 - s); dw2 = sum_t du_t GELU(z_t); db2 = sum_t du_t;
+ *   dz = du w2 GELU'(z) with z = W1 h + b1; db1 = sum_t dz_t;
+ *   dW1 = sum_t dz_t h_t^T; dh = dz W1   (erf GELU).
+ *  h [T_in, D], W1 [H1, D], b1, w2 [H1]: bf16 (the forward's inputs);
+ *  s [T_in] fp32: the forward's scores (b2 enters only through them);
+ *  ds [T_in] fp32; dh [T_in, D] bf16 out; dW1 [H1, D], db1, dw2 [H1], db2 [1]
+ *  fp32 out (all written; zero when T_in = 0). Sums run in a fixed order
+ *  (deterministic).
+ * Supported: bf16, D % 64 == 0, H1 % 64 == 0; h, W1, dh, dW1 16-byte
+ * aligned. Workspace: tg_gate_score_bwd_workspace_size() bytes, 256-byte
+ * aligned (none when T_in = 0).
+ * ------------------------------------------------------------------------- */
+size_t tg_gate_score_bwd_workspace_size(int64_t T_in, int D, int H1, tg_dtype dtype);
+tg_status tg_gate_score_bwd(const void* h, int64_t T_in, int D, int H1, const void* W1,
+                            const void* b1, const void* w2, tg_dtype dtype, const float* s,
+                            const float* ds, void* dh, float* dW1, float* db1, float* dw2,
+                            float* db2, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gradient of the prompt scores through the compaction — [TC] early token
+ * filtering: pruned tokens stop at the gate layer and never reach the layers
+ * whose attention reads the scores. ds[kept_idx[r]] = ds_c[r] for r < T and
+ * ds[i] = 0 for every other i < T_in (a kept slot of -1, written for a
+ * rejected sequence, carries nothing). kept_idx [T] int32 as written by
+ * tg_topk_select; ds_c [T], ds [T_in] fp32. */
+tg_status tg_compact_scores_bwd(const float* ds_c, const int32_t* kept_idx, int64_t T, int64_t T_in,
+                                float* ds, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
  * Decode attention over the pruned K/V cache — [TC] engineering section:
  * once prefill has fixed the gate bias, decoding folds it into the attention
  * mask and runs ordinary attention over the cache; [TC] early token

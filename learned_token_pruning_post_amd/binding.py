@@ -38,6 +38,8 @@ ABI_FUNCTIONS = (
     "tg_gated_prefill_workspace_size", "tg_gated_prefill",
     "tg_full_prefill_workspace_size", "tg_full_prefill",
     "tg_decode_attn_workspace_size", "tg_decode_attn_fwd",
+    "tg_gated_attn_bwd_workspace_size", "tg_gated_attn_bwd",
+    "tg_gate_score_bwd_workspace_size", "tg_gate_score_bwd", "tg_compact_scores_bwd",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -138,6 +140,17 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(LayerWeights), i32, ctypes.POINTER(LayerDims),
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tg_full_prefill.restype = i32
+    L.tg_gated_attn_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.tg_gated_attn_bwd_workspace_size.restype = sz
+    L.tg_gated_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, vp, vp, vp,
+                                    vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tg_gated_attn_bwd.restype = i32
+    L.tg_gate_score_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
+    L.tg_gate_score_bwd_workspace_size.restype = sz
+    L.tg_gate_score_bwd.argtypes = [vp, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tg_gate_score_bwd.restype = i32
+    L.tg_compact_scores_bwd.argtypes = [vp, vp, i64, i64, vp, vp]
+    L.tg_compact_scores_bwd.restype = i32
     L.tg_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.tg_decode_attn_workspace_size.restype = sz
     L.tg_decode_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
@@ -282,6 +295,54 @@ def gated_attn_fwd(q, k, v, s_c, t, g, cu_kept, max_k: int, o=None, lse=None, wa
                                    max_k, Hq, Hkv, d, dtype_code(q.dtype), _p(o), _p(lse), None, 0,
                                    _stream()), "tg_gated_attn_fwd")
     return o, lse
+
+
+def gated_attn_bwd(q, k, v, s_c, t, g, cu_kept, max_k: int, o, lse, dO, ws=None):
+    """tg_gated_attn_bwd: gradients of the gated attention (fp32). Returns a dict
+    dq, dk, dv, ds, dt, dg."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    B = cu_kept.numel() - 1
+    dev = q.device
+    f = lambda shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    r = {"dq": f((T, Hq, d)), "dk": f((T, Hkv, d)), "dv": f((T, Hkv, d)), "ds": f((T,)), "dt": f((Hq,)),
+         "dg": f((Hq,))}
+    need = lib().tg_gated_attn_bwd_workspace_size(B, T, max_k, Hq, Hkv, d, dtype_code(q.dtype))
+    if ws is None or ws.numel() < need:
+        ws = _empty_ws(max(need, 1), dev)
+    _check(lib().tg_gated_attn_bwd(_p(q), _p(k), _p(v), _p(s_c), _p(t), _p(g), _p(cu_kept), B, T, max_k, Hq,
+                                   Hkv, d, dtype_code(q.dtype), _p(o), _p(lse), _p(dO), _p(r["dq"]), _p(r["dk"]),
+                                   _p(r["dv"]), _p(r["ds"]), _p(r["dt"]), _p(r["dg"]), _p(ws), ws.numel(),
+                                   _stream()), "tg_gated_attn_bwd")
+    return r
+
+
+def gate_score_bwd(h, W1, b1, w2, s, ds, ws=None):
+    """tg_gate_score_bwd: returns dict dh (h's dtype), dW1, db1, dw2, db2 (fp32)."""
+    T_in, D = h.shape
+    H1 = W1.shape[0]
+    dev = h.device
+    r = {"dh": torch.empty_like(h), "dW1": torch.empty((H1, D), dtype=torch.float32, device=dev),
+         "db1": torch.empty(H1, dtype=torch.float32, device=dev),
+         "dw2": torch.empty(H1, dtype=torch.float32, device=dev),
+         "db2": torch.empty(1, dtype=torch.float32, device=dev)}
+    need = lib().tg_gate_score_bwd_workspace_size(T_in, D, H1, dtype_code(h.dtype))
+    if need and (ws is None or ws.numel() < need):
+        ws = _empty_ws(need, dev)
+    _check(lib().tg_gate_score_bwd(_p(h), T_in, D, H1, _p(W1), _p(b1), _p(w2), dtype_code(h.dtype), _p(s),
+                                   _p(ds), _p(r["dh"]), _p(r["dW1"]), _p(r["db1"]), _p(r["dw2"]), _p(r["db2"]),
+                                   _p(ws) if need else None, ws.numel() if need else 0, _stream()),
+           "tg_gate_score_bwd")
+    return r
+
+
+def compact_scores_bwd(ds_c, kept, T_in: int, ds=None):
+    """tg_compact_scores_bwd: the prompt scores' gradient (zeros off the kept tokens)."""
+    if ds is None:
+        ds = torch.empty(T_in, dtype=torch.float32, device=ds_c.device)
+    _check(lib().tg_compact_scores_bwd(_p(ds_c), _p(kept), kept.numel(), T_in, _p(ds), _stream()),
+           "tg_compact_scores_bwd")
+    return ds
 
 
 def decode_attn_fwd(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g, max_len: int, o=None, lse=None,

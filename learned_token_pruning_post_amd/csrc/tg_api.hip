@@ -281,6 +281,87 @@ tg_status tg_gated_attn_fwd(const void* q, const void* k, const void* v, const f
 
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
+// backward of the gated attention
+// ---------------------------------------------------------------------------
+
+size_t tg_gated_attn_bwd_workspace_size(int B, int64_t T, int max_k, int Hq, int Hkv, int d,
+                                        tg_dtype dtype) {
+  if (dtype != TG_BF16 || B <= 0 || T < 0 || max_k < 0 || !tg::attn_bwd_supported(Hq, Hkv, d)) return 0;
+  return tg::attn_bwd_workspace_bytes(B, T, max_k, Hq, Hkv, d);
+}
+
+tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const float* s_c,
+                            const float* t, const float* g, const int32_t* d_cu_kept, int B, int64_t T,
+                            int max_k, int Hq, int Hkv, int d, tg_dtype dtype, const void* o,
+                            const float* lse, const void* dO, float* dq, float* dk, float* dv, float* ds,
+                            float* dt, float* dg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  TG_CHECK(B >= 0 && T >= 0 && T <= INT_MAX && max_k >= 0 && Hq > 0 && Hkv > 0 && d > 0,
+           TG_ERR_INVALID_ARG);
+  TG_CHECK(Hq % Hkv == 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(dtype == TG_BF16, TG_ERR_UNSUPPORTED);
+  TG_CHECK(tg::attn_bwd_supported(Hq, Hkv, d), TG_ERR_UNSUPPORTED);
+  TG_CHECK((int64_t)T * Hq * (d / 8) / 256 < INT_MAX, TG_ERR_UNSUPPORTED);  // prep grid
+  if (B == 0 || T == 0 || max_k == 0) return TG_OK;
+  TG_CHECK(q && k && v && s_c && t && g && d_cu_kept && o && lse && dO, TG_ERR_INVALID_ARG);
+  TG_CHECK(dq && dk && dv && ds && dt && dg, TG_ERR_INVALID_ARG);
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  TG_CHECK(a16(q) && a16(k) && a16(v) && a16(o) && a16(dO) && a16(dq) && a16(dk) && a16(dv),
+           TG_ERR_INVALID_ARG);
+  const size_t need = tg::attn_bwd_workspace_bytes(B, T, max_k, Hq, Hkv, d);
+  TG_CHECK(ws && ws_bytes >= need, TG_ERR_WORKSPACE);
+  TG_CHECK(((uintptr_t)ws & 255u) == 0, TG_ERR_INVALID_ARG);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+  return launched(tg::launch_attn_bwd(q, k, v, s_c, t, g, d_cu_kept, B, T, max_k, Hq, Hkv, d, o, lse, dO,
+                                      dq, dk, dv, ds, dt, dg, ws, stream));
+}
+
+// ---------------------------------------------------------------------------
+// backward of the scorer and of the compaction
+// ---------------------------------------------------------------------------
+
+size_t tg_gate_score_bwd_workspace_size(int64_t T_in, int D, int H1, tg_dtype dtype) {
+  if (dtype != TG_BF16 || T_in <= 0 || D <= 0 || H1 <= 0) return 0;
+  return tg::score_bwd_workspace_bytes(T_in, D, H1);
+}
+
+tg_status tg_gate_score_bwd(const void* h, int64_t T_in, int D, int H1, const void* W1, const void* b1,
+                            const void* w2, tg_dtype dtype, const float* s, const float* ds, void* dh,
+                            float* dW1, float* db1, float* dw2, float* db2, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  TG_CHECK(T_in >= 0 && T_in <= INT_MAX && D > 0 && H1 > 0, TG_ERR_INVALID_ARG);
+  TG_CHECK(dtype == TG_BF16, TG_ERR_UNSUPPORTED);
+  TG_CHECK(D % 64 == 0 && H1 % 64 == 0, TG_ERR_UNSUPPORTED);
+  // 32-bit buffer ranges of the products' operands
+  TG_CHECK(fits32(T_in, D) && fits32(T_in, H1) && fits32(H1, D), TG_ERR_UNSUPPORTED);
+  TG_CHECK(W1 && b1 && w2 && dW1 && db1 && dw2 && db2, TG_ERR_INVALID_ARG);
+  TG_CHECK(T_in == 0 || (h && s && ds && dh), TG_ERR_INVALID_ARG);
+  auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
+  TG_CHECK(a16(h) && a16(W1) && a16(dh) && a16(dW1), TG_ERR_INVALID_ARG);
+  const size_t need = tg::score_bwd_workspace_bytes(T_in, D, H1);
+  TG_CHECK(T_in == 0 || (ws && ws_bytes >= need && ((uintptr_t)ws & 255u) == 0), TG_ERR_WORKSPACE);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+  if (T_in == 0) {  // no tokens: every gradient is zero
+    TG_LAUNCH(tg::launch_fill_f32(dW1, (int64_t)H1 * D, 0.f, stream));
+    TG_LAUNCH(tg::launch_fill_f32(db1, H1, 0.f, stream));
+    TG_LAUNCH(tg::launch_fill_f32(dw2, H1, 0.f, stream));
+    return launched(tg::launch_fill_f32(db2, 1, 0.f, stream));
+  }
+  return launched(tg::launch_score_bwd(h, T_in, D, H1, W1, b1, w2, s, ds, dh, dW1, db1, dw2, db2, ws, stream));
+}
+
+tg_status tg_compact_scores_bwd(const float* ds_c, const int32_t* kept_idx, int64_t T, int64_t T_in,
+                                float* ds, hipStream_t stream) {
+  TG_CHECK(T >= 0 && T_in >= 0 && T <= T_in && T_in <= INT_MAX, TG_ERR_INVALID_ARG);
+  if (T_in == 0) return TG_OK;
+  TG_CHECK(ds && (T == 0 || (ds_c && kept_idx)), TG_ERR_INVALID_ARG);
+  tg_status a = check_arch();
+  if (a != TG_OK) return a;
+  return launched(tg::launch_scatter_scores(ds_c, kept_idx, T, T_in, ds, stream));
+}
+
+// ---------------------------------------------------------------------------
 // decode attention over the pruned cache
 // ---------------------------------------------------------------------------
 

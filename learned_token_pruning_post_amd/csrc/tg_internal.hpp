@@ -125,4 +125,21 @@ hipError_t launch_decode_attn(const void* q, const void* kA, const void* vA, con
                               int max_len, int Hq, int Hkv, int d, bool is_bf16, void* o, float* lse,
                               int32_t* status, void* ws, hipStream_t stream);
 
+// ---- backward of the gated attention (bf16; d in {64, 128}, Hq / Hkv in {1, 2, 4}) ----
+bool attn_bwd_supported(int Hq, int Hkv, int d);
+size_t attn_bwd_workspace_bytes(int B, int64_t T, int max_k, int Hq, int Hkv, int d);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* s_c, const float* t,
+                           const float* g, const int32_t* cu, int B, int64_t T, int max_k, int Hq, int Hkv,
+                           int d, const void* o, const float* lse, const void* dO, float* dq, float* dk,
+                           float* dv, float* ds, float* dt, float* dg, void* ws, hipStream_t stream);
+
+// ---- backward of the scorer (bf16; D % 64 == 0, H1 % 64 == 0) and of the compaction ----
+size_t score_bwd_workspace_bytes(int64_t T, int D, int H1);
+hipError_t launch_score_bwd(const void* h, int64_t T, int D, int H1, const void* W1, const void* b1,
+                            const void* w2, const float* s, const float* ds, void* dh, float* dW1,
+                            float* db1, float* dw2, float* db2, void* ws, hipStream_t stream);
+// ds[kept[r]] = ds_c[r] for r < T, every other ds[i] (i < T_in) = 0
+hipError_t launch_scatter_scores(const float* ds_c, const int32_t* kept, int64_t T, int64_t T_in, float* ds,
+                                 hipStream_t stream);
+
 }  // namespace tg

@@ -332,6 +332,23 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, in
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
+// gradient of the prompt scores through the compaction: zero, then scatter
+__global__ void scatter_scores_kernel(const float* __restrict__ ds_c, const int32_t* __restrict__ kept, int64_t T,
+                                      int64_t T_in, float* __restrict__ ds) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= T) return;
+  const int32_t i = kept[r];
+  if (i >= 0 && i < T_in) ds[i] = ds_c[r];  // -1 slots of a rejected sequence carry nothing
+}
+
+hipError_t launch_scatter_scores(const float* ds_c, const int32_t* kept, int64_t T, int64_t T_in, float* ds,
+                                 hipStream_t stream) {
+  hipError_t e = launch_fill_f32(ds, T_in, 0.f, stream);
+  if (e != hipSuccess || T == 0) return e;
+  scatter_scores_kernel<<<dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream>>>(ds_c, kept, T, T_in, ds);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);

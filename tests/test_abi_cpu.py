@@ -191,6 +191,49 @@ def test_decode_attention_argument_errors(L):
     assert call(B=0) == OK                         # nothing to do
 
 
+def test_attention_backward_argument_errors(L):
+    ws = L.tg_gated_attn_bwd_workspace_size
+    need = ws(1, 4096, 4096, 16, 8, 128, 1)
+    assert need >= 2 * 16 * 4096 * 4 + 8 * 4096 * 4     # lse2 and D per (head, query), ds per kv head
+    assert ws(1, 4096, 4096, 16, 8, 128, 0) == 0 and ws(1, 4096, 4096, 16, 2, 128, 1) == 0  # fp32, G=8
+    f = L.tg_gated_attn_bwd
+
+    def call(B=1, T=4096, max_k=4096, Hq=16, Hkv=8, d=128, dt=1, q=FAKE, dq=FAKE, w=None, wsb=0):
+        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, max_k, Hq, Hkv, d, dt, FAKE, FAKE, FAKE, dq, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, w, wsb, None)
+    assert call(Hq=12) == INVALID
+    assert call(dt=0) == UNSUP                      # bf16 only
+    assert call(Hkv=2) == UNSUP                     # group of 8
+    assert call(d=96) == UNSUP
+    assert call(T=-1) == INVALID
+    assert call(q=None) == INVALID
+    assert call(dq=None) == INVALID
+    assert call(q=ctypes.c_void_p(0x100008)) == INVALID
+    assert call() == WS
+    assert call(w=FAKE, wsb=need - 1) == WS
+    assert call(w=ctypes.c_void_p(0x100010), wsb=need) == INVALID
+    assert call(B=0) == OK and call(T=0) == OK and call(max_k=0) == OK
+
+
+def test_scorer_backward_argument_errors(L):
+    assert L.tg_gate_score_bwd_workspace_size(32768, 2048, 256, 1) >= 2 * 32768 * 256 * 2 + 16 * 256 * 2048 * 4
+    assert L.tg_gate_score_bwd_workspace_size(32768, 2048, 256, 0) == 0
+    f = L.tg_gate_score_bwd
+
+    def call(T=1000, D=256, H1=64, dt=1, h=FAKE, dW1=FAKE, w=None, wsb=0):
+        return f(h, T, D, H1, FAKE, FAKE, FAKE, dt, FAKE, FAKE, FAKE, dW1, FAKE, FAKE, FAKE, w, wsb, None)
+    assert call(dt=0) == UNSUP
+    assert call(D=200) == UNSUP and call(H1=96) == UNSUP
+    assert call(T=-1) == INVALID
+    assert call(h=None) == INVALID and call(dW1=None) == INVALID
+    assert call(h=ctypes.c_void_p(0x100008)) == INVALID
+    assert call() == WS
+    g = L.tg_compact_scores_bwd
+    assert g(FAKE, FAKE, 11, 10, FAKE, None) == INVALID   # more kept than tokens
+    assert g(FAKE, None, 5, 10, FAKE, None) == INVALID
+    assert g(None, None, 0, 0, None, None) == OK
+
+
 def test_layer_stack_argument_errors(L):
     f = L.tg_upper_layer_stack_fwd
     dm = _dims()

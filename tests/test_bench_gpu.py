@@ -57,6 +57,9 @@ def test_bench_json_line_small_workload():
     dec = d["decode_vs_unpruned"]
     assert dec["kept_prompt_keys"] == 1024 and dec["prompt_keys_unpruned"] == 8192
     assert dec["pruned_us"] > 0 and dec["speedup"] > 1 and 0 < dec["pruned_frac_hbm"] < 1
+    # the gate's gradient path timed at the workload's shapes
+    bw = d["backward"]
+    assert bw["attn_bwd_us"] > 0 and bw["scorer_bwd_us"] > 0 and 0 < bw["attn_bwd_frac_mfma_peak"] < 1
     # the graph replay of the same step takes about as long as the eager step
     g = d["ms_per_step_hip_graph"]
     assert g is not None and 0.5 * d["ms_per_step"] < g < 1.5 * d["ms_per_step"]
