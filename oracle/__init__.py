@@ -8,6 +8,6 @@ from .tokengate_oracle import (FORCED_GT_BUDGET, BUDGET_GT_LEN, NAN_SCORE,  # no
                                gelu, sigmoid, gate_score, select_one, topk_select,
                                compact, rmsnorm, rope, gated_attention, decode_attention, silu,
                                gated_attention_backward, gelu_grad, gate_score_backward,
-                               compact_backward,
+                               compact_backward, gdn_mixer,
                                qkv_rope, o_proj, swiglu_act, down_proj,
                                upper_layer, gated_prefill)

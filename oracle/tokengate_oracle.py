@@ -312,6 +312,46 @@ def decode_attention(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g):
 
 
 # ----------------------------------------------------------------------------
+# Hybrid variant: the Gated DeltaNet token mixer on the kept tokens
+# ----------------------------------------------------------------------------
+
+def gdn_mixer(q, k, v, alpha, beta, cu, state_in=None, eps: float = 1e-6):
+    """Gated DeltaNet recurrence over each sequence of a packed batch.
+
+    [TC] section on the gate position: in a hybrid model (Qwen3.5-2B) only
+    some layers use full attention and the rest are Gated DeltaNet; the
+    scorer reads hidden states, so the gate can sit on a GDN layer, and a GDN
+    layer above the gate has no attention logits to bias, so it simply runs
+    on the kept tokens. The recurrence (the Gated DeltaNet layer's, per head,
+    state S [dv, dk], zero or ``state_in`` at a sequence's start):
+        k^ = k / |k|, q^ = q / (|q| sqrt(dk))
+        S <- alpha_t S;  S <- S + beta_t (v_t - S k^_t) k^_t^T;  o_t = S q^_t
+    i.e. S_t = alpha_t S_{t-1} (I - beta_t k^ k^T) + beta_t v_t k^T.
+    q, k: [T, H, dk]; v: [T, H, dv]; alpha, beta: [T, H]; cu: [B+1].
+    Returns (o [T, H, dv], state [B, H, dv, dk] after each sequence's last token).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, beta = _f64(alpha), _f64(beta)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.asarray(cu, dtype=np.int64)
+    B = len(cu) - 1
+    o = np.zeros((T, H, dv))
+    state = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if state_in is None else _f64(state_in)[b, h].copy()
+            for tt in range(int(cu[b]), int(cu[b + 1])):
+                kh = k[tt, h] / math.sqrt(float(k[tt, h] @ k[tt, h]) + eps)
+                qh = q[tt, h] / (math.sqrt(float(q[tt, h] @ q[tt, h]) + eps) * math.sqrt(dk))
+                S = alpha[tt, h] * S
+                S = S + beta[tt, h] * np.outer(v[tt, h] - S @ kh, kh)
+                o[tt, h] = S @ qh
+            state[b, h] = S
+    return o, state
+
+
+# ----------------------------------------------------------------------------
 # Backward: the gradient path from the upper attention to the scorer
 # ----------------------------------------------------------------------------
 

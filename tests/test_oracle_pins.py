@@ -825,3 +825,83 @@ def test_gradient_path_through_the_compaction():
     np.testing.assert_allclose(ds, st.grad.numpy(), atol=1e-12)
     pruned = np.setdiff1d(np.arange(50), kept)
     assert np.all(ds[pruned] == 0) and np.all(ds[kept] == ds_c)
+
+
+# ----------------------------------------------------------------------------
+# hybrid variant: the Gated DeltaNet mixer
+# ----------------------------------------------------------------------------
+
+def _gdn_case(seed, cu, H, dk, dv):
+    rng = np.random.default_rng(seed)
+    T = int(cu[-1])
+    return (rng.standard_normal((T, H, dk)), rng.standard_normal((T, H, dk)), rng.standard_normal((T, H, dv)),
+            rng.uniform(0.8, 1.0, (T, H)), rng.uniform(0.0, 1.0, (T, H)))
+
+
+def test_gdn_matches_the_unrolled_product_form():
+    # S_T = sum_t beta_t v_t k_t^T prod_{s>t} A_s with A_s = alpha_s (I - beta_s k_s k_s^T),
+    # written as explicit matrix products (another evaluation order than the recurrence)
+    cu = np.array([0, 9, 9, 14])
+    q, k, v, al, be = _gdn_case(61, cu, 2, 4, 3)
+    o, st = O.gdn_mixer(q, k, v, al, be, cu)
+    for b in range(3):
+        lo, hi = cu[b], cu[b + 1]
+        for h in range(2):
+            for t in range(lo, hi):
+                S = np.zeros((3, 4))
+                for u in range(lo, t + 1):
+                    ku = k[u, h] / math.sqrt(k[u, h] @ k[u, h] + 1e-6)
+                    P = np.eye(4)
+                    for w_ in range(u + 1, t + 1):
+                        kw = k[w_, h] / math.sqrt(k[w_, h] @ k[w_, h] + 1e-6)
+                        P = P @ (al[w_, h] * (np.eye(4) - be[w_, h] * np.outer(kw, kw)))
+                    S = S + be[u, h] * np.outer(v[u, h], ku) @ P
+                # the decay alpha_u of step u multiplies the state before its own write, not the write
+                qh = q[t, h] / (math.sqrt(q[t, h] @ q[t, h] + 1e-6) * 2.0)
+                np.testing.assert_allclose(o[t, h], S @ qh, atol=1e-12)
+            if hi > lo:
+                np.testing.assert_allclose(st[b, h], S, atol=1e-12)
+    assert np.all(st[1] == 0)            # the empty sequence keeps the zero state
+
+
+def test_gdn_closed_forms():
+    # one token: S = beta v k^T, o = beta (k^.q^) v
+    q, k, v, al, be = _gdn_case(62, np.array([0, 1]), 1, 8, 5)
+    o, _ = O.gdn_mixer(q, k, v, al, be, np.array([0, 1]))
+    kh = k[0, 0] / math.sqrt(k[0, 0] @ k[0, 0] + 1e-6)
+    qh = q[0, 0] / (math.sqrt(q[0, 0] @ q[0, 0] + 1e-6) * math.sqrt(8))
+    np.testing.assert_allclose(o[0, 0], be[0, 0] * (kh @ qh) * v[0, 0], atol=1e-12)
+    # alpha = beta = 1 with orthonormal keys: an exact associative memory; reading with
+    # q = k_j returns v_j / sqrt(dk)
+    dk = 4
+    keys = np.eye(dk)[None].repeat(1, axis=0).transpose(1, 0, 2)       # [4, 1, 4]
+    vals = np.random.default_rng(63).standard_normal((dk, 1, 3))
+    qq = np.zeros((dk + 1, 1, dk))
+    qq[-1, 0] = keys[2, 0]
+    kk = np.concatenate([keys, keys[:1] * 0 + keys[:1]])
+    vv = np.concatenate([vals, vals[:1]])
+    al1, be1 = np.ones((dk + 1, 1)), np.ones((dk + 1, 1))
+    be1[-1] = 0.0                                                      # the last step only reads
+    o, st = O.gdn_mixer(qq, kk, vv, al1, be1, np.array([0, dk + 1]))
+    np.testing.assert_allclose(o[-1, 0], vals[2, 0] / math.sqrt(dk), atol=1e-5)
+    np.testing.assert_allclose(st[0, 0], vals[:, 0].T @ keys[:, 0], atol=1e-5)
+    # beta = 0: the state only decays; writing twice the same key with beta = 1 overwrites
+    o0, st0 = O.gdn_mixer(qq, kk, vv, al1 * 0.5, be1 * 0, np.array([0, dk + 1]), state_in=np.ones((1, 1, 3, dk)))
+    np.testing.assert_allclose(st0[0, 0], 0.5 ** (dk + 1) * np.ones((3, dk)), atol=1e-12)
+    k2 = np.zeros((2, 1, 3))
+    k2[:, 0, 0] = 1.0
+    v2 = np.array([[[1.0, 2.0]], [[5.0, -1.0]]])
+    _, st2 = O.gdn_mixer(k2, k2, v2, np.ones((2, 1)), np.ones((2, 1)), np.array([0, 2]))
+    np.testing.assert_allclose(st2[0, 0][:, 0], [5.0, -1.0], atol=1e-5)
+
+
+def test_gdn_state_carries_across_calls():
+    # running a sequence in two calls, the second starting from the first's state,
+    # equals one call (the recurrence is a left fold)
+    cu = np.array([0, 12])
+    q, k, v, al, be = _gdn_case(64, cu, 2, 6, 4)
+    o, st = O.gdn_mixer(q, k, v, al, be, cu)
+    o1, s1 = O.gdn_mixer(q[:5], k[:5], v[:5], al[:5], be[:5], np.array([0, 5]))
+    o2, s2 = O.gdn_mixer(q[5:], k[5:], v[5:], al[5:], be[5:], np.array([0, 7]), state_in=s1)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), o, atol=1e-12)
+    np.testing.assert_allclose(s2, st, atol=1e-12)
