@@ -57,6 +57,8 @@ def parse():
                     help="skip the peak-memory comparison with the unpruned path")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward of the gated attention and of the scorer")
+    ap.add_argument("--no-gdn", action="store_true",
+                    help="skip timing the hybrid variant's Gated DeltaNet mixer")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-attention comparison over the pruned and the full cache")
     ap.add_argument("--no-prefill-time", action="store_true",
@@ -358,6 +360,43 @@ def backward_timing(torch, tg, w, reps=5):
             "shapes": "attention: 1 sequence of %d kept tokens, %d/%d heads x %d; scorer: %d tokens, %d -> %d"
                       % (K, Hq, Hkv, d, N, D, H1),
             "note": "mean of %d calls after a warm-up; attention backward work = 2.5x the forward's" % reps}
+
+
+def gdn_timing(torch, tg, w, reps=3):
+    """The hybrid variant's Gated DeltaNet mixer (tg_gdn_fwd) over one sequence
+    of the kept-token count, at the model's head shapes (one head per query
+    head, dk = dv = head dim): seeded random operands, HIP events on the launch
+    stream. Algorithmic work per token and head: S k, the rank-1 write (a
+    multiply and an FMA per state element) and S q, 6 dk dv flops (fp32, on
+    the vector ALUs: a sequential recurrence, no matmul)."""
+    dm = w.dims
+    dt = torch.bfloat16 if dm.dtype == "bf16" else torch.float32
+    K, H, d = w.K[0], dm.Hq, dm.d
+    gen = torch.Generator(device="cuda").manual_seed(3000 + w.cfg_id)
+    rnd = lambda shape: torch.randn(shape, generator=gen, device="cuda").to(dt)
+    q, k, v = rnd((K, H, d)), rnd((K, H, d)), rnd((K, H, d))
+    al = 0.8 + 0.2 * torch.rand((K, H), generator=gen, device="cuda")
+    be = torch.rand((K, H), generator=gen, device="cuda")
+    cu = torch.tensor([0, K], dtype=torch.int32, device="cuda")
+    o = torch.empty_like(v)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+    tg.gdn_fwd(q, k, v, al, be, cu, o=o)
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for _ in range(reps):
+        tg.gdn_fwd(q, k, v, al, be, cu, o=o)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    us = ev.ms(0, 1) / reps * 1e3
+    ev.close()
+    flop = 6.0 * K * H * d * d
+    tf = flop / (us * 1e-6) / 1e12
+    return {"us": round(us, 1), "tokens": K, "heads": H, "dk": d, "dv": d, "tflops": round(tf, 2),
+            "frac_fp32_vector_peak": round(tf / PEAK_F32_TFLOPS, 4),
+            "workgroups": H * (d // (4 * (64 // (d // 8)))),
+            "note": "one sequence: the recurrence is sequential over its tokens, parallel over heads and "
+                    "state rows only; mean of %d calls after a warm-up" % reps}
 
 
 DECODE_BATCH = 16  # sequences per decode step
@@ -713,6 +752,9 @@ def main():
     if not args.no_backward:
         print("[bench] backward of the gated attention and of the scorer", file=sys.stderr, flush=True)
         out["backward"] = backward_timing(torch, tg, w)
+    if not args.no_gdn:
+        print("[bench] Gated DeltaNet mixer over the kept tokens", file=sys.stderr, flush=True)
+        out["gdn_kept_tokens"] = gdn_timing(torch, tg, w)
     if not args.no_decode:
         print("[bench] decode attention over the pruned and the full cache", file=sys.stderr, flush=True)
         out["decode_vs_unpruned"] = decode_vs_unpruned(torch, tg, w)

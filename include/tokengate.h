@@ -482,6 +482,28 @@ tg_status tg_compact_scores_bwd(const float* ds_c, const int32_t* kept_idx, int6
                                 float* ds, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Gated DeltaNet mixer of the hybrid variant — [TC] section on the gate
+ * position: in a hybrid model (Qwen3.5-2B) only some layers use full
+ * attention and the rest are Gated DeltaNet; the scorer reads hidden states,
+ * so the gate can sit on a GDN layer, and a GDN layer above the gate has no
+ * attention logits to bias: it runs on the kept tokens (the rows compacted
+ * by tg_select_compact, packed by d_cu). Per sequence and head, state S
+ * [dv, dk] (state_in's, or zero), for each token in order:
+ *   k^ = k / sqrt(|k|^2 + 1e-6),  q^ = q / (sqrt(|q|^2 + 1e-6) sqrt(dk))
+ *   S <- alpha S;  S <- S + beta (v - S k^) k^T;  o = S q^
+ *  q, k [T, H, dk], v [T, H, dv], o [T, H, dv] out: dtype; alpha, beta
+ *  [T, H] fp32 (decay and write strength of each token and head); d_cu
+ *  [B+1] int32 (device); state_in / state_out [B, H, dv, dk] fp32, optional
+ *  (NULL: start from zero / do not write).
+ * Supported: dk in {64, 128}, dv % 32 == 0; q and k 16-byte aligned. No
+ * workspace.
+ * ------------------------------------------------------------------------- */
+tg_status tg_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* beta, const int32_t* d_cu, int B, int H, int dk, int dv,
+                     tg_dtype dtype, const float* state_in, void* o, float* state_out,
+                     hipStream_t stream);
+
+/* -------------------------------------------------------------------------
  * Decode attention over the pruned K/V cache — [TC] engineering section:
  * once prefill has fixed the gate bias, decoding folds it into the attention
  * mask and runs ordinary attention over the cache; [TC] early token

@@ -40,6 +40,7 @@ ABI_FUNCTIONS = (
     "tg_decode_attn_workspace_size", "tg_decode_attn_fwd",
     "tg_gated_attn_bwd_workspace_size", "tg_gated_attn_bwd",
     "tg_gate_score_bwd_workspace_size", "tg_gate_score_bwd", "tg_compact_scores_bwd",
+    "tg_gdn_fwd",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -151,6 +152,8 @@ def lib() -> ctypes.CDLL:
     L.tg_gate_score_bwd.restype = i32
     L.tg_compact_scores_bwd.argtypes = [vp, vp, i64, i64, vp, vp]
     L.tg_compact_scores_bwd.restype = i32
+    L.tg_gdn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.tg_gdn_fwd.restype = i32
     L.tg_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.tg_decode_attn_workspace_size.restype = sz
     L.tg_decode_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
@@ -343,6 +346,21 @@ def compact_scores_bwd(ds_c, kept, T_in: int, ds=None):
     _check(lib().tg_compact_scores_bwd(_p(ds_c), _p(kept), kept.numel(), T_in, _p(ds), _stream()),
            "tg_compact_scores_bwd")
     return ds
+
+
+def gdn_fwd(q, k, v, alpha, beta, cu, state_in=None, o=None, state_out=None, want_state=False):
+    """tg_gdn_fwd: the Gated DeltaNet mixer over the packed sequences of cu.
+    Returns (o, state_out)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    B = cu.numel() - 1
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(lib().tg_gdn_fwd(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(cu), B, H, dk, dv, dtype_code(q.dtype),
+                            _p(state_in), _p(o), _p(state_out), _stream()), "tg_gdn_fwd")
+    return o, state_out
 
 
 def decode_attn_fwd(q, kA, vA, sA, cuA, kB, vB, sB, lenB, t, g, max_len: int, o=None, lse=None,

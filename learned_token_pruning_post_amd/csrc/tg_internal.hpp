@@ -142,4 +142,10 @@ hipError_t launch_score_bwd(const void* h, int64_t T, int D, int H1, const void*
 hipError_t launch_scatter_scores(const float* ds_c, const int32_t* kept, int64_t T, int64_t T_in, float* ds,
                                  hipStream_t stream);
 
+// ---- Gated DeltaNet mixer (dk in {64, 128}, dv % 32 == 0) ----
+bool gdn_supported(int dk, int dv);
+hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                      const int32_t* cu, int B, int H, int dk, int dv, bool is_bf16, const float* state_in,
+                      void* o, float* state_out, hipStream_t stream);
+
 }  // namespace tg

@@ -234,6 +234,18 @@ def test_scorer_backward_argument_errors(L):
     assert g(None, None, 0, 0, None, None) == OK
 
 
+def test_gdn_argument_errors(L):
+    f = L.tg_gdn_fwd
+
+    def call(B=1, H=4, dk=128, dv=128, dt=1, q=FAKE, o=FAKE):
+        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, B, H, dk, dv, dt, None, o, None, None)
+    assert call(dk=96) == UNSUP and call(dv=48) == UNSUP and call(dt=5) == UNSUP
+    assert call(H=0) == INVALID and call(B=-1) == INVALID
+    assert call(q=None) == INVALID and call(o=None) == INVALID
+    assert call(q=ctypes.c_void_p(0x100004)) == INVALID
+    assert call(B=0) == OK
+
+
 def test_layer_stack_argument_errors(L):
     f = L.tg_upper_layer_stack_fwd
     dm = _dims()

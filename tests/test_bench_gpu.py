@@ -60,6 +60,7 @@ def test_bench_json_line_small_workload():
     # the gate's gradient path timed at the workload's shapes
     bw = d["backward"]
     assert bw["attn_bwd_us"] > 0 and bw["scorer_bwd_us"] > 0 and 0 < bw["attn_bwd_frac_mfma_peak"] < 1
+    assert d["gdn_kept_tokens"]["us"] > 0 and d["gdn_kept_tokens"]["tokens"] == 1024
     # the graph replay of the same step takes about as long as the eager step
     g = d["ms_per_step_hip_graph"]
     assert g is not None and 0.5 * d["ms_per_step"] < g < 1.5 * d["ms_per_step"]
