@@ -20,11 +20,16 @@
 //    computes S = Q K^T and dP = dO V^T with K and V of its keys held as
 //    register B operands, so the accumulators put one key per lane and P and
 //    dL feed dV^T += dO^T P and dK^T += Q^T dL straight from registers (the
-//    A operands dO^T and Q^T are gathered from LDS). The per-key sums for ds,
-//    dg and dt are then per lane. The heads of a group meet in LDS at the end;
+//    A operands dO^T and Q^T come from transposing LDS reads). The per-key
+//    sums for ds, dg and dt are then per lane. The heads of a group meet in
+//    LDS at the end;
 //  * dQ: mirrors the forward's layout (S^T = K Q^T, one query per lane), one
 //    workgroup per (sequence, kv head, pair of query tiles), K, V and scores
-//    of each 32-key tile staged in LDS; dQ^T += K^T dL^T;
+//    of each 32-key tile staged in LDS; dQ^T += K^T dL^T (K^T by transposing
+//    LDS reads);
+//  * staging: direct-to-LDS buffer loads over the sequence's rows (reads past
+//    its end give zeros), double-buffered: the next step's tiles are in flight
+//    while the current one is computed, one barrier per step;
 //  * reductions: ds over kv heads, dt and dg over workgroups, in a fixed
 //    order (deterministic).
 #include "tg_common.hpp"
@@ -44,21 +49,41 @@ struct Tile {
   __device__ static const bf16x8& chunk(const bf16* base, int r, int c) {
     return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + r * RB + ((c ^ swz(r)) << 4));
   }
-  __device__ static bf16 elem(const bf16* base, int r, int col) {
-    return *reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + r * RB +
-                                          (((col >> 3) ^ swz(r)) << 4) + ((col & 7) << 1));
-  }
-  // rows [0, nrows) from global rows src + r * stride (elements); rows at or
-  // past `valid` are zero
-  __device__ static void stage(bf16* base, const bf16* src, size_t stride, int nrows, int valid) {
-    for (int i = threadIdx.x; i < nrows * NCH; i += NT) {
-      const int r = i / NCH, c = i % NCH;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < valid) v = *reinterpret_cast<const u32x4*>(src + (size_t)r * stride + c * 8);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + r * RB + ((c ^ swz(r)) << 4)) = v;
-    }
-  }
 };
+
+// A operand of a transposed tile (rows of A = feature columns, k-slots = tile
+// rows): lane l holds feature 32*db + l%32 and the 8 tile rows 16*ks + {0..3,
+// 8..11} + 4*(l/32), the row order of registers 8*ks .. 8*ks+7 of an
+// accumulator (acc_row). Two ds_read_tr16_b64: within 16 lanes, lane 4e+m
+// addresses row e, features 4m .. 4m+3, and lane i receives feature i of
+// rows 0..3.
+template <int HD>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* base, int ks, int db, int lane) {
+  const int vg = (lane >> 4) & 3, vs = lane & 15;
+  const int r = 16 * ks + 4 * (vg >> 1) + (vs >> 2);
+  const int d = 32 * db + 16 * (vg & 1) + 4 * (vs & 3);
+  const char* b = reinterpret_cast<const char*>(base);
+  const char* lo = b + r * Tile<HD>::RB + (((d >> 3) ^ Tile<HD>::swz(r)) << 4) + (d & 7) * 2;
+  const char* hi = b + (r + 8) * Tile<HD>::RB + (((d >> 3) ^ Tile<HD>::swz(r + 8)) << 4) + (d & 7) * 2;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(lo));
+  const bf16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(hi));
+  return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Direct-to-LDS load of 32 rows of a row-strided bf16 tensor into a swizzled
+// Tile: 1 KB blocks of RPB rows; lane l of a block lands in row l / NCH, slot
+// l % NCH and fetches the logical chunk the swizzle puts there. `rs` covers the
+// sequence's rows (reads past its end give zeros); `row0` is the tile's first
+// row in the sequence, `rstride` the bytes between rows, `col` the byte offset
+// of the tile's columns inside a row (the head).
+template <int HD>
+__device__ __forceinline__ void dma_tile(const i32x4& rs, uint32_t row0, uint32_t rstride, uint32_t col,
+                                         uint32_t lds_tile, int blk, int lane) {
+  constexpr int NCH = Tile<HD>::NCH, RPB = 1024 / Tile<HD>::RB;
+  const int r = blk * RPB + lane / NCH, slot = lane % NCH;
+  const uint32_t off = (row0 + (uint32_t)r) * rstride + col + (uint32_t)((slot ^ Tile<HD>::swz(r)) << 4);
+  buf_dma16(rs, off, __builtin_amdgcn_readfirstlane(lds_tile + blk * 1024));
+}
 
 // query / key index of accumulator register r of lane group g (rows of a 32x32 tile)
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
@@ -128,11 +153,17 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args a) {
 template <int G, int HD>
 struct KvSmem {
   static constexpr int WPK = 4 / G;
-  bf16 q[G][32 * HD];
-  bf16 o[G][32 * HD];  // dO
-  float l2[G][32], dl[G][32];
-  // heads of a group meet here: dK^T and dV^T of a 32-key sub-tile ([d][key])
-  float red[G > 1 ? WPK : 1][2][HD * 32];
+  struct Stage {
+    bf16 q[G][32 * HD];
+    bf16 o[G][32 * HD];  // dO
+  };
+  union {
+    Stage st[2];  // double-buffered Q and dO rows of the query step
+    // after the query loop, the heads of a group meet here: dK^T and dV^T of a
+    // 32-key sub-tile ([d][key])
+    float red[G > 1 ? WPK : 1][2][HD * 32];
+  };
+  float l2[2][G][32], dl[2][G][32];
   float dsr[4][32];
   float tgr[4][2];
 };
@@ -142,9 +173,12 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
   constexpr int WPK = 4 / G;  // 32-key sub-tiles per key tile
   constexpr int BK = 32 * WPK;
   constexpr int NS = HD / 16, ND = HD / 32;
+  constexpr int NBLK = 32 * Tile<HD>::RB / 1024;  // 1 KB blocks per 32-row tile
+  constexpr int BPW = 2 * G * NBLK / 4;            // of them per wave and step
   using TL = Tile<HD>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char dkdv_smem[];
-  auto& S = *reinterpret_cast<KvSmem<G, HD>*>(dkdv_smem);
+  using SM = KvSmem<G, HD>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char dkdv_smem[];
+  auto& S = *reinterpret_cast<SM*>(dkdv_smem);
 
   const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, grp = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -160,20 +194,53 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
   const float g2 = a.g[h] * TG_LOG2E;
   float dg_acc = 0.f, dt_acc = 0.f;
 
+  // Q and dO rows of the group's heads: resources over the sequence's rows
+  const uint32_t rstride = (uint32_t)a.Hq * HD * 2u;
+  const i32x4 rq = make_rsrc(a.q + (size_t)seq0 * a.Hq * HD + (size_t)hk * G * HD, (uint32_t)Kb * rstride);
+  const i32x4 ro = make_rsrc(a.dO + (size_t)seq0 * a.Hq * HD + (size_t)hk * G * HD, (uint32_t)Kb * rstride);
+  const uint32_t lds0 = lds_addr(dkdv_smem);
+  // one step's loads into stage buffer sb: 2 * G * NBLK blocks, BPW per wave
+  auto issue = [&](int qt, int sb) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int bi = w * BPW + i;
+      const int tens = bi / (G * NBLK), gg = (bi / NBLK) % G, blk = bi % NBLK;
+      const uint32_t dst = lds0 + (uint32_t)((char*)(tens ? &S.st[sb].o[gg][0] : &S.st[sb].q[gg][0]) -
+                                             (char*)dkdv_smem);
+      // rows of head gg sit gg * HD elements further into each token's row
+      dma_tile<HD>(tens ? ro : rq, (uint32_t)(qt * 32), rstride, (uint32_t)(gg * HD * 2), dst, blk, lane);
+    }
+  };
+  float pl2 = INFINITY, pdl = 0.f;  // this thread's (head, row) of the next step's lse and D
+  auto fetch_ld = [&](int qt) {
+    if (tid < G * 32) {
+      const int gg = tid / 32, r = tid % 32;
+      const bool qv = qt * 32 + r < Kb;
+      const size_t at = (size_t)(hk * G + gg) * a.T + seq0 + qt * 32 + r;
+      pl2 = qv ? a.lse2[at] : INFINITY;  // P = 0 for rows past the sequence
+      pdl = qv ? a.delta[at] : 0.f;
+    }
+  };
+  auto put_ld = [&](int sb) {
+    if (tid < G * 32) {
+      S.l2[sb][tid / 32][tid % 32] = pl2;
+      S.dl[sb][tid / 32][tid % 32] = pdl;
+    }
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
     const int kt = pass == 0 ? p : nk - 1 - p;
     if (p >= (nk + 1) / 2 || (pass == 1 && kt == p)) break;  // uniform over the workgroup
     const int kb = kt * BK + 32 * ksub;                        // first key of this wave
     const int kj = kb + l31;
     const bool kval = kj < Kb;
-    // K and V of the wave's keys as B operands (column = key, k-slots = features)
     bf16x8 kfr[NS], vfr[NS];
     {
       const size_t off = ((size_t)(seq0 + (kval ? kj : 0)) * a.Hkv + hk) * HD + 8 * grp;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        kfr[s] = kval ? *reinterpret_cast<const bf16x8*>(a.k + off + 16 * s) : zero_bf16x8();
-        vfr[s] = kval ? *reinterpret_cast<const bf16x8*>(a.v + off + 16 * s) : zero_bf16x8();
+      for (int s_ = 0; s_ < NS; ++s_) {
+        kfr[s_] = kval ? *reinterpret_cast<const bf16x8*>(a.k + off + 16 * s_) : zero_bf16x8();
+        vfr[s_] = kval ? *reinterpret_cast<const bf16x8*>(a.v + off + 16 * s_) : zero_bf16x8();
       }
     }
     const float sj = kval ? a.s_c[seq0 + kj] : 0.f;
@@ -186,57 +253,53 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
     }
     float dl_acc = 0.f;
 
-    for (int qt = (kt * BK) / 32; qt < nq; ++qt) {
+    const int qt0 = (kt * BK) / 32;
+    __syncthreads();  // the stage buffers (and the reduction area aliasing them) are free
+    issue(qt0, 0);
+    fetch_ld(qt0);
+    put_ld(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int qt = qt0; qt < nq; ++qt) {
+      const int sb = (qt - qt0) & 1;
+      if (qt + 1 < nq) {
+        issue(qt + 1, sb ^ 1);
+        fetch_ld(qt + 1);
+      }
       const int q0 = qt * 32;
-      __syncthreads();  // the previous step's readers are done with the staging area
+      if (q0 + 31 >= kb) {  // some query of the step sees this wave's keys
+        const bf16* sq = S.st[sb].q[gi];
+        const bf16* so = S.st[sb].o[gi];
+        f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
 #pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const size_t src = ((size_t)(seq0 + q0) * a.Hq + hk * G + gg) * HD;
-        TL::stage(S.q[gg], a.q + src, (size_t)a.Hq * HD, 32, Kb - q0);
-        TL::stage(S.o[gg], a.dO + src, (size_t)a.Hq * HD, 32, Kb - q0);
-      }
-      if (tid < G * 32) {
-        const int gg = tid / 32, r = tid % 32;
-        const bool qv = q0 + r < Kb;
-        const size_t at = (size_t)(hk * G + gg) * a.T + seq0 + q0 + r;
-        S.l2[gg][r] = qv ? a.lse2[at] : INFINITY;  // P = 0 for rows past the sequence
-        S.dl[gg][r] = qv ? a.delta[at] : 0.f;
-      }
-      __syncthreads();
-      if (q0 + 31 < kb) continue;  // every query of the step precedes this wave's keys
-      f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
+        for (int s_ = 0; s_ < NS; ++s_) {
+          sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), kfr[s_], sacc);
+          pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), vfr[s_], pacc);
+        }
+        float P[16], dL[16];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc = mfma32(TL::chunk(S.q[gi], l31, 2 * s + grp), kfr[s], sacc);
-        pacc = mfma32(TL::chunk(S.o[gi], l31, 2 * s + grp), vfr[s], pacc);
-      }
-      float P[16], dL[16];
+        for (int r = 0; r < 16; ++r) {
+          const int qi = acc_row(r, grp);
+          const bool vis = kval && kj <= q0 + qi;
+          const float pr = vis ? exp2f(fmaf(c2, sacc[r], bias2) - S.l2[sb][gi][qi]) : 0.f;
+          P[r] = pr;
+          dL[r] = pr * (pacc[r] - S.dl[sb][gi][qi]);
+          dl_acc += dL[r];
+          dt_acc = fmaf(dL[r], sacc[r], dt_acc);
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = acc_row(r, grp);
-        const bool vis = kval && kj <= q0 + qi;
-        const float pr = vis ? exp2f(fmaf(c2, sacc[r], bias2) - S.l2[gi][qi]) : 0.f;
-        P[r] = pr;
-        dL[r] = pr * (pacc[r] - S.dl[gi][qi]);
-        dl_acc += dL[r];
-        dt_acc = fmaf(dL[r], sacc[r], dt_acc);
-      }
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 pb = pack8(P + 8 * ks), lb = pack8(dL + 8 * ks);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pb = pack8(P + 8 * ks), lb = pack8(dL + 8 * ks);
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          bf16x8 oa, qa;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int qi = 16 * ks + 8 * (j >> 2) + 4 * grp + (j & 3);
-            oa[j] = TL::elem(S.o[gi], qi, 32 * db + l31);
-            qa[j] = TL::elem(S.q[gi], qi, 32 * db + l31);
+          for (int db = 0; db < ND; ++db) {
+            dvT[db] = mfma32(tr_frag<HD>(so, ks, db, lane), pb, dvT[db]);
+            dkT[db] = mfma32(tr_frag<HD>(sq, ks, db, lane), lb, dkT[db]);
           }
-          dvT[db] = mfma32(oa, pb, dvT[db]);
-          dkT[db] = mfma32(qa, lb, dkT[db]);
         }
       }
+      if (qt + 1 < nq) put_ld(sb ^ 1);
+      wait_vmcnt<0>();
+      __syncthreads();
     }
     // per-key sums of this head: dL summed over the queries (both lane groups)
     const float dl_key = xsum32(dl_acc);
@@ -245,7 +308,6 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dkT[db][r] *= cnat;
-    __syncthreads();  // staging area free; reduction buffers may be written
     if constexpr (G > 1) {
       for (int src = 1; src < G; ++src) {
         if (gi == src) {
@@ -293,7 +355,6 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
         a.ds_part[(size_t)hk * a.T + seq0 + kj] = sum;
       }
     }
-    __syncthreads();
   }
   // this workgroup's dg and dt of each head of the group (zeros when it had no keys)
   dg_acc = wave_sum(dg_acc);
@@ -316,9 +377,9 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
 
 template <int HD>
 struct QSmem {
-  bf16 k[32 * HD];
-  bf16 v[32 * HD];
-  float s[32];
+  bf16 k[2][32 * HD];
+  bf16 v[2][32 * HD];
+  float s[2][64];
 };
 
 template <int G, int HD>
@@ -326,8 +387,10 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
   constexpr int WPH = 4 / G;  // 32-query sub-tiles per query tile
   constexpr int BQ = 32 * WPH;
   constexpr int NS = HD / 16, ND = HD / 32;
+  constexpr int NBLK = 32 * Tile<HD>::RB / 1024;  // 1 KB blocks per 32-row tile
+  constexpr int BPW = 2 * NBLK / 4;               // of them per wave and step (K and V)
   using TL = Tile<HD>;
-  __shared__ __attribute__((aligned(16))) QSmem<HD> S;
+  __shared__ __attribute__((aligned(1024))) QSmem<HD> S;
 
   const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, grp = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,6 +405,23 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
   const float cnat = a.t[h] * rsqrtf((float)HD);
   const float g2 = a.g[h] * TG_LOG2E;
 
+  const uint32_t rstride = (uint32_t)a.Hkv * HD * 2u;
+  const i32x4 rk = make_rsrc(a.k + (size_t)seq0 * a.Hkv * HD + (size_t)hk * HD, (uint32_t)Kb * rstride);
+  const i32x4 rv = make_rsrc(a.v + (size_t)seq0 * a.Hkv * HD + (size_t)hk * HD, (uint32_t)Kb * rstride);
+  const i32x4 rsc = make_rsrc(a.s_c + seq0, (uint32_t)Kb * 4u);
+  const uint32_t lk = lds_addr(&S.k[0][0]), lv = lds_addr(&S.v[0][0]), ls = lds_addr(&S.s[0][0]);
+  auto issue = [&](int kt, int sb) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int bi = w * BPW + i;
+      const int tens = bi / NBLK, blk = bi % NBLK;
+      dma_tile<HD>(tens ? rv : rk, (uint32_t)(kt * 32), rstride, 0u,
+                   (tens ? lv : lk) + (uint32_t)(sb * 32 * HD * 2), blk, lane);
+    }
+    if (w == 0)  // one score per lane (lanes past the 32 keys read zeros or another tile's keys; unused)
+      buf_dma4(rsc, (uint32_t)(kt * 32 + lane) * 4u, __builtin_amdgcn_readfirstlane(ls + (uint32_t)(sb * 256)));
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
     const int qt = pass == 0 ? p : nq - 1 - p;
     if (p >= (nq + 1) / 2 || (pass == 1 && qt == p)) break;  // uniform over the workgroup
@@ -352,9 +432,9 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
     {
       const size_t off = ((size_t)(seq0 + (qval ? qi : 0)) * a.Hq + h) * HD + 8 * grp;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        qfr[s] = qval ? *reinterpret_cast<const bf16x8*>(a.q + off + 16 * s) : zero_bf16x8();
-        ofr[s] = qval ? *reinterpret_cast<const bf16x8*>(a.dO + off + 16 * s) : zero_bf16x8();
+      for (int s_ = 0; s_ < NS; ++s_) {
+        qfr[s_] = qval ? *reinterpret_cast<const bf16x8*>(a.q + off + 16 * s_) : zero_bf16x8();
+        ofr[s_] = qval ? *reinterpret_cast<const bf16x8*>(a.dO + off + 16 * s_) : zero_bf16x8();
       }
     }
     const size_t at = (size_t)h * a.T + seq0 + (qval ? qi : 0);
@@ -364,46 +444,41 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
 #pragma unroll
     for (int db = 0; db < ND; ++db) dqT[db] = zero_f32x16();
     const int last_key = min(qt * BQ + BQ, Kb) - 1;
-    for (int kt = 0; kt * 32 <= last_key; ++kt) {
+    const int nkt = last_key / 32 + 1;
+    __syncthreads();  // the previous pass's readers are done with the buffers
+    issue(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int sb = kt & 1;
+      if (kt + 1 < nkt) issue(kt + 1, sb ^ 1);
       const int k0 = kt * 32;
-      __syncthreads();
-      {
-        const size_t src = ((size_t)(seq0 + k0) * a.Hkv + hk) * HD;
-        TL::stage(S.k, a.k + src, (size_t)a.Hkv * HD, 32, Kb - k0);
-        TL::stage(S.v, a.v + src, (size_t)a.Hkv * HD, 32, Kb - k0);
-        if (tid < 32) S.s[tid] = k0 + tid < Kb ? a.s_c[seq0 + k0 + tid] : 0.f;
-      }
-      __syncthreads();
-      if (k0 > q0 + 31) continue;  // every key of the tile follows this wave's queries
-      f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
+      if (k0 <= q0 + 31) {  // some key of the tile precedes a query of this wave
+        const bf16* sk = S.k[sb];
+        f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc = mfma32(TL::chunk(S.k, l31, 2 * s + grp), qfr[s], sacc);
-        pacc = mfma32(TL::chunk(S.v, l31, 2 * s + grp), ofr[s], pacc);
-      }
-      float dL[16];
+        for (int s_ = 0; s_ < NS; ++s_) {
+          sacc = mfma32(TL::chunk(sk, l31, 2 * s_ + grp), qfr[s_], sacc);
+          pacc = mfma32(TL::chunk(S.v[sb], l31, 2 * s_ + grp), ofr[s_], pacc);
+        }
+        float dL[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = acc_row(r, grp);
-        const int kj = k0 + kr;
-        const bool vis = qval && kj <= qi && kj < Kb;
-        const float pr = vis ? exp2f(fmaf(c2, sacc[r], g2 * S.s[kr]) - l2) : 0.f;
-        dL[r] = pr * (pacc[r] - dl);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int kr = acc_row(r, grp);
+          const int kj = k0 + kr;
+          const bool vis = qval && kj <= qi && kj < Kb;
+          const float pr = vis ? exp2f(fmaf(c2, sacc[r], g2 * S.s[sb][kr]) - l2) : 0.f;
+          dL[r] = pr * (pacc[r] - dl);
+        }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 lb = pack8(dL + 8 * ks);
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 lb = pack8(dL + 8 * ks);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          bf16x8 ka;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int kr = 16 * ks + 8 * (j >> 2) + 4 * grp + (j & 3);
-            ka[j] = TL::elem(S.k, kr, 32 * db + l31);
-          }
-          dqT[db] = mfma32(ka, lb, dqT[db]);
+          for (int db = 0; db < ND; ++db) dqT[db] = mfma32(tr_frag<HD>(sk, ks, db, lane), lb, dqT[db]);
         }
       }
+      wait_vmcnt<0>();
+      __syncthreads();
     }
     if (qval) {
       float* dqr = a.dq + ((size_t)(seq0 + qi) * a.Hq + h) * HD;
