@@ -13,9 +13,10 @@
 // k, q, alpha, beta), so the recurrence runs in parallel over rows and stays
 // sequential over tokens. A workgroup takes RPWG rows of one (sequence, head);
 // a row's state lives in the registers of dk / 8 lanes (8 fp32 each). Per
-// token, S k, |k|^2 and |q|^2 finish with DPP butterflies inside those lanes;
-// the normalisation folds into two scalars, so only S k -> write sits on the
-// serial chain (the read S q^ overlaps the next token). k, q, v, alpha and
+// token, S k finishes with DPP butterflies inside those lanes; 1/|k| and
+// 1/(|q| sqrt(dk)) are computed for the whole chunk while it is staged, so
+// only S k -> write sits on the serial chain (the read S q^ overlaps the next
+// token, whose operands are read from LDS during this one). k, q, v, alpha and
 // beta of 32-token chunks are staged in LDS, double-buffered: the next chunk's
 // global loads are issued before the current chunk is processed and land in
 // the other buffer after it; outputs collect in LDS and leave coalesced.
@@ -38,12 +39,30 @@ __device__ __forceinline__ float dpp(float x) {
 // sum over aligned groups of N lanes (8 or 16); every lane of a group gets it
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 8 || N == 16, "group size");
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
   v += dpp<0xB1>(v);                          // quad permute [1,0,3,2]
   v += dpp<0x4E>(v);                          // quad permute [2,3,0,1]
   v += dpp<0x141>(v);                         // row half mirror
-  if constexpr (N == 16) v += dpp<0x140>(v);  // row mirror
+  if constexpr (N >= 16) v += dpp<0x140>(v);  // row mirror
+  if constexpr (N == 32) v += __shfl_xor(v, 16, 64);
   return v;
+}
+
+// sum of squares of the 8 elements in 16 bytes of T
+__device__ __forceinline__ float sq8(const u32x4& r, bf16) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(r[i] << 16), hi = __uint_as_float(r[i] & 0xffff0000u);
+    acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+  }
+  return acc;
+}
+__device__ __forceinline__ float sq8(const u32x4& r, float) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(r[i]), __uint_as_float(r[i]), acc);
+  return acc;
 }
 
 template <typename T>
@@ -80,6 +99,7 @@ struct Smem {
   T q[2][C][DK];
   float v[2][C][RPWG];
   float a[2][C], b[2][C];
+  float nk[2][C], nq[2][C];  // 1/|k| and 1/(|q| sqrt(dk)) of each token
   float o[C][RPWG];
 };
 
@@ -164,10 +184,20 @@ __global__ __launch_bounds__(NT) void gdn_kernel(Args A) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + i * NT;
+      // the KCH pieces of a row sit in KCH consecutive lanes (KCH divides 64 and NT):
+      // their sums of squares reduce inside those lanes (all lanes take part)
+      const float n2 = group_sum<KCH>(p < NKQ ? sq8(pk[i], T{}) : 0.f);
       if (p < NKQ) {
         const int which = p / (CT * KCH), r = (p / KCH) % CT, c16 = p % KCH;
         char* dst = reinterpret_cast<char*>(which ? &S.q[buf][r][0] : &S.k[buf][r][0]) + 16 * c16;
         *reinterpret_cast<u32x4*>(dst) = pk[i];
+        if (c16 == 0) {
+          const float inv = rsqrtf(n2 + EPS);
+          if (which)
+            S.nq[buf][r] = inv * rsqrtf((float)DK);
+          else
+            S.nk[buf][r] = inv;
+        }
       }
     }
 #pragma unroll
@@ -191,29 +221,44 @@ __global__ __launch_bounds__(NT) void gdn_kernel(Args A) {
     const int buf = c & 1;
     if (c + 1 < nchunk) load_chunk(c + 1);  // in flight while this chunk is processed
     const int nt = min(CT, L - c * CT);
-    for (int t = 0; t < nt; ++t) {
-      float kx[8], qx[8];
+    // operands of token t + 1 are read while token t is computed
+    float kx[8], qx[8], al, be, vi, ik, iq;
+    auto fetch = [&](int t) {
       to_f32x8<T>(&S.k[buf][t][ds * 8], kx);
       to_f32x8<T>(&S.q[buf][t][ds * 8], qx);
-      const float al = S.a[buf][t], be = S.b[buf][t], vi = S.v[buf][t][rloc];
-      float dk0 = 0.f, dk1 = 0.f, nk = 0.f, nq = 0.f;
+      al = S.a[buf][t];
+      be = S.b[buf][t];
+      vi = S.v[buf][t][rloc];
+      ik = S.nk[buf][t];
+      iq = S.nq[buf][t];
+    };
+    fetch(0);
+    for (int t = 0; t < nt; ++t) {
+      float ck[8], cq[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ck[e] = kx[e];
+        cq[e] = qx[e];
+      }
+      const float cal = al, cbe = be, cvi = vi, cik = ik, ciq = iq;
+      if (t + 1 < nt) fetch(t + 1);
+      float dk0 = 0.f, dk1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        dk0 = fmaf(st[e], kx[e], dk0);
-        dk1 = fmaf(st[e + 1], kx[e + 1], dk1);
-        nk = fmaf(kx[e], kx[e], fmaf(kx[e + 1], kx[e + 1], nk));
-        nq = fmaf(qx[e], qx[e], fmaf(qx[e + 1], qx[e + 1], nq));
+        dk0 = fmaf(st[e], ck[e], dk0);
+        dk1 = fmaf(st[e + 1], ck[e + 1], dk1);
       }
-      const float dkr = group_sum<LPR>(dk0 + dk1);
-      const float ik = rsqrtf(group_sum<LPR>(nk) + EPS);
-      const float u = al * dkr * ik;             // (alpha S) k^
-      const float cc = be * (vi - u) * ik;       // write strength along the raw k
+      const float u = cal * group_sum<LPR>(dk0 + dk1) * cik;  // (alpha S) k^
+      const float cc = cbe * (cvi - u) * cik;                 // write strength along the raw k
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st[e] = fmaf(cc, kx[e], al * st[e]);
-      float od = 0.f;
+      for (int e = 0; e < 8; ++e) st[e] = fmaf(cc, ck[e], cal * st[e]);
+      float od0 = 0.f, od1 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) od = fmaf(st[e], qx[e], od);
-      od = group_sum<LPR>(od) * rsqrtf(group_sum<LPR>(nq) + EPS) * qscale;
+      for (int e = 0; e < 8; e += 2) {
+        od0 = fmaf(st[e], cq[e], od0);
+        od1 = fmaf(st[e + 1], cq[e + 1], od1);
+      }
+      const float od = group_sum<LPR>(od0 + od1) * ciq;
       if (ds == 0) S.o[t][rloc] = od;
     }
     __syncthreads();  // outputs complete; the other buffer is no longer read
