@@ -15,8 +15,8 @@
 //     dw2, db1, db2;
 //  3. dh = dz W1 by the same GEMM on a transposed copy of W1;
 //  4. dW1 = dz^T h: a split-K MFMA kernel over token chunks (the reduction
-//     runs over tokens, so both operands are read down their columns from
-//     LDS slabs with padded rows), fp32 partials per chunk;
+//     runs over tokens, so both operands come from transposing reads of LDS
+//     slabs with padded rows, double-buffered), fp32 partials per chunk;
 //  5. fixed-order sums of the partials (deterministic).
 #include "tg_common.hpp"
 #include "tg_internal.hpp"
@@ -29,7 +29,8 @@ constexpr int ROWS_PER_BLOCK = 64;  // tokens per block of pass 2
 constexpr int CHUNK = 2048;         // tokens per split of pass 4
 constexpr int TILE = 128;           // output tile of pass 4 (m and n)
 constexpr int SLAB = 32;            // tokens per LDS slab
-constexpr int PADW = TILE + 8;      // padded LDS row (elements): the two lane groups' rows land 32 banks apart
+constexpr int PADW = TILE + 32;     // padded LDS row (elements): 320 bytes, so the four rows of one
+                                    // transposing read start 64 bytes apart modulo the 256-byte bank width
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float gelu_grad(float x) {
@@ -65,18 +66,33 @@ __global__ __launch_bounds__(NT) void dz_kernel(const bf16* __restrict__ z, cons
   if (threadIdx.x == 0) pb[2 * H1] = du_sum;
 }
 
-// sums over the pass-2 blocks: dw2, db1 [H1], db2
+// sums over the pass-2 blocks: dw2, db1 [H1], db2. A workgroup takes 32 of
+// the 2*H1+1 entries; 8 lanes per entry sum every 8th block (four loads in
+// flight each), then the 8 partial sums combine in a fixed order.
 __global__ __launch_bounds__(NT) void small_reduce_kernel(const float* __restrict__ part, int nblk, int H1,
                                                           float* __restrict__ dw2, float* __restrict__ db1,
                                                           float* __restrict__ db2) {
-  const int i = blockIdx.x * NT + threadIdx.x;  // over 2 * H1 + 1 entries
-  if (i > 2 * H1) return;
-  float acc = 0.f;
-  for (int b = 0; b < nblk; ++b) acc += part[(size_t)b * (2 * H1 + 1) + i];
-  if (i < H1)
-    dw2[i] = acc;
-  else if (i < 2 * H1)
-    db1[i - H1] = acc;
+  const int ne = 2 * H1 + 1;
+  const int e = blockIdx.x * 32 + threadIdx.x / 8, j = threadIdx.x % 8;
+  const int ec = min(e, ne - 1);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int b = j;
+  for (; b + 24 < nblk; b += 32) {
+    a0 += part[(size_t)b * ne + ec];
+    a1 += part[(size_t)(b + 8) * ne + ec];
+    a2 += part[(size_t)(b + 16) * ne + ec];
+    a3 += part[(size_t)(b + 24) * ne + ec];
+  }
+  for (; b < nblk; b += 8) a0 += part[(size_t)b * ne + ec];
+  float acc = (a0 + a1) + (a2 + a3);
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  if (j != 0 || e >= ne) return;
+  if (e < H1)
+    dw2[e] = acc;
+  else if (e < 2 * H1)
+    db1[e - H1] = acc;
   else
     db2[0] = acc;
 }
@@ -99,12 +115,30 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const bf16* __restrict__ 
   }
 }
 
+// 8 rows (k-slots) x 1 column (lane) of a [SLAB][PADW] bf16 slab as an MFMA
+// operand: lane l takes column c0 + l%32 and rows 16*ks + {0..3, 8..11} +
+// 4*(l/32) (the same row order for both operands, so it cancels); two
+// ds_read_tr16_b64: within 16 lanes, lane 4e+m addresses row e, columns
+// 4m .. 4m+3, and lane i receives column i of rows 0..3.
+__device__ __forceinline__ bf16x8 slab_frag(const bf16 (*slab)[PADW], int ks, int c0, int lane) {
+  const int vg = (lane >> 4) & 3, vs = lane & 15;
+  const int r = 16 * ks + 4 * (vg >> 1) + (vs >> 2);
+  const int c = c0 + 16 * (vg & 1) + 4 * (vs & 3);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(&slab[r][c]));
+  const bf16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(&slab[r + 8][c]));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // pass 4: part[split][m][n] = sum over the split's tokens t of A[t][m] B[t][n]
-// (A = dz [T, M], B = h [T, N]); 4 waves of 64 x 64 on a 128 x 128 tile
+// (A = dz [T, M], B = h [T, N]); 4 waves of 64 x 64 on a 128 x 128 tile; the
+// next slab's rows are loaded into registers while the current one is
+// multiplied, then written to the other LDS buffer (one barrier per slab)
 __global__ __launch_bounds__(NT) void tn_kernel(const bf16* __restrict__ A, const bf16* __restrict__ Bm,
                                                 int64_t T, int M, int N, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) bf16 sa[SLAB][PADW];
-  __shared__ __attribute__((aligned(16))) bf16 sb[SLAB][PADW];
+  __shared__ __attribute__((aligned(16))) bf16 sa[2][SLAB][PADW];
+  __shared__ __attribute__((aligned(16))) bf16 sb[2][SLAB][PADW];
+  constexpr int PPT = SLAB * TILE / 8 / NT;  // 16-byte pieces per thread and operand
   const int ntn = (N + TILE - 1) / TILE, ntm = (M + TILE - 1) / TILE;
   const int bid = blockIdx.x;
   const int tn = bid % ntn, tm = (bid / ntn) % ntm, split = bid / (ntn * ntm);
@@ -117,36 +151,48 @@ __global__ __launch_bounds__(NT) void tn_kernel(const bf16* __restrict__ A, cons
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero_f32x16();
-
-  for (int64_t ts = t0; ts < t1; ts += SLAB) {
-    __syncthreads();
-    // stage 32 tokens x 128 columns of A and of B (16-byte pieces; zero past the ends)
-    for (int i = tid; i < SLAB * TILE / 8; i += NT) {
-      const int r = i / (TILE / 8), c = (i % (TILE / 8)) * 8;
+  u32x4 pa[PPT], pb[PPT];
+  auto load = [&](int64_t ts) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int q = tid + i * NT, r = q / (TILE / 8), c = (q % (TILE / 8)) * 8;
       const int64_t t = ts + r;
-      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-      if (t < t1 && m0 + c < M) va = *reinterpret_cast<const u32x4*>(A + (size_t)t * M + m0 + c);
-      if (t < t1 && n0 + c < N) vb = *reinterpret_cast<const u32x4*>(Bm + (size_t)t * N + n0 + c);
-      *reinterpret_cast<u32x4*>(&sa[r][c]) = va;
-      *reinterpret_cast<u32x4*>(&sb[r][c]) = vb;
+      pa[i] = u32x4{0u, 0u, 0u, 0u};
+      pb[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t < t1 && m0 + c < M) pa[i] = *reinterpret_cast<const u32x4*>(A + (size_t)t * M + m0 + c);
+      if (t < t1 && n0 + c < N) pb[i] = *reinterpret_cast<const u32x4*>(Bm + (size_t)t * N + n0 + c);
     }
-    __syncthreads();
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int q = tid + i * NT, r = q / (TILE / 8), c = (q % (TILE / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&sa[buf][r][c]) = pa[i];
+      *reinterpret_cast<u32x4*>(&sb[buf][r][c]) = pb[i];
+    }
+  };
+  load(t0);
+  put(0);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t ts = t0; ts < t1; ts += SLAB, buf ^= 1) {
+    const bool more = ts + SLAB < t1;
+    if (more) load(ts + SLAB);
 #pragma unroll
     for (int ks = 0; ks < SLAB / 16; ++ks) {
       bf16x8 af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 16 * ks + 8 * grp + j;
-          af[i][j] = sa[t][wm * 64 + 32 * i + l31];
-          bf[i][j] = sb[t][wn * 64 + 32 * i + l31];
-        }
+      for (int i = 0; i < 2; ++i) {
+        af[i] = slab_frag(sa[buf], ks, wm * 64 + 32 * i, lane);
+        bf[i] = slab_frag(sb[buf], ks, wn * 64 + 32 * i, lane);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
     }
+    if (more) put(buf ^ 1);
+    __syncthreads();
   }
   // acc[i][j]: lane l holds column n = n0 + wn*64 + 32j + l31, rows m = m0 + wm*64 + 32i + row(r)
   float* pp = part + (size_t)split * M * N;
@@ -223,8 +269,8 @@ hipError_t launch_score_bwd(const void* h, int64_t T, int D, int H1, const void*
   dz_kernel<<<dim3((unsigned)L.nblk), dim3(NT), 0, stream>>>(z, static_cast<const bf16*>(b1),
                                                             static_cast<const bf16*>(w2), s, ds, T, H1, dz, part2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  small_reduce_kernel<<<dim3((unsigned)((2 * H1 + 1 + NT - 1) / NT)), dim3(NT), 0, stream>>>(part2, L.nblk, H1,
-                                                                                            dw2, db1, db2);
+  small_reduce_kernel<<<dim3((unsigned)((2 * H1 + 1 + 31) / 32)), dim3(NT), 0, stream>>>(part2, L.nblk, H1, dw2,
+                                                                                          db1, db2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   transpose_kernel<<<dim3((unsigned)(((H1 + 63) / 64) * ((D + 63) / 64))), dim3(NT), 0, stream>>>(
       static_cast<const bf16*>(W1), w1t, H1, D);

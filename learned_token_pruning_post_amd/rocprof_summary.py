@@ -153,6 +153,7 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("--cmd", required=True, help="the command that produced the csv")
     s.add_argument("--title", default="Kernel durations")
+    s.add_argument("--top", type=int, default=20, help="rows of the table (longest total first)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -164,7 +165,7 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd_name == "stats":
-        print("# %s\n\nCommand:\n\n```\n%s\n```\n\n%s" % (a.title, a.cmd, stats_table(a.csv)))
+        print("# %s\n\nCommand:\n\n```\n%s\n```\n\n%s" % (a.title, a.cmd, stats_table(a.csv, a.top)))
         return
     res = traffic(a.fetch, a.write, a.kernel if len(a.kernel) > 1 else a.kernel[0], a.copy_bytes, a.stage)
     res["stage"] = a.stage
