@@ -366,9 +366,12 @@ def gdn_timing(torch, tg, w, reps=3):
     """The hybrid variant's Gated DeltaNet mixer (tg_gdn_fwd) over one sequence
     of the kept-token count, at the model's head shapes (one head per query
     head, dk = dv = head dim): seeded random operands, HIP events on the launch
-    stream. Algorithmic work per token and head: S k, the rank-1 write (a
-    multiply and an FMA per state element) and S q, 6 dk dv flops (fp32, on
-    the vector ALUs: a sequential recurrence, no matmul)."""
+    stream. bf16 runs the chunked form (64-token chunks): a parallel prep
+    kernel over all chunks and heads, then a scan over the chunks of each
+    sequence, head and 32 state rows. Work reported two ways: the token
+    recurrence's 6 dk dv flops per token and head, and the matrix-core flops
+    the chunked form performs (per chunk and head: K K^T, Q K^T, two halves of
+    T times K^ and V, then U, the two output products and the state update)."""
     dm = w.dims
     dt = torch.bfloat16 if dm.dtype == "bf16" else torch.float32
     K, H, d = w.K[0], dm.Hq, dm.d
@@ -379,24 +382,33 @@ def gdn_timing(torch, tg, w, reps=3):
     be = torch.rand((K, H), generator=gen, device="cuda")
     cu = torch.tensor([0, K], dtype=torch.int32, device="cuda")
     o = torch.empty_like(v)
+    need = tg.lib().tg_gdn_workspace_size(K, 1, H, d, d, tg.dtype_code(dt))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     ev = HipEvents(2)
-    tg.gdn_fwd(q, k, v, al, be, cu, o=o)
+    tg.gdn_fwd(q, k, v, al, be, cu, o=o, ws=ws)
     torch.cuda.synchronize()
     ev.record(0, stream)
     for _ in range(reps):
-        tg.gdn_fwd(q, k, v, al, be, cu, o=o)
+        tg.gdn_fwd(q, k, v, al, be, cu, o=o, ws=ws)
     ev.record(1, stream)
     torch.cuda.synchronize()
     us = ev.ms(0, 1) / reps * 1e3
     ev.close()
     flop = 6.0 * K * H * d * d
-    tf = flop / (us * 1e-6) / 1e12
-    return {"us": round(us, 1), "tokens": K, "heads": H, "dk": d, "dv": d, "tflops": round(tf, 2),
-            "frac_fp32_vector_peak": round(tf / PEAK_F32_TFLOPS, 4),
-            "workgroups": H * (d // (4 * (64 // (d // 8)))),
-            "note": "one sequence: the recurrence is sequential over its tokens, parallel over heads and "
-                    "state rows only; mean of %d calls after a warm-up" % reps}
+    C = 64
+    mfma_flop = ((K + C - 1) // C) * H * (2.0 * C * C * d * 2 + 2 * (2.0 * C * C * d) * 2
+                                         + 2.0 * C * d * d * 3 + 2.0 * C * C * d)
+    out = {"us": round(us, 1), "tokens": K, "heads": H, "dk": d, "dv": d,
+           "recurrence_tflops": round(flop / (us * 1e-6) / 1e12, 3),
+           "workspace_mb": round(need / 1e6, 1),
+           "note": "one sequence; mean of %d calls after a warm-up" % reps}
+    if dt == torch.bfloat16:
+        tf = mfma_flop / (us * 1e-6) / 1e12
+        out.update({"chunked_mfma_gflop": round(mfma_flop / 1e9, 2), "mfma_tflops": round(tf, 2),
+                    "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "scan_workgroups": H * (d // 32)})
+    return out
 
 
 DECODE_BATCH = 16  # sequences per decode step

@@ -492,16 +492,23 @@ tg_status tg_compact_scores_bwd(const float* ds_c, const int32_t* kept_idx, int6
  *   k^ = k / sqrt(|k|^2 + 1e-6),  q^ = q / (sqrt(|q|^2 + 1e-6) sqrt(dk))
  *   S <- alpha S;  S <- S + beta (v - S k^) k^T;  o = S q^
  *  q, k [T, H, dk], v [T, H, dv], o [T, H, dv] out: dtype; alpha, beta
- *  [T, H] fp32 (decay and write strength of each token and head); d_cu
- *  [B+1] int32 (device); state_in / state_out [B, H, dv, dk] fp32, optional
- *  (NULL: start from zero / do not write).
- * Supported: dk in {64, 128}, dv % 32 == 0; q and k 16-byte aligned. No
- * workspace.
+ *  [T, H] fp32 (decay and write strength of each token and head; alpha in
+ *  [0, 1]); d_cu [B+1] int32 (device), with d_cu[B] <= T (rows at or past T
+ *  are never read or written; with T = 0 the row operands may be NULL); state_in / state_out [B, H, dv, dk] fp32,
+ *  optional (NULL: start from zero / do not write), 16-byte aligned.
+ * bf16 runs the chunked form of the recurrence on the matrix cores (chunks of
+ * 64 tokens; a decay below e^-80 counts as e^-80 inside a chunk); its
+ * workspace is tg_gdn_workspace_size() bytes, 256-byte aligned (0 when T is
+ * 0). fp32 runs the token recurrence itself and takes no workspace (ws may
+ * be NULL). Splitting a sequence over calls at a multiple of 64 tokens, with
+ * the state carried, gives the same bits as one call.
+ * Supported: dk in {64, 128}, dv % 32 == 0; q and k 16-byte aligned.
  * ------------------------------------------------------------------------- */
+size_t tg_gdn_workspace_size(int64_t T, int B, int H, int dk, int dv, tg_dtype dtype);
 tg_status tg_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                     const float* beta, const int32_t* d_cu, int B, int H, int dk, int dv,
-                     tg_dtype dtype, const float* state_in, void* o, float* state_out,
-                     hipStream_t stream);
+                     const float* beta, const int32_t* d_cu, int64_t T, int B, int H, int dk,
+                     int dv, tg_dtype dtype, const float* state_in, void* o, float* state_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
  * Decode attention over the pruned K/V cache — [TC] engineering section:

@@ -40,7 +40,7 @@ ABI_FUNCTIONS = (
     "tg_decode_attn_workspace_size", "tg_decode_attn_fwd",
     "tg_gated_attn_bwd_workspace_size", "tg_gated_attn_bwd",
     "tg_gate_score_bwd_workspace_size", "tg_gate_score_bwd", "tg_compact_scores_bwd",
-    "tg_gdn_fwd",
+    "tg_gdn_workspace_size", "tg_gdn_fwd",
 )
 LAYER_STAGES = 8
 LAYER_STAGE_NAMES = ("rope_table", "rmsnorm_attn", "qkv_rope_kv", "gated_attn", "o_proj_resid",
@@ -152,7 +152,9 @@ def lib() -> ctypes.CDLL:
     L.tg_gate_score_bwd.restype = i32
     L.tg_compact_scores_bwd.argtypes = [vp, vp, i64, i64, vp, vp]
     L.tg_compact_scores_bwd.restype = i32
-    L.tg_gdn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.tg_gdn_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.tg_gdn_workspace_size.restype = sz
+    L.tg_gdn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.tg_gdn_fwd.restype = i32
     L.tg_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.tg_decode_attn_workspace_size.restype = sz
@@ -348,7 +350,7 @@ def compact_scores_bwd(ds_c, kept, T_in: int, ds=None):
     return ds
 
 
-def gdn_fwd(q, k, v, alpha, beta, cu, state_in=None, o=None, state_out=None, want_state=False):
+def gdn_fwd(q, k, v, alpha, beta, cu, state_in=None, o=None, state_out=None, want_state=False, ws=None):
     """tg_gdn_fwd: the Gated DeltaNet mixer over the packed sequences of cu.
     Returns (o, state_out)."""
     T, H, dk = q.shape
@@ -358,8 +360,13 @@ def gdn_fwd(q, k, v, alpha, beta, cu, state_in=None, o=None, state_out=None, wan
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if want_state and state_out is None:
         state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    _check(lib().tg_gdn_fwd(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(cu), B, H, dk, dv, dtype_code(q.dtype),
-                            _p(state_in), _p(o), _p(state_out), _stream()), "tg_gdn_fwd")
+    code = dtype_code(q.dtype)
+    need = lib().tg_gdn_workspace_size(T, B, H, dk, dv, code)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().tg_gdn_fwd(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(cu), T, B, H, dk, dv, code,
+                            _p(state_in), _p(o), _p(state_out), _p(ws), ws.numel() if ws is not None else 0,
+                            _stream()), "tg_gdn_fwd")
     return o, state_out
 
 

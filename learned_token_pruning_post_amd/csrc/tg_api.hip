@@ -365,21 +365,35 @@ tg_status tg_compact_scores_bwd(const float* ds_c, const int32_t* kept_idx, int6
 // Gated DeltaNet mixer of the hybrid variant
 // ---------------------------------------------------------------------------
 
+size_t tg_gdn_workspace_size(int64_t T, int B, int H, int dk, int dv, tg_dtype dtype) {
+  if (dtype != TG_BF16 || T <= 0 || B <= 0 || H <= 0 || !tg::gdn_supported(dk, dv)) return 0;
+  return tg::gdn_chunk_workspace_bytes(T, B, H, dk, dv);
+}
+
 tg_status tg_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
-                     const int32_t* d_cu, int B, int H, int dk, int dv, tg_dtype dtype, const float* state_in,
-                     void* o, float* state_out, hipStream_t stream) {
-  TG_CHECK(B >= 0 && H > 0 && dk > 0 && dv > 0, TG_ERR_INVALID_ARG);
+                     const int32_t* d_cu, int64_t T, int B, int H, int dk, int dv, tg_dtype dtype,
+                     const float* state_in, void* o, float* state_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  TG_CHECK(B >= 0 && H > 0 && dk > 0 && dv > 0 && T >= 0 && T <= INT_MAX, TG_ERR_INVALID_ARG);
   TG_CHECK(dtype_ok(dtype), TG_ERR_UNSUPPORTED);
   TG_CHECK(tg::gdn_supported(dk, dv), TG_ERR_UNSUPPORTED);
   TG_CHECK((int64_t)B * H * (dv / 16) <= INT_MAX, TG_ERR_UNSUPPORTED);
+  TG_CHECK(((T + 63) / 64 + B) * (int64_t)H <= INT_MAX, TG_ERR_UNSUPPORTED);
   if (B == 0) return TG_OK;
-  TG_CHECK(q && k && v && alpha && beta && d_cu && o, TG_ERR_INVALID_ARG);
+  TG_CHECK(d_cu && (T == 0 || (q && k && v && o && alpha && beta)), TG_ERR_INVALID_ARG);
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
-  TG_CHECK(a16(q) && a16(k), TG_ERR_INVALID_ARG);
+  TG_CHECK(a16(q) && a16(k) && a16(state_in) && a16(state_out), TG_ERR_INVALID_ARG);
+  const bool bf = dtype == TG_BF16;
+  if (bf && T > 0) {
+    const size_t need = tg::gdn_chunk_workspace_bytes(T, B, H, dk, dv);
+    TG_CHECK(ws && ws_bytes >= need && ((uintptr_t)ws & 255u) == 0, TG_ERR_WORKSPACE);
+  }
   tg_status a = check_arch();
   if (a != TG_OK) return a;
-  return launched(tg::launch_gdn(q, k, v, alpha, beta, d_cu, B, H, dk, dv, dtype == TG_BF16, state_in, o,
-                                 state_out, stream));
+  if (bf)
+    return launched(tg::launch_gdn_chunked(q, k, v, alpha, beta, d_cu, T, B, H, dk, dv, state_in, o, state_out,
+                                           ws, stream));
+  return launched(tg::launch_gdn(q, k, v, alpha, beta, d_cu, B, H, dk, dv, false, state_in, o, state_out, stream));
 }
 
 // ---------------------------------------------------------------------------

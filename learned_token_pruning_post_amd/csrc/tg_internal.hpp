@@ -147,5 +147,10 @@ bool gdn_supported(int dk, int dv);
 hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                       const int32_t* cu, int B, int H, int dk, int dv, bool is_bf16, const float* state_in,
                       void* o, float* state_out, hipStream_t stream);
+// chunked form for bf16 (matrix cores): workspace of chunk records
+size_t gdn_chunk_workspace_bytes(int64_t T, int B, int H, int dk, int dv);
+hipError_t launch_gdn_chunked(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                              const int32_t* cu, int64_t T, int B, int H, int dk, int dv, const float* state_in,
+                              void* o, float* state_out, void* ws, hipStream_t stream);
 
 }  // namespace tg

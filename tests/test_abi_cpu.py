@@ -237,12 +237,18 @@ def test_scorer_backward_argument_errors(L):
 def test_gdn_argument_errors(L):
     f = L.tg_gdn_fwd
 
-    def call(B=1, H=4, dk=128, dv=128, dt=1, q=FAKE, o=FAKE):
-        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, B, H, dk, dv, dt, None, o, None, None)
+    def call(B=1, H=4, dk=128, dv=128, dt=1, q=FAKE, o=FAKE, T=1000, st=None, ws=None, nws=0):
+        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, T, B, H, dk, dv, dt, st, o, None, ws, nws, None)
     assert call(dk=96) == UNSUP and call(dv=48) == UNSUP and call(dt=5) == UNSUP
-    assert call(H=0) == INVALID and call(B=-1) == INVALID
+    assert call(H=0) == INVALID and call(B=-1) == INVALID and call(T=-1) == INVALID
     assert call(q=None) == INVALID and call(o=None) == INVALID
     assert call(q=ctypes.c_void_p(0x100004)) == INVALID
+    assert call(st=ctypes.c_void_p(0x100008)) == INVALID       # the state is read 16 bytes at a time
+    need = L.tg_gdn_workspace_size(1000, 1, 4, 128, 128, 1)
+    assert need > 0 and L.tg_gdn_workspace_size(1000, 1, 4, 128, 128, 0) == 0   # fp32: no workspace
+    assert L.tg_gdn_workspace_size(0, 1, 4, 128, 128, 1) == 0
+    assert call() == WS and call(ws=FAKE, nws=need - 1) == WS                 # bf16 needs the chunk records
+    assert call(ws=ctypes.c_void_p(0x100010), nws=need) == WS                 # 256-byte aligned
     assert call(B=0) == OK
 
 

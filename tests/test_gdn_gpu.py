@@ -3,6 +3,9 @@ against the fp64 oracle (Tencent Cloud TokenGate article, section on the gate
 position: a GDN layer above the gate has no logits to bias and runs on the
 kept tokens). Outputs within atol 2e-2 / rtol 1e-2 (bf16) or 1e-4 (fp32);
 the fp32 state within 1e-4 / 1e-4 for fp32 inputs and the bf16 bound for bf16.
+bf16 runs the chunked form (64-token chunks, matrix cores), fp32 the token
+recurrence: the cases cover partial chunks, empty and one-token sequences,
+dv not a multiple of dk, a decay of exactly 0 and a carried state.
 """
 import numpy as np
 import pytest
@@ -37,6 +40,7 @@ def _case(seed, lens, H, dk, dv, dtype):
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 128, 64),
+                                         ("bf16", 128, 96), ("bf16", 64, 160),
                                          ("f32", 128, 128), ("f32", 64, 96)])
 def test_gdn_matches_oracle_ragged(dtype, dk, dv):
     lens = [300, 0, 1, 77, 1000]
@@ -49,24 +53,73 @@ def test_gdn_matches_oracle_ragged(dtype, dk, dv):
     say("  gdn", dtype, "dk", dk, "dv", dv, "max err o %.3g state %.3g" % (e, es))
 
 
-def test_gdn_state_carries_across_calls():
+@pytest.mark.parametrize("dtype,cut", [("bf16", (384, 64)), ("f32", (400, 100))])
+def test_gdn_state_carries_across_calls(dtype, cut):
+    """Two sequences split over two calls with the state carried: the same bits
+    as one call (bf16 splits at multiples of the 64-token chunk, so the chunks
+    are the same; the fp32 recurrence splits anywhere)."""
     lens = [700, 129]
-    dev, cu = _case(72, lens, 4, 128, 128, "bf16")
+    dev, cu = _case(72, lens, 4, 128, 128, dtype)
     o, st = tg.gdn_fwd(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["cu"], want_state=True)
-    # the same sequences split in two calls: first 400 / 100 tokens, then the rest from the carried state
-    first = np.array([0, 400, 500], np.int32)
-    idx1 = np.r_[0:400, 700:800]
-    idx2 = np.r_[400:700, 800:829]
+    a, b = cut
+    idx1 = np.r_[0:a, 700:700 + b]
+    idx2 = np.r_[a:700, 700 + b:829]
     pick = lambda t, idx: t[torch.from_numpy(idx).cuda()].contiguous()
     o1, s1 = tg.gdn_fwd(*(pick(dev[n], idx1) for n in ("q", "k", "v", "alpha", "beta")),
-                        torch.from_numpy(first).cuda(), want_state=True)
+                        torch.tensor([0, a, a + b], dtype=torch.int32, device="cuda"), want_state=True)
     o2, s2 = tg.gdn_fwd(*(pick(dev[n], idx2) for n in ("q", "k", "v", "alpha", "beta")),
-                        torch.tensor([0, 300, 329], dtype=torch.int32, device="cuda"), state_in=s1, want_state=True)
+                        torch.tensor([0, 700 - a, 829 - a - b], dtype=torch.int32, device="cuda"), state_in=s1,
+                        want_state=True)
     torch.cuda.synchronize()
     whole = torch.empty_like(o)
     whole[torch.from_numpy(idx1).cuda()] = o1
     whole[torch.from_numpy(idx2).cuda()] = o2
     assert torch.equal(whole, o) and torch.equal(s2, st)
+
+
+def test_gdn_zero_decay_and_carried_state():
+    """A decay of exactly 0 (the state resets inside a chunk) and a given start
+    state, against the oracle."""
+    lens = [150, 64, 3]
+    dev, cu = _case(74, lens, 4, 128, 128, "bf16")
+    al = dev["alpha"].clone()
+    al[10, 0] = 0.0
+    al[63, 1] = 0.0
+    al[64, 2] = 0.0
+    al[151, 3] = 0.0
+    rng = np.random.default_rng(74)
+    st0 = torch.from_numpy((0.3 * rng.standard_normal((3, 4, 128, 128))).astype(np.float32)).cuda()
+    o, st = tg.gdn_fwd(dev["q"], dev["k"], dev["v"], al, dev["beta"], dev["cu"], state_in=st0, want_state=True)
+    torch.cuda.synchronize()
+    o_r, st_r = O.gdn_mixer(f64(dev["q"]), f64(dev["k"]), f64(dev["v"]), f64(al), f64(dev["beta"]), cu,
+                            state_in=f64(st0))
+    e = assert_close(f64(o), o_r, "bf16", "gdn output")
+    es = assert_close(st.cpu().numpy(), st_r, "bf16", "gdn state")
+    say("  gdn zero decay + state: max err o %.3g state %.3g" % (e, es))
+
+
+def test_gdn_long_sequence():
+    """One 2048-token sequence (32 chunks: the state crosses many chunk
+    boundaries), two heads, against the oracle."""
+    dev, cu = _case(75, [2048], 2, 128, 128, "bf16")
+    o, st = tg.gdn_fwd(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["cu"], want_state=True)
+    torch.cuda.synchronize()
+    o_r, st_r = O.gdn_mixer(f64(dev["q"]), f64(dev["k"]), f64(dev["v"]), f64(dev["alpha"]), f64(dev["beta"]), cu)
+    e = assert_close(f64(o), o_r, "bf16", "gdn output")
+    es = assert_close(st.cpu().numpy(), st_r, "bf16", "gdn state")
+    say("  gdn 2048 tokens: max err o %.3g state %.3g" % (e, es))
+
+
+def test_gdn_no_tokens():
+    """Every sequence empty (T = 0): the state passes through unchanged."""
+    rng = np.random.default_rng(76)
+    st0 = torch.from_numpy(rng.standard_normal((2, 4, 128, 128)).astype(np.float32)).cuda()
+    e = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((0, 4), dtype=torch.float32, device="cuda")
+    cu = torch.zeros(3, dtype=torch.int32, device="cuda")
+    o, st = tg.gdn_fwd(e, e, e, z, z, cu, state_in=st0, want_state=True)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 4, 128) and torch.equal(st, st0)
 
 
 def test_gdn_on_the_kept_tokens():
