@@ -502,7 +502,7 @@ tg_status tg_compact_scores_bwd(const float* ds_c, const int32_t* kept_idx, int6
  * 0). fp32 runs the token recurrence itself and takes no workspace (ws may
  * be NULL). Splitting a sequence over calls at a multiple of 64 tokens, with
  * the state carried, gives the same bits as one call.
- * Supported: dk in {64, 128}, dv % 32 == 0; q and k 16-byte aligned.
+ * Supported: dk in {64, 128}, dv % 32 == 0; q, k, v and o 16-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t tg_gdn_workspace_size(int64_t T, int B, int H, int dk, int dv, tg_dtype dtype);
 tg_status tg_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha,

@@ -382,7 +382,7 @@ tg_status tg_gdn_fwd(const void* q, const void* k, const void* v, const float* a
   if (B == 0) return TG_OK;
   TG_CHECK(d_cu && (T == 0 || (q && k && v && o && alpha && beta)), TG_ERR_INVALID_ARG);
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
-  TG_CHECK(a16(q) && a16(k) && a16(state_in) && a16(state_out), TG_ERR_INVALID_ARG);
+  TG_CHECK(a16(q) && a16(k) && a16(v) && a16(o) && a16(state_in) && a16(state_out), TG_ERR_INVALID_ARG);
   const bool bf = dtype == TG_BF16;
   if (bf && T > 0) {
     const size_t need = tg::gdn_chunk_workspace_bytes(T, B, H, dk, dv);

@@ -43,16 +43,35 @@ constexpr float LOGA_MIN = -80.f;  // log-decay floor: a = 0 acts as e^-80 insid
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// One (chunk, head) record of the workspace. Every matrix is stored with the
+// 16-byte pieces of each row permuted (piece c of row r at c ^ swz(r)), so
+// that the scan kernel's linear copies into LDS give a layout in which a
+// 16-lane read of 16 consecutive rows, same logical piece, hits 16 distinct
+// 16-byte bank groups: swz(r) = r & 15 for 256-byte rows, (r >> 1) & 7 for
+// 128-byte rows (two rows share the 256-byte bank space).
 template <int DK>
-struct Rec {  // byte offsets inside one (chunk, head) record of the workspace
+struct Rec {
   static constexpr size_t WN = 0;                          // [C][DK] bf16
   static constexpr size_t QG = WN + (size_t)C * DK * 2;    // [C][DK] bf16
   static constexpr size_t PG = QG + (size_t)C * DK * 2;    // [C][C] bf16
   static constexpr size_t KT = PG + (size_t)C * C * 2;     // [DK][C] bf16
-  static constexpr size_t GC = KT + (size_t)DK * C * 2;    // fp32 (padded to 256 bytes)
-  static constexpr size_t UT = GC + 256;                   // [C][dv] fp32
-  __host__ __device__ static size_t bytes(int dv) { return (UT + (size_t)C * dv * 4 + 255) & ~(size_t)255; }
+  static constexpr size_t GC = KT + (size_t)DK * C * 2;    // fp32 (its own 1 KB)
+  static constexpr size_t UT = GC + 1024;                  // dv / 32 blocks of [32 features][C] fp32
+  static constexpr size_t HEAD = UT;                       // bytes every scan workgroup copies
+  __host__ __device__ static size_t bytes(int dv) { return UT + (size_t)C * dv * 4; }
 };
+
+// byte offset of element e (of `esz` bytes) of row r in a row of `rb` bytes
+__device__ __forceinline__ uint32_t swz_off(int r, int e, int esz, int rb) {
+  const int c = e * esz / 16, in = e * esz % 16;
+  const int sw = rb == 256 ? (r & 15) : ((r >> 1) & 7);
+  return (uint32_t)(r * rb + ((c ^ sw) << 4) + in);
+}
+// byte offset of 16-byte piece c of row r
+__device__ __forceinline__ uint32_t swz_piece(int r, int c, int rb) {
+  const int sw = rb == 256 ? (r & 15) : ((r >> 1) & 7);
+  return (uint32_t)(r * rb + ((c ^ sw) << 4));
+}
 
 // first chunk slot of sequence b: cu[b] / C + b (slot ranges of consecutive
 // sequences never overlap; ceil(T / C) + B slots cover a batch)
@@ -211,17 +230,20 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
   }
   __syncthreads();
 
-  // ---- K K^T and Q K^T (raw bf16 products, fp32 accumulators), QG ----
-  const int ti = w >> 1, tj = w & 1;  // this wave's 32 x 32 tile of both
+  // ---- K K^T and K Q^T (raw bf16 products, fp32 accumulators), QG ----
+  // wave w: tile (rows 32 ti.., columns 32 tj..) of K K^T and tile (rows j in
+  // 32 tj.., columns i in 32 ti..) of K Q^T, so that a lane ends with four
+  // consecutive j of one row i of the stored product
+  const int ti = w >> 1, tj = w & 1;
   f32x16 g = zero_f32x16(), pq = zero_f32x16();
 #pragma unroll
   for (int ks = 0; ks < DK / 16; ++ks) {
     const int kc = 16 * ks + 8 * hf;
     const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&S.k[32 * ti + l31][kc]);
-    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&S.u.q[32 * ti + l31][kc]);
+    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(&S.u.q[32 * ti + l31][kc]);
     const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&S.k[32 * tj + l31][kc]);
     g = mfma32(ka, kb, g);
-    pq = mfma32(qa, kb, pq);
+    pq = mfma32(kb, qb, pq);
   }
   // QG[i][d] = g_i nq_i q_i[d]
   for (int p = tid; p < C * DK / 8; p += NT) {
@@ -234,20 +256,34 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
       y[2 * e] = f2bf(__uint_as_float(x[e] << 16) * sc);
       y[2 * e + 1] = f2bf(__uint_as_float(x[e] & 0xffff0000u) * sc);
     }
-    *reinterpret_cast<bf16x8*>(rec + R::QG + ((size_t)r * DK + 8 * c16) * 2) = y;
+    *reinterpret_cast<bf16x8*>(rec + R::QG + swz_piece(r, c16, DK * 2)) = y;
   }
   __syncthreads();  // q is no longer read: its space becomes the system matrix
   {
-    // accumulator: lane holds column j = 32 tj + l31, rows i = 32 ti + 8 (r/4) + 4 hf + r%4
+    // K K^T: lane holds column j = 32 tj + l31, rows i = 32 ti + 8 (r/4) + 4 hf + r%4
     const int j = 32 * tj + l31;
     const float nkj = S.nk[j], lgj = S.lg[j];
-    bf16* pg = reinterpret_cast<bf16*>(rec + R::PG);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * ti + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float dec = j <= i ? __expf(S.lg[i] - lgj) : 0.f;  // g_i / g_j <= 1 below the diagonal
-      S.u.m[i][j] = j < i ? S.be[i] * dec * S.nk[i] * nkj * g[r] : 0.f;
-      pg[i * C + j] = f2bf(S.nq[i] * nkj * dec * pq[r]);
+      const float dec = j < i ? __expf(S.lg[i] - lgj) : 0.f;  // g_i / g_j <= 1 below the diagonal
+      S.u.m[i][j] = S.be[i] * dec * S.nk[i] * nkj * g[r];
+    }
+    // K Q^T: lane holds column i = 32 ti + l31, rows j = 32 tj + 8 (r/4) + 4 hf + r%4;
+    // PG[i][j] = nq_i nk_j (g_i / g_j) q_i . k_j for j <= i, four j per 8-byte store
+    const int i = 32 * ti + l31;
+    const float nqi = S.nq[i], lgi = S.lg[i];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int j0 = 32 * tj + 8 * g4 + 4 * hf;
+      bf16x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = j0 + e;
+        const float dec = jj <= i ? __expf(lgi - S.lg[jj]) : 0.f;
+        y[e] = f2bf(nqi * S.nk[jj] * dec * pq[4 * g4 + e]);
+      }
+      *reinterpret_cast<bf16x4*>(rec + R::PG + swz_off(i, j0, 2, C * 2)) = y;
     }
   }
   __syncthreads();
@@ -282,47 +318,77 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
     }
   } else {
     const float lgC = S.lg[C - 1];
-    bf16* kt = reinterpret_cast<bf16*>(rec + R::KT);
-    for (int p = tid - 64; p < C * DK; p += NT - 64) {
-      const int d = p / C, j = p % C;
-      const float kv = bf2f(S.k[j][d]) * S.nk[j];
-      kt[(size_t)d * C + j] = f2bf(__expf(lgC - S.lg[j]) * kv);
-      S.xt[d][j] = f2bf(S.be[j] * __expf(S.lg[j]) * kv);
+    for (int p = tid - 64; p < DK * (C / 8); p += NT - 64) {
+      const int d = p / (C / 8), jc = p % (C / 8);
+      bf16x8 ykt, yx;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * jc + e;
+        const float kv = bf2f(S.k[j][d]) * S.nk[j];
+        ykt[e] = f2bf(__expf(lgC - S.lg[j]) * kv);
+        yx[e] = f2bf(S.be[j] * __expf(S.lg[j]) * kv);
+      }
+      *reinterpret_cast<bf16x8*>(rec + R::KT + swz_piece(d, jc, C * 2)) = ykt;
+      *reinterpret_cast<bf16x8*>(&S.xt[d][8 * jc]) = yx;
     }
     if (tid == 64) *reinterpret_cast<float*>(rec + R::GC) = __expf(lgC);
   }
   __syncthreads();
 
-  // ---- WN = -T diag(b g) K^ ----
+  // ---- WN = -T diag(b g) K^, as W^T = X^T T^T (rows d, columns i): a lane
+  // ends with four consecutive d of one row i ----
   {
-    bf16* wn = reinterpret_cast<bf16*>(rec + R::WN);
-    t_times_x<DK>(S, w, lane, [&](int rb, int cb, const f32x16& acc) {
-      const int col = 32 * cb + l31;
+    constexpr int NTILE = 2 * (DK / 32);
+    for (int tt = w; tt < NTILE; tt += 4) {
+      const int ib = tt & 1, db = tt >> 1;
+      f32x16 acc = zero_f32x16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * rb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        wn[(size_t)i * DK + col] = f2bf(-acc[r]);
+      for (int ks = 0; ks < C / 16; ++ks) {
+        const int kc = 16 * ks + 8 * hf;
+        const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&S.xt[32 * db + l31][kc]);
+        const bf16x8 th = *reinterpret_cast<const bf16x8*>(&S.u.t.hi[32 * ib + l31][kc]);
+        const bf16x8 tl = *reinterpret_cast<const bf16x8*>(&S.u.t.lo[32 * ib + l31][kc]);
+        acc = mfma32(xa, th, acc);
+        acc = mfma32(xa, tl, acc);
       }
-    });
+      const int i = 32 * ib + l31;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = f2bf(-acc[4 * g4 + e]);
+        *reinterpret_cast<bf16x4*>(rec + R::WN + swz_off(i, d0, 2, DK * 2)) = y;
+      }
+    }
   }
   // ---- Ut = T diag(b) V, DK columns of V at a time ----
-  float* ut = reinterpret_cast<float*>(rec + R::UT);
+  unsigned char* ut = rec + R::UT;  // block col / 32: [32 features][C rows] fp32
   for (int c0 = 0; c0 < dv; c0 += DK) {
     __syncthreads();  // the previous product has read xt
-    for (int p = tid; p < C * DK; p += NT) {
-      const int j = p / DK, col = p % DK;
-      float x = 0.f;
-      if (j < n && c0 + col < dv) x = S.be[j] * bf2f(A.v[((size_t)(tb + j) * H + h) * dv + c0 + col]);
-      S.xt[col][j] = f2bf(x);
+    for (int p = tid; p < C * (DK / 8); p += NT) {
+      const int j = p / (DK / 8), cp = p % (DK / 8);
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (j < n && c0 + 8 * cp < dv)
+        x = *reinterpret_cast<const u32x4*>(A.v + ((size_t)(tb + j) * H + h) * dv + c0 + 8 * cp);
+      const float bj = S.be[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S.xt[8 * cp + 2 * e][j] = f2bf(bj * __uint_as_float(x[e] << 16));
+        S.xt[8 * cp + 2 * e + 1][j] = f2bf(bj * __uint_as_float(x[e] & 0xffff0000u));
+      }
     }
     __syncthreads();
     t_times_x<DK>(S, w, lane, [&](int rb, int cb, const f32x16& acc) {
       const int col = c0 + 32 * cb + l31;
       if (col < dv) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * rb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          ut[(size_t)i * dv + col] = acc[r];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int i0 = 32 * rb + 8 * g4 + 4 * hf;
+          f32x4_t y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = acc[4 * g4 + e];
+          *reinterpret_cast<f32x4_t*>(ut + (size_t)(col >> 5) * (32 * C * 4) + swz_off(col & 31, i0, 4, C * 4)) = y;
         }
       }
     });
@@ -334,24 +400,22 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
 // ---------------------------------------------------------------------------
 template <int DK>
 struct ScanSmem {
-  bf16 s[32][DK + 8];  // chunk-start state, rows r of this block: S[r][d] in bf16
-  bf16 u[32][C + 8];   // U^T[r][j] of the chunk
-};
-
-template <int DK>
-struct Frags {  // one chunk's operands of this wave (A-operand rows, fp32 U start)
-  bf16x8 a[DK / 16];  // WN rows (waves 0, 1) or QG rows (waves 2, 3)
-  bf16x8 p[C / 16];   // PG rows (waves 2, 3)
-  bf16x8 kt[C / 16];  // KT rows (waves holding a tile of S^T)
-  float ut[16];       // Ut entries of the wave's U tile (waves 0, 1)
-  float gc;
+  static constexpr int STAGE = (int)Rec<DK>::HEAD + 32 * C * 4;  // a record's shared part + one U block
+  unsigned char st[2][STAGE];  // the current and the next chunk's operands
+  bf16 s[32][DK + 8];          // chunk-start state, rows r of this block: S[r][d] in bf16
+  bf16 u[32][C + 8];           // U^T[r][j] of the chunk
+  bf16 o[C][32];               // the chunk's output tile, rows i, features r0 .. r0 + 31
 };
 
 template <int DK>
 __global__ __launch_bounds__(NT) void scan_kernel(Args A) {
   using R = Rec<DK>;
+  using SM = ScanSmem<DK>;
   constexpr int DKT = DK / 32;  // tiles of S^T (one per wave w < DKT)
-  __shared__ __attribute__((aligned(16))) ScanSmem<DK> S;
+  constexpr int NP = SM::STAGE / 1024;  // 1 KB copies per stage
+  static_assert(SM::STAGE % 1024 == 0, "stage in whole 1 KB copies");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char gdn_smem[];
+  SM& S = *reinterpret_cast<SM*>(gdn_smem);
   const int H = A.H, dv = A.dv, nrb = dv / 32;
   const int rb = blockIdx.x % nrb, h = (blockIdx.x / nrb) % H, b = blockIdx.x / (nrb * H);
   const int r0 = rb * 32;
@@ -362,17 +426,34 @@ __global__ __launch_bounds__(NT) void scan_kernel(Args A) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l31 = lane & 31, hf = lane >> 5;
   const size_t rbytes = R::bytes(dv);
 
+  // copy chunk c's operands into stage sl: the record's shared part, then
+  // this workgroup's U block (1 KB per wave instruction, direct to LDS);
+  // wave w copies pieces w, w + 4, ...; part k of PARTS issues its share k
+  constexpr int PPW = (NP + 3) / 4, PARTS = 4, PPP = (PPW + PARTS - 1) / PARTS;
+  auto issue = [&](int c, int sl, int part) {
+    const unsigned char* rec = A.ws + ((size_t)(sb + c) * H + h) * rbytes;
+    const uint32_t dst = lds_addr(&S.st[sl][0]);
+#pragma unroll
+    for (int ii = 0; ii < PPP; ++ii) {
+      const int p = w + 4 * (part * PPP + ii);
+      if (part * PPP + ii < PPW && p < NP) {
+        const unsigned char* src = p < (int)(R::HEAD / 1024) ? rec + (size_t)p * 1024
+                                                              : rec + R::UT + (size_t)rb * (32 * C * 4) +
+                                                                    (size_t)(p - R::HEAD / 1024) * 1024;
+        lds_dma16(src + lane * 16, __builtin_amdgcn_readfirstlane(dst + p * 1024));
+      }
+    }
+  };
+
   // S^T tile of wave w: lane holds column r = l31, rows d = 32 w + 8 (q/4) + 4 hf + q%4
   f32x16 st = zero_f32x16();
   const size_t so = (((size_t)b * H + h) * dv + r0 + l31) * DK;
-  if (w < DKT) {
-    if (A.state_in) {
+  if (w < DKT && A.state_in) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(A.state_in + so + 32 * w + 8 * g4 + 4 * hf);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(A.state_in + so + 32 * w + 8 * g4 + 4 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[4 * g4 + e] = x[e];
-      }
+      for (int e = 0; e < 4; ++e) st[4 * g4 + e] = x[e];
     }
   }
   auto put_state = [&]() {
@@ -385,102 +466,114 @@ __global__ __launch_bounds__(NT) void scan_kernel(Args A) {
     }
   };
   if (w < DKT) put_state();
-
-  auto fetch = [&](int c, Frags<DK>& F) {
-    const unsigned char* rec = A.ws + ((size_t)(sb + c) * H + h) * rbytes;
-    const int kc = 8 * hf;
-    if (w < 2) {
-#pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks)
-        F.a[ks] = *reinterpret_cast<const bf16x8*>(rec + R::WN + ((size_t)(32 * w + l31) * DK + 16 * ks + kc) * 2);
-      const float* ut = reinterpret_cast<const float*>(rec + R::UT);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * w + 8 * (r >> 2) + 4 * hf + (r & 3);
-        F.ut[r] = ut[(size_t)i * dv + r0 + l31];
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks)
-        F.a[ks] =
-            *reinterpret_cast<const bf16x8*>(rec + R::QG + ((size_t)(32 * (w - 2) + l31) * DK + 16 * ks + kc) * 2);
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks)
-        F.p[ks] = *reinterpret_cast<const bf16x8*>(rec + R::PG + ((size_t)(32 * (w - 2) + l31) * C + 16 * ks + kc) * 2);
-    }
-    if (w < DKT) {
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks)
-        F.kt[ks] = *reinterpret_cast<const bf16x8*>(rec + R::KT + ((size_t)(32 * w + l31) * C + 16 * ks + kc) * 2);
-    }
-    F.gc = *reinterpret_cast<const float*>(rec + R::GC);
+  // chunk c's output tile leaves from LDS at the start of the next iteration,
+  // 16 bytes per thread (its stores then have a whole chunk to complete
+  // before the wave's next wait)
+  auto store_o = [&](int c) {
+    const int i = tid >> 2, pc = tid & 3;
+    const int64_t t = (int64_t)t0 + c * C + i;
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(&S.o[i][8 * pc]);
+    if (c * C + i < L && t < A.T) *reinterpret_cast<bf16x8*>(A.o + ((size_t)t * H + h) * dv + r0 + 8 * pc) = y;
   };
-
-  Frags<DK> cur;
-  if (nch > 0) fetch(0, cur);
-  __syncthreads();  // the bf16 state is in LDS
-  for (int c = 0; c < nch; ++c) {
-    Frags<DK> nxt;
-    if (c + 1 < nch) fetch(c + 1, nxt);
-    // phase A: U = Ut + WN S0^T (waves 0, 1), O = QG S0^T (waves 2, 3)
-    f32x16 acc;
-    if (w < 2) {
+  if (nch > 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = cur.ut[r];
-    } else {
-      acc = zero_f32x16();
-    }
+    for (int part = 0; part < PARTS; ++part) issue(0, 0, part);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // chunk 0's operands and the bf16 state are in LDS
+  const int ta = w & 1;  // row block of U (waves 0, 1) or O (waves 2, 3)
+  for (int c = 0; c < nch; ++c) {
+    const int sl = c & 1;
+    const unsigned char* stg = S.st[sl];
+    const bool more = c + 1 < nch;
+    if (c > 0) store_o(c - 1);
+    // phase A: U = Ut + WN S0^T (waves 0, 1), O = QG S0^T (waves 2, 3);
+    // every operand read is issued before the MFMAs, the copies of the next
+    // chunk (into the stage read before the previous barrier) between them
+    f32x16 acc;
     {
+      bf16x8 af[DK / 16], sf[DK / 16];
+      const unsigned char* am = stg + (w < 2 ? R::WN : R::QG);
+      const int ar = 32 * ta + l31;
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) {
+        af[ks] = *reinterpret_cast<const bf16x8*>(am + swz_piece(ar, 2 * ks + hf, DK * 2));
+        sf[ks] = *reinterpret_cast<const bf16x8*>(&S.s[l31][16 * ks + 8 * hf]);
+      }
+      if (w < 2) {
+        // Ut block: [32 features r][C rows i] fp32; lane reads 4 rows of column l31 at once
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int pc = (32 * ta + 8 * g4 + 4 * hf) >> 2;
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stg + R::HEAD + swz_piece(l31, pc, C * 4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * g4 + e] = x[e];
+        }
+      } else {
+        acc = zero_f32x16();
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 acc2 = zero_f32x16();
 #pragma unroll
       for (int ks = 0; ks < DK / 16; ks += 2) {
-        const bf16x8 s0 = *reinterpret_cast<const bf16x8*>(&S.s[l31][16 * ks + 8 * hf]);
-        const bf16x8 s1 = *reinterpret_cast<const bf16x8*>(&S.s[l31][16 * ks + 16 + 8 * hf]);
-        acc = mfma32(cur.a[ks], s0, acc);
-        acc2 = mfma32(cur.a[ks + 1], s1, acc2);
+        acc = mfma32(af[ks], sf[ks], acc);
+        acc2 = mfma32(af[ks + 1], sf[ks + 1], acc2);
+        if (more && (ks >> 1) < PARTS) issue(c + 1, sl ^ 1, ks >> 1);
+      }
+      if (more) {
+#pragma unroll
+        for (int part = DK / 32; part < PARTS; ++part) issue(c + 1, sl ^ 1, part);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
     }
     if (w < 2) {
-      // U tile (rows j = 32 w + ..., column r = l31) -> U^T[r][j] in bf16
+      // U tile (rows j = 32 ta + ..., column r = l31) -> U^T[r][j] in bf16
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         bf16x4 y;
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = f2bf(acc[4 * g4 + e]);
-        *reinterpret_cast<bf16x4*>(&S.u[l31][32 * w + 8 * g4 + 4 * hf]) = y;
+        *reinterpret_cast<bf16x4*>(&S.u[l31][32 * ta + 8 * g4 + 4 * hf]) = y;
       }
     }
-    __syncthreads();  // U^T complete; every read of the chunk-start state is done
+    __syncthreads();  // U^T complete; the chunk-start state and the output buffer were read
     // phase B: S^T <- g_C S^T + KT U (waves w < DKT), O += PG U (waves 2, 3)
-    if (w < DKT) {
+    {
+      bf16x8 uf[C / 16], kf[C / 16], pf[C / 16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] *= cur.gc;
+      for (int ks = 0; ks < C / 16; ++ks) uf[ks] = *reinterpret_cast<const bf16x8*>(&S.u[l31][16 * ks + 8 * hf]);
+      if (w < DKT) {
 #pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) {
-        const bf16x8 ub = *reinterpret_cast<const bf16x8*>(&S.u[l31][16 * ks + 8 * hf]);
-        st = mfma32(cur.kt[ks], ub, st);
+        for (int ks = 0; ks < C / 16; ++ks)
+          kf[ks] = *reinterpret_cast<const bf16x8*>(stg + R::KT + swz_piece(32 * w + l31, 2 * ks + hf, C * 2));
       }
-      put_state();
+      if (w >= 2) {
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks)
+          pf[ks] = *reinterpret_cast<const bf16x8*>(stg + R::PG + swz_piece(32 * ta + l31, 2 * ks + hf, C * 2));
+      }
+      const float gc = *reinterpret_cast<const float*>(stg + R::GC);
+      __builtin_amdgcn_sched_barrier(0);
+      if (w < DKT) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] *= gc;
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks) st = mfma32(kf[ks], uf[ks], st);
+      }
+      if (w >= 2) {
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks) acc = mfma32(pf[ks], uf[ks], acc);
+        // output tile: column r = l31, rows i = 32 ta + 8 (q/4) + 4 hf + q%4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S.o[32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3)][l31] = f2bf(acc[r]);
+      }
+      if (w < DKT) put_state();
     }
-    if (w >= 2) {
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) {
-        const bf16x8 ub = *reinterpret_cast<const bf16x8*>(&S.u[l31][16 * ks + 8 * hf]);
-        acc = mfma32(cur.p[ks], ub, acc);
-      }
-      // O tile: column r = l31 (feature r0 + r), rows i = 32 (w-2) + ...
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * (w - 2) + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const int64_t t = (int64_t)t0 + c * C + i;
-        if (c * C + i < L && t < A.T) A.o[((size_t)t * H + h) * dv + r0 + l31] = f2bf(acc[r]);
-      }
-    }
-    __syncthreads();  // the next chunk's state copy is in LDS; U^T may be overwritten
-    if (c + 1 < nch) cur = nxt;
+    wait_vmcnt<0>();  // the next chunk's operands have landed (and this wave's stores are done)
+    __syncthreads();  // the next chunk's state and this chunk's outputs are in LDS; the stage may be refilled
   }
+  if (nch > 0) store_o(nch - 1);
   if (A.state_out && w < DKT) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -499,7 +592,10 @@ hipError_t launch(const Args& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  scan_kernel<DK><<<dim3((unsigned)((int64_t)a.B * a.H * (a.dv / 32))), dim3(NT), 0, stream>>>(a);
+  constexpr size_t lds = sizeof(ScanSmem<DK>);
+  const hipError_t e = ensure_dynamic_lds<scan_kernel<DK>>((int)lds);
+  if (e != hipSuccess) return e;
+  scan_kernel<DK><<<dim3((unsigned)((int64_t)a.B * a.H * (a.dv / 32))), dim3(NT), lds, stream>>>(a);
   return hipGetLastError();
 }
 
