@@ -131,7 +131,10 @@ struct PrepSmem {
     } t;                 // T = hi + lo (products)
   } u;
   bf16 xt[DK][C + 8];  // right operand of T X, transposed: (b g k^)^T, then (b v)^T blocks
+  float tf[C][C + 4];  // T in fp32 (blocked solve)
+  float xb[3][16][17]; // block products of one block diagonal of the solve
   float nk[C], nq[C], lg[C], be[C];
+  float eg[C], egc[C];  // g_j and g_C / g_j
 };
 
 // Y = T X for 2 * DK / 32 output tiles of 32 x 32 (rows of T, columns of X),
@@ -188,32 +191,41 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
   constexpr int KCH = DK / 8;                // 16-byte pieces per row
   constexpr int PPT = C * KCH / NT;          // pieces per thread and matrix
   static_assert(C * KCH % NT == 0 && NT % KCH == 0, "piece split");
+  {
+    // every load in flight before the first use
+    u32x4 x[2][PPT];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const bf16* src = m ? A.q : A.k;
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT, r = p / KCH, c16 = p % KCH;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (r < n) x = *reinterpret_cast<const u32x4*>(src + ((size_t)(tb + r) * H + h) * DK + 8 * c16);
-      *reinterpret_cast<u32x4*>(m ? &S.u.q[r][8 * c16] : &S.k[r][8 * c16]) = x;
-      // the KCH pieces of a row sit in KCH consecutive lanes
-      float s2 = sq8(x);
-      if constexpr (KCH == 16) {
-        s2 = sum16(s2);
-      } else {
-        s2 += dppf<0xB1>(s2);
-        s2 += dppf<0x4E>(s2);
-        s2 += dppf<0x141>(s2);
+      for (int i = 0; i < PPT; ++i) {
+        const int p = tid + i * NT, r = p / KCH, c16 = p % KCH;
+        x[m][i] = u32x4{0u, 0u, 0u, 0u};
+        if (r < n)
+          x[m][i] = *reinterpret_cast<const u32x4*>((m ? A.q : A.k) + ((size_t)(tb + r) * H + h) * DK + 8 * c16);
       }
-      if (c16 == 0) {
-        const float inv = rsqrtf(s2 + EPS);
-        if (m)
-          S.nq[r] = inv * rsqrtf((float)DK);
-        else
-          S.nk[r] = inv;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int p = tid + i * NT, r = p / KCH, c16 = p % KCH;
+        *reinterpret_cast<u32x4*>(m ? &S.u.q[r][8 * c16] : &S.k[r][8 * c16]) = x[m][i];
+        // the KCH pieces of a row sit in KCH consecutive lanes
+        float s2 = sq8(x[m][i]);
+        if constexpr (KCH == 16) {
+          s2 = sum16(s2);
+        } else {
+          s2 += dppf<0xB1>(s2);
+          s2 += dppf<0x4E>(s2);
+          s2 += dppf<0x141>(s2);
+        }
+        if (c16 == 0) {
+          const float inv = rsqrtf(s2 + EPS);
+          if (m)
+            S.nq[r] = inv * rsqrtf((float)DK);
+          else
+            S.nk[r] = inv;
+        }
       }
-    }
   }
   if (w == 0) {
     const bool live = lane < n;
@@ -226,6 +238,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
       if (lane >= o) la += y;
     }
     S.lg[lane] = la;
+    S.eg[lane] = __expf(la);
+    S.egc[lane] = __expf(__shfl(la, 63, 64) - la);
     S.be[lane] = live ? A.beta[(size_t)(tb + lane) * H + h] : 0.f;
   }
   __syncthreads();
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
   // QG[i][d] = g_i nq_i q_i[d]
   for (int p = tid; p < C * DK / 8; p += NT) {
     const int r = p / KCH, c16 = p % KCH;
-    const float sc = __expf(S.lg[r]) * S.nq[r];
+    const float sc = S.eg[r] * S.nq[r];
     const u32x4 x = *reinterpret_cast<const u32x4*>(&S.u.q[r][8 * c16]);
     bf16x8 y;
 #pragma unroll
@@ -288,16 +302,19 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
   }
   __syncthreads();
 
-  // ---- T = (I + M)^-1 by forward substitution (wave 0: lane = column);
-  // waves 1-3 meanwhile write KT and stage (b g k^)^T ----
+  // ---- T = (I + M)^-1, blocked in 16 x 16: wave 0 solves the four diagonal
+  // blocks by forward substitution (lane = block and column); then every
+  // thread takes part in the off-diagonal blocks, one block diagonal at a
+  // time: X_IJ = sum_{J<=K<I} M_IK T_KJ, T_IJ = -T_II X_IJ ----
   if (w == 0) {
-    float tc[C];
+    const int bb = lane >> 4, c = lane & 15;
+    float tc[16];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      float a0 = i == lane ? 1.f : 0.f, a1 = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      float a0 = i == c ? 1.f : 0.f, a1 = 0.f;
 #pragma unroll
       for (int j4 = 0; j4 < i; j4 += 4) {
-        const f32x4_t mr = *reinterpret_cast<const f32x4_t*>(&S.u.m[i][j4]);
+        const f32x4_t mr = *reinterpret_cast<const f32x4_t*>(&S.u.m[16 * bb + i][16 * bb + j4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (j4 + e < i) {
@@ -309,29 +326,71 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
       }
       tc[i] = a0 + a1;
     }
-    // every read of M is done (program order): T overwrites it, split in two bf16
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const bf16 th = f2bf(tc[i]);
-      S.u.t.hi[i][lane] = th;
-      S.u.t.lo[i][lane] = f2bf(tc[i] - bf2f(th));
-    }
-  } else {
-    const float lgC = S.lg[C - 1];
-    for (int p = tid - 64; p < DK * (C / 8); p += NT - 64) {
+    for (int i = 0; i < 16; ++i) S.tf[16 * bb + i][16 * bb + c] = tc[i];  // zeros above the diagonal
+  }
+  {
+    // KT[d][j] = (g_C / g_j) k^_j[d] to the workspace, (b g k^)^T into xt (16 bytes at a time)
+    for (int p = tid; p < DK * (C / 8); p += NT) {
       const int d = p / (C / 8), jc = p % (C / 8);
       bf16x8 ykt, yx;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = 8 * jc + e;
         const float kv = bf2f(S.k[j][d]) * S.nk[j];
-        ykt[e] = f2bf(__expf(lgC - S.lg[j]) * kv);
-        yx[e] = f2bf(S.be[j] * __expf(S.lg[j]) * kv);
+        ykt[e] = f2bf(S.egc[j] * kv);
+        yx[e] = f2bf(S.be[j] * S.eg[j] * kv);
       }
       *reinterpret_cast<bf16x8*>(rec + R::KT + swz_piece(d, jc, C * 2)) = ykt;
       *reinterpret_cast<bf16x8*>(&S.xt[d][8 * jc]) = yx;
     }
-    if (tid == 64) *reinterpret_cast<float*>(rec + R::GC) = __expf(lgC);
+    if (tid == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(S.lg[C - 1]);
+  }
+  __syncthreads();
+  {
+    const int oi = tid >> 4, oc = tid & 15;
+#pragma unroll
+    for (int dd = 1; dd < 4; ++dd) {
+#pragma unroll
+      for (int I = dd; I < 4; ++I) {
+        const int J = I - dd;
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+        for (int K = J; K < I; ++K)
+#pragma unroll
+          for (int k4 = 0; k4 < 16; k4 += 4) {
+            const f32x4_t mr = *reinterpret_cast<const f32x4_t*>(&S.u.m[16 * I + oi][16 * K + k4]);
+            x0 = fmaf(mr[0], S.tf[16 * K + k4][16 * J + oc], x0);
+            x1 = fmaf(mr[1], S.tf[16 * K + k4 + 1][16 * J + oc], x1);
+            x0 = fmaf(mr[2], S.tf[16 * K + k4 + 2][16 * J + oc], x0);
+            x1 = fmaf(mr[3], S.tf[16 * K + k4 + 3][16 * J + oc], x1);
+          }
+        S.xb[I - dd][oi][oc] = x0 + x1;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int I = dd; I < 4; ++I) {
+        float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < 16; k4 += 4) {
+          const f32x4_t tr = *reinterpret_cast<const f32x4_t*>(&S.tf[16 * I + oi][16 * I + k4]);
+          y0 = fmaf(tr[0], S.xb[I - dd][k4][oc], y0);
+          y1 = fmaf(tr[1], S.xb[I - dd][k4 + 1][oc], y1);
+          y0 = fmaf(tr[2], S.xb[I - dd][k4 + 2][oc], y0);
+          y1 = fmaf(tr[3], S.xb[I - dd][k4 + 3][oc], y1);
+        }
+        S.tf[16 * I + oi][16 * (I - dd) + oc] = -(y0 + y1);
+      }
+      __syncthreads();
+    }
+  }
+  // every read of M is done: T overwrites it, split in two bf16 (zero above the diagonal)
+  for (int p = tid; p < C * C; p += NT) {
+    const int i = p / C, j = p % C;
+    const float t = j > i ? 0.f : S.tf[i][j];
+    const bf16 th = f2bf(t);
+    S.u.t.hi[i][j] = th;
+    S.u.t.lo[i][j] = f2bf(t - bf2f(th));
   }
   __syncthreads();
 
@@ -366,16 +425,23 @@ __global__ __launch_bounds__(NT) void prep_kernel(Args A) {
   unsigned char* ut = rec + R::UT;  // block col / 32: [32 features][C rows] fp32
   for (int c0 = 0; c0 < dv; c0 += DK) {
     __syncthreads();  // the previous product has read xt
-    for (int p = tid; p < C * (DK / 8); p += NT) {
-      const int j = p / (DK / 8), cp = p % (DK / 8);
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    constexpr int VPT = C * (DK / 8) / NT;  // 16-byte pieces of V per thread
+    u32x4 xv[VPT];
+#pragma unroll
+    for (int ii = 0; ii < VPT; ++ii) {
+      const int p = tid + ii * NT, j = p / (DK / 8), cp = p % (DK / 8);
+      xv[ii] = u32x4{0u, 0u, 0u, 0u};
       if (j < n && c0 + 8 * cp < dv)
-        x = *reinterpret_cast<const u32x4*>(A.v + ((size_t)(tb + j) * H + h) * dv + c0 + 8 * cp);
+        xv[ii] = *reinterpret_cast<const u32x4*>(A.v + ((size_t)(tb + j) * H + h) * dv + c0 + 8 * cp);
+    }
+#pragma unroll
+    for (int ii = 0; ii < VPT; ++ii) {
+      const int p = tid + ii * NT, j = p / (DK / 8), cp = p % (DK / 8);
       const float bj = S.be[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        S.xt[8 * cp + 2 * e][j] = f2bf(bj * __uint_as_float(x[e] << 16));
-        S.xt[8 * cp + 2 * e + 1][j] = f2bf(bj * __uint_as_float(x[e] & 0xffff0000u));
+        S.xt[8 * cp + 2 * e][j] = f2bf(bj * __uint_as_float(xv[ii][e] << 16));
+        S.xt[8 * cp + 2 * e + 1][j] = f2bf(bj * __uint_as_float(xv[ii][e] & 0xffff0000u));
       }
     }
     __syncthreads();
