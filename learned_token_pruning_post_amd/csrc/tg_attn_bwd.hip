@@ -163,7 +163,8 @@ struct KvSmem {
     // 32-key sub-tile ([d][key])
     float red[G > 1 ? WPK : 1][2][HD * 32];
   };
-  float l2[2][G][32], dl[2][G][32];
+  __attribute__((aligned(16))) float l2[2][G][32];
+  __attribute__((aligned(16))) float dl[2][G][32];
   float dsr[4][32];
   float tgr[4][2];
 };
@@ -276,14 +277,23 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
           sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), kfr[s_], sacc);
           pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), vfr[s_], pacc);
         }
+        // the rows' lse and D, four consecutive rows per read (acc_row order)
+        f32x4 l2v[4], dlv[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          l2v[r4] = *reinterpret_cast<const f32x4*>(&S.l2[sb][gi][acc_row(4 * r4, grp)]);
+          dlv[r4] = *reinterpret_cast<const f32x4*>(&S.dl[sb][gi][acc_row(4 * r4, grp)]);
+        }
         float P[16], dL[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = acc_row(r, grp);
           const bool vis = kval && kj <= q0 + qi;
-          const float pr = vis ? exp2f(fmaf(c2, sacc[r], bias2) - S.l2[sb][gi][qi]) : 0.f;
+          // the exponent is <= 0 up to rounding (P <= 1); hardware exp2, then the mask
+          const float e = __builtin_amdgcn_exp2f(fmaf(c2, sacc[r], bias2) - l2v[r >> 2][r & 3]);
+          const float pr = vis ? e : 0.f;
           P[r] = pr;
-          dL[r] = pr * (pacc[r] - S.dl[sb][gi][qi]);
+          dL[r] = pr * (pacc[r] - dlv[r >> 2][r & 3]);
           dl_acc += dL[r];
           dt_acc = fmaf(dL[r], sacc[r], dt_acc);
         }
@@ -379,7 +389,7 @@ template <int HD>
 struct QSmem {
   bf16 k[2][32 * HD];
   bf16 v[2][32 * HD];
-  float s[2][64];
+  __attribute__((aligned(16))) float s[2][64];
 };
 
 template <int G, int HD>
@@ -461,13 +471,19 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
           sacc = mfma32(TL::chunk(sk, l31, 2 * s_ + grp), qfr[s_], sacc);
           pacc = mfma32(TL::chunk(S.v[sb], l31, 2 * s_ + grp), ofr[s_], pacc);
         }
+        // the keys' scores, four consecutive keys per read (acc_row order)
+        f32x4 sv[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) sv[r4] = *reinterpret_cast<const f32x4*>(&S.s[sb][acc_row(4 * r4, grp)]);
         float dL[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kr = acc_row(r, grp);
           const int kj = k0 + kr;
           const bool vis = qval && kj <= qi && kj < Kb;
-          const float pr = vis ? exp2f(fmaf(c2, sacc[r], g2 * S.s[sb][kr]) - l2) : 0.f;
+          // the exponent is <= 0 up to rounding (P <= 1); hardware exp2, then the mask
+          const float e = __builtin_amdgcn_exp2f(fmaf(c2, sacc[r], g2 * sv[r >> 2][r & 3]) - l2);
+          const float pr = vis ? e : 0.f;
           dL[r] = pr * (pacc[r] - dl);
         }
 #pragma unroll

@@ -238,3 +238,30 @@ def test_decode_outputs_stay_inside_their_buffers(lens):
     _check_all(o, lse, st, ws)
     assert torch.equal(o.t, o_ref) and torch.equal(lse.t, lse_ref) and torch.equal(st.t, st_ref[:B])
 
+
+
+@pytest.mark.parametrize("dtype,lens,dk,dv", [("bf16", [300, 0, 1, 77, 130], 128, 96),
+                                              ("bf16", [64, 65], 64, 160),
+                                              ("f32", [33, 0, 70], 64, 64)])
+def test_gdn_outputs_stay_inside_their_buffers(dtype, lens, dk, dv):
+    """Gated DeltaNet mixer (chunked bf16 path with its chunk records, fp32
+    token path): o, the state and the workspace between guard bands, with a
+    carried start state and partial, empty and one-token sequences; outputs
+    equal to an unguarded call."""
+    B, H, T = len(lens), 4, int(sum(lens))
+    say("canaries, gdn:", dtype, lens, "dk", dk, "dv", dv)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    act = lambda o, shape: to_device(activations(65, o, shape, dtype))
+    q, k, v = act(1, (T, H, dk)), act(2, (T, H, dk)), act(3, (T, H, dv))
+    gen = torch.Generator().manual_seed(65)
+    al = (0.8 + 0.2 * torch.rand((T, H), generator=gen)).cuda()
+    be = torch.rand((T, H), generator=gen).cuda()
+    st0 = (0.3 * torch.randn((B, H, dv, dk), generator=gen)).cuda()
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
+    o_ref, st_ref = tg.gdn_fwd(q, k, v, al, be, cu, state_in=st0, want_state=True)
+    lib = tg.lib()
+    o, st = Guarded("o", (T, H, dv), dt), Guarded("state", (B, H, dv, dk), torch.float32)
+    ws = _ws("gdn ws", lib.tg_gdn_workspace_size(T, B, H, dk, dv, tg.dtype_code(dt)))
+    tg.gdn_fwd(q, k, v, al, be, cu, state_in=st0, o=o.t, state_out=st.t, ws=ws.t if ws.nbytes else None)
+    _check_all(o, st, ws)
+    assert torch.equal(o.t, o_ref) and torch.equal(st.t, st_ref)
