@@ -198,14 +198,14 @@ __global__ __launch_bounds__(NT) void decode_partial_kernel(Args a) {
 #pragma unroll
         for (int u = 1; u < U; ++u) mx = fmaxf(mx, lg[gg][u]);
         const float mn = fmaxf(m[gg], mx);
-        const float al = exp2f(m[gg] - mn);
+        const float al = __builtin_amdgcn_exp2f(m[gg] - mn);
         m[gg] = mn;
         l[gg] *= al;
 #pragma unroll
         for (int e = 0; e < E; ++e) o[gg][e] *= al;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float p = exp2f(lg[gg][u] - mn);
+          const float p = __builtin_amdgcn_exp2f(lg[gg][u] - mn);
           l[gg] += p;
           float vx[E];
           Slice<T>::unpack(vr[u], vx);
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NT) void decode_partial_kernel(Args a) {
     for (int gg = 0; gg < G; ++gg) {
       const float mo = __shfl_xor(m[gg], sh, 64);
       const float mn = fmaxf(m[gg], mo);
-      const float as = exp2f(m[gg] - mn), ao = exp2f(mo - mn);
+      const float as = __builtin_amdgcn_exp2f(m[gg] - mn), ao = __builtin_amdgcn_exp2f(mo - mn);
       l[gg] = l[gg] * as + __shfl_xor(l[gg], sh, 64) * ao;
 #pragma unroll
       for (int e = 0; e < E; ++e) o[gg][e] = o[gg][e] * as + __shfl_xor(o[gg][e], sh, 64) * ao;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(NT) void decode_partial_kernel(Args a) {
     float ls = 0.f, os = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
-      const float sc = exp2f(sm_m[v][gg] - mx);
+      const float sc = __builtin_amdgcn_exp2f(sm_m[v][gg] - mx);
       ls = fmaf(sm_l[v][gg], sc, ls);
       os = fmaf(sm_o[v][gg][e], sc, os);
     }
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(Args a) {
   for (int c = 0; c < nc; ++c) mx = fmaxf(mx, a.pml[2 * (p0 + c)]);
   float ls = 0.f, os = 0.f;
   for (int c = 0; c < nc; ++c) {
-    const float sc = exp2f(a.pml[2 * (p0 + c)] - mx);
+    const float sc = __builtin_amdgcn_exp2f(a.pml[2 * (p0 + c)] - mx);
     ls = fmaf(a.pml[2 * (p0 + c) + 1], sc, ls);
     os = fmaf(a.po[(p0 + c) * D + e], sc, os);
   }
