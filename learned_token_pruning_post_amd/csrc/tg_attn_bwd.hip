@@ -277,6 +277,14 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
           sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), kfr[s_], sacc);
           pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), vfr[s_], pacc);
         }
+        // the fragment reads run two k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s_ = 0; s_ < NS - 2; ++s_) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // the rows' lse and D, four consecutive rows per read (acc_row order)
         f32x4 l2v[4], dlv[4];
 #pragma unroll
@@ -306,6 +314,14 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
             dkT[db] = mfma32(tr_frag<HD>(sq, ks, db, lane), lb, dkT[db]);
           }
         }
+        // the transposing reads (two per MFMA) run two MFMAs ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * ND - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       if (qt + 1 < nq) put_ld(sb ^ 1);
       wait_vmcnt<0>();
@@ -471,6 +487,14 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
           sacc = mfma32(TL::chunk(sk, l31, 2 * s_ + grp), qfr[s_], sacc);
           pacc = mfma32(TL::chunk(S.v[sb], l31, 2 * s_ + grp), ofr[s_], pacc);
         }
+        // the fragment reads run two k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s_ = 0; s_ < NS - 2; ++s_) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // the keys' scores, four consecutive keys per read (acc_row order)
         f32x4 sv[4];
 #pragma unroll
@@ -492,6 +516,14 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
 #pragma unroll
           for (int db = 0; db < ND; ++db) dqT[db] = mfma32(tr_frag<HD>(sk, ks, db, lane), lb, dqT[db]);
         }
+        // the transposing reads (two per MFMA) run two MFMAs ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * ND - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       wait_vmcnt<0>();
       __syncthreads();
