@@ -94,6 +94,20 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// erf without branches: Abramowitz and Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26: erf(a) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 +
+// a5 t^5) exp(-a^2), t = 1 / (1 + p a), a = |x|, absolute error <= 1.5e-7;
+// odd in x. Hardware reciprocal and exp2 (each ~1 ulp).
+__device__ __forceinline__ float erf_fast(float x) {
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f),
+               0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-a * a * TG_LOG2E);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -117,7 +117,7 @@ __device__ __forceinline__ void block_src(const GemmParams& p, int n0, int m0, i
 }
 
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  return 0.5f * z * (1.0f + erf_fast(z * 0.70710678118654752f));
 }
 
 template <int MODE, int BN, int BM, int WN, int WM, int NSTAGE>
@@ -133,6 +133,9 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+  // SCORE: b1 and w2 of the tile's features (zero past N), staged once; the
+  // first k-tile's barrier makes them visible to the epilogue
+  __shared__ float sbw[MODE == MODE_SCORE ? 2 * BN : 1];
 
   // XCD-aware tile order (see the file header)
   int mb, nb;
@@ -158,6 +161,13 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     }
   }
   const int n0 = nb * BN, m0 = mb * BM;
+  if constexpr (MODE == MODE_SCORE) {
+    for (int i = threadIdx.x; i < BN; i += WN * WM * 64) {
+      const bool ok = n0 + i < p.N;
+      sbw[i] = ok ? bf2f(p.b1[n0 + i]) : 0.f;
+      sbw[BN + i] = ok ? bf2f(p.w2[n0 + i]) : 0.f;
+    }
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -556,12 +566,10 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
       for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int n = n0 + wn * TN + j * 32 + rq * 8 + half * 4 + t;
-          if (n < p.N) {
-            const float bb = bf2f(p.b1[n]), ww = bf2f(p.w2[n]);
+          const int nl = wn * TN + j * 32 + rq * 8 + half * 4 + t;  // features past N: b1 = w2 = 0
+          const float bb = sbw[nl], ww = sbw[BN + nl];
 #pragma unroll
-            for (int i = 0; i < SM; ++i) part[i] += gelu_erf(acc[j][i][rq * 4 + t] + bb) * ww;
-          }
+          for (int i = 0; i < SM; ++i) part[i] += gelu_erf(acc[j][i][rq * 4 + t] + bb) * ww;
         }
     __syncthreads();  // every wave is done with the LDS ring
     float* red = reinterpret_cast<float*>(smem);

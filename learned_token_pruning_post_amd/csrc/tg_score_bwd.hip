@@ -32,9 +32,10 @@ constexpr int SLAB = 32;            // tokens per LDS slab
 constexpr int PADW = TILE + 32;     // padded LDS row (elements): 320 bytes, so the four rows of one
                                     // transposing read start 64 bytes apart modulo the 256-byte bank width
 
-__device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erf_fast(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float gelu_grad(float x) {
-  return 0.5f * (1.f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+  return 0.5f * (1.f + erf_fast(x * 0.70710678118654752f)) +
+         x * 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.5f * TG_LOG2E * x * x);
 }
 
 // pass 2: thread k of a block handles hidden unit k (and k + NT, ...) over ROWS_PER_BLOCK tokens
