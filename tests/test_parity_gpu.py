@@ -768,3 +768,42 @@ def test_attention_bias_reduces_to_plain_when_gain_zero():
     o2, _ = tg.gated_attn_fwd(q, k, v, torch.rand(T, device="cuda"), t, g, cu, 300)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_layer_chain_against_oracle_chain(dtype):
+    """Four stacked upper layers on the GPU against the oracle's own four-layer
+    chain, both started from the same compacted rows, positions and scores
+    (compaction is bit-exact): every kept row of the final hidden state and
+    of each layer's K cache within four times the one-layer bound. Each
+    layer's rounding enters the residual stream and is carried forward, so
+    the bound grows with the depth; four layers' worth is the derived limit."""
+    L = 4
+    dims = ModelDims(D=256, Hq=4, Hkv=2, d=64, I=512, H1=64, dtype=dtype)
+    w = custom(31, N=[300, 0, 1, 77, 200], K=[120, 0, 1, 30, 64], F=2, dims=dims, layers=L)
+    dw = DeviceWorkload(w, n_layers=L, keep_host=True)
+    gp = GatedPrefill(dw)
+    gp.score()
+    gp.select()
+    gp.compact()
+    x0 = gp.x.clone()
+    for l in range(L):
+        gp.layer(l)
+    torch.cuda.synchronize()
+    pos, sc, cu = gp.pos_c.cpu().numpy(), f64(gp.s_c), dw.host_gate.cu_kept
+    x = f64(x0)
+    atol, rtol = TOL[dtype]
+    worst = 0.0
+    for l in range(L):
+        r = O.upper_layer(x, pos, sc, layer_dict(dw.host_layers[l]), dims, cu)
+        got_k = f64(gp.kcache[l])
+        lim = L * (atol + rtol * np.abs(r["k"]))
+        assert np.all(np.abs(got_k - r["k"]) <= lim), "layer %d k cache" % l
+        x = r["x2"]
+    err = np.abs(f64(gp.x) - x)
+    lim = L * (atol + rtol * np.abs(x))
+    bad = err > lim
+    assert not bad.any(), "final x: %d/%d outside %d x the one-layer bound, worst %.3g" % (
+        int(bad.sum()), bad.size, L, float(err.max()))
+    worst = float(err.max())
+    say("  %d-layer chain (%s): final x max err %.3g (one-layer atol %g)" % (L, dtype, worst, atol))
