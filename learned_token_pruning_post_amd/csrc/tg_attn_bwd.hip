@@ -163,6 +163,9 @@ struct KvSmem {
     // 32-key sub-tile ([d][key])
     float red[G > 1 ? WPK : 1][2][HD * 32];
   };
+  // K and V rows of the workgroup's key sub-tiles (B operands of S and dP)
+  __attribute__((aligned(16))) bf16 kt[WPK][32 * HD];
+  __attribute__((aligned(16))) bf16 vt[WPK][32 * HD];
   __attribute__((aligned(16))) float l2[2][G][32];
   __attribute__((aligned(16))) float dl[2][G][32];
   float dsr[4][32];
@@ -178,6 +181,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
   constexpr int BPW = 2 * G * NBLK / 4;            // of them per wave and step
   using TL = Tile<HD>;
   using SM = KvSmem<G, HD>;
+  static_assert(sizeof(SM) <= 160 * 1024, "dK/dV LDS fits a CU");
   extern __shared__ __attribute__((aligned(1024))) unsigned char dkdv_smem[];
   auto& S = *reinterpret_cast<SM*>(dkdv_smem);
 
@@ -256,6 +260,14 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
 
     const int qt0 = (kt * BK) / 32;
     __syncthreads();  // the stage buffers (and the reduction area aliasing them) are free
+    if (gi == 0) {  // this sub-tile's K and V rows into LDS (the heads of the group share them)
+#pragma unroll
+      for (int s_ = 0; s_ < NS; ++s_) {
+        const int off = l31 * TL::RB + (((2 * s_ + grp) ^ TL::swz(l31)) << 4);
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(&S.kt[ksub][0]) + off) = kfr[s_];
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(&S.vt[ksub][0]) + off) = vfr[s_];
+      }
+    }
     issue(qt0, 0);
     fetch_ld(qt0);
     put_ld(0);
@@ -263,65 +275,87 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
     __syncthreads();
     for (int qt = qt0; qt < nq; ++qt) {
       const int sb = (qt - qt0) & 1;
+      // the accumulators stay in AGPRs across steps (no copies at the loop back edge)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) asm volatile("" : "+a"(dkT[db]), "+a"(dvT[db]));
       if (qt + 1 < nq) {
         issue(qt + 1, sb ^ 1);
         fetch_ld(qt + 1);
       }
       const int q0 = qt * 32;
-      if (q0 + 31 >= kb) {  // some query of the step sees this wave's keys
+      {  // a step no query of which sees this wave's keys gives P = 0 through the mask
         const bf16* sq = S.st[sb].q[gi];
         const bf16* so = S.st[sb].o[gi];
         f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
+        const bf16* skt = S.kt[ksub];
+        const bf16* svt = S.vt[ksub];
 #pragma unroll
         for (int s_ = 0; s_ < NS; ++s_) {
-          sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), kfr[s_], sacc);
-          pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), vfr[s_], pacc);
+          sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), TL::chunk(skt, l31, 2 * s_ + grp), sacc);
+          pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), TL::chunk(svt, l31, 2 * s_ + grp), pacc);
         }
-        // the fragment reads run two k-steps ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // the fragment reads (four per k-step) run two k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
         for (int s_ = 0; s_ < NS - 2; ++s_) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        // the rows' lse and D, four consecutive rows per read (acc_row order)
-        f32x4 l2v[4], dlv[4];
+        __builtin_amdgcn_sched_barrier(0);
+        // dV / dK products: MFMA i takes (ks, db) = (i / (2 ND), (i / 2) % ND), even i dV
+        // (dO^T, P), odd i dK (Q^T, dL); the transposed fragments are read PF MFMAs ahead,
+        // the first PF of them under the softmax
+        constexpr int NM = 4 * ND, PF = 4;
+        auto trf = [&](int i) { return tr_frag<HD>(i & 1 ? sq : so, i / (2 * ND), (i >> 1) % ND, lane); };
+        bf16x8 fq[NM];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          l2v[r4] = *reinterpret_cast<const f32x4*>(&S.l2[sb][gi][acc_row(4 * r4, grp)]);
-          dlv[r4] = *reinterpret_cast<const f32x4*>(&S.dl[sb][gi][acc_row(4 * r4, grp)]);
-        }
-        float P[16], dL[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = acc_row(r, grp);
-          const bool vis = kval && kj <= q0 + qi;
-          // the exponent is <= 0 up to rounding (P <= 1); hardware exp2, then the mask
-          const float e = __builtin_amdgcn_exp2f(fmaf(c2, sacc[r], bias2) - l2v[r >> 2][r & 3]);
-          const float pr = vis ? e : 0.f;
-          P[r] = pr;
-          dL[r] = pr * (pacc[r] - dlv[r >> 2][r & 3]);
-          dl_acc += dL[r];
-          dt_acc = fmaf(dL[r], sacc[r], dt_acc);
-        }
+        for (int i = 0; i < PF; ++i) fq[i] = trf(i);
+        __builtin_amdgcn_sched_barrier(0);
+        // P and dL eight rows at a time (one k-step of the dV / dK products),
+        // packed to bf16 right away; the rows' lse and D four rows per read
+        bf16x8 pbk[2], lbk[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 pb = pack8(P + 8 * ks), lb = pack8(dL + 8 * ks);
+          float P[8], dL[8];
 #pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            dvT[db] = mfma32(tr_frag<HD>(so, ks, db, lane), pb, dvT[db]);
-            dkT[db] = mfma32(tr_frag<HD>(sq, ks, db, lane), lb, dkT[db]);
+          for (int r4 = 0; r4 < 2; ++r4) {
+            const int rb = 8 * ks + 4 * r4;
+            const f32x4 l2v = *reinterpret_cast<const f32x4*>(&S.l2[sb][gi][acc_row(rb, grp)]);
+            const f32x4 dlv = *reinterpret_cast<const f32x4*>(&S.dl[sb][gi][acc_row(rb, grp)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = rb + e;
+              const int qi = acc_row(r, grp);
+              const bool vis = kval && kj <= q0 + qi;
+              // the exponent is <= 0 up to rounding (P <= 1); hardware exp2, then the mask
+              const float ex = __builtin_amdgcn_exp2f(fmaf(c2, sacc[r], bias2) - l2v[e]);
+              const float pr = vis ? ex : 0.f;
+              P[4 * r4 + e] = pr;
+              dL[4 * r4 + e] = pr * (pacc[r] - dlv[e]);
+              dl_acc += dL[4 * r4 + e];
+              dt_acc = fmaf(dL[4 * r4 + e], sacc[r], dt_acc);
+            }
           }
+          pbk[ks] = pack8(P);
+          lbk[ks] = pack8(dL);
         }
-        // the transposing reads (two per MFMA) run two MFMAs ahead
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4 * ND - 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int i = 0; i < NM; ++i) {
+          if (i + PF < NM) fq[i + PF] = trf(i + PF);
+          const int ks = i / (2 * ND), db = (i >> 1) % ND;
+          if (i & 1)
+            dkT[db] = mfma32(fq[i], lbk[ks], dkT[db]);
+          else
+            dvT[db] = mfma32(fq[i], pbk[ks], dvT[db]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+        for (int i = 0; i < NM - PF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
       }
       if (qt + 1 < nq) put_ld(sb ^ 1);
       wait_vmcnt<0>();
@@ -477,9 +511,12 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
       const int sb = kt & 1;
+      // the accumulators stay in AGPRs across steps (no copies at the loop back edge)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) asm volatile("" : "+a"(dqT[db]));
       if (kt + 1 < nkt) issue(kt + 1, sb ^ 1);
       const int k0 = kt * 32;
-      if (k0 <= q0 + 31) {  // some key of the tile precedes a query of this wave
+      {  // a tile no key of which precedes a query of this wave gives P = 0 through the mask
         const bf16* sk = S.k[sb];
         f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
 #pragma unroll
@@ -495,6 +532,14 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // dQ products: MFMA i takes (ks, db) = (i / ND, i % ND); the transposed K
+        // fragments are read PF MFMAs ahead, the first PF of them under the softmax
+        constexpr int NM = 2 * ND, PF = 4;
+        bf16x8 fq[NM];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) fq[i] = tr_frag<HD>(sk, i / ND, i % ND, lane);
+        __builtin_amdgcn_sched_barrier(0);
         // the keys' scores, four consecutive keys per read (acc_row order)
         f32x4 sv[4];
 #pragma unroll
@@ -510,20 +555,19 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
           const float pr = vis ? e : 0.f;
           dL[r] = pr * (pacc[r] - dl);
         }
+        const bf16x8 lb[2] = {pack8(dL), pack8(dL + 8)};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 lb = pack8(dL + 8 * ks);
-#pragma unroll
-          for (int db = 0; db < ND; ++db) dqT[db] = mfma32(tr_frag<HD>(sk, ks, db, lane), lb, dqT[db]);
+        for (int i = 0; i < NM; ++i) {
+          if (i + PF < NM) fq[i + PF] = tr_frag<HD>(sk, (i + PF) / ND, (i + PF) % ND, lane);
+          dqT[i % ND] = mfma32(fq[i], lb[i / ND], dqT[i % ND]);
         }
-        // the transposing reads (two per MFMA) run two MFMAs ahead
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * ND - 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int i = 0; i < NM - PF; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
       }
       wait_vmcnt<0>();
       __syncthreads();
