@@ -160,7 +160,7 @@ __device__ __forceinline__ void t_times_x(PrepSmem<DK>& S, int w, int lane, Fn&&
 }
 
 template <int DK>
-__global__ __launch_bounds__(NT) void prep_kernel(Args A) {
+__global__ __launch_bounds__(NT, 2) void prep_kernel(Args A) {
   using R = Rec<DK>;
   __shared__ __attribute__((aligned(16))) PrepSmem<DK> S;
   const int H = A.H, dv = A.dv;
@@ -474,7 +474,7 @@ struct ScanSmem {
 };
 
 template <int DK>
-__global__ __launch_bounds__(NT) void scan_kernel(Args A) {
+__global__ __launch_bounds__(NT, 2) void scan_kernel(Args A) {
   using R = Rec<DK>;
   using SM = ScanSmem<DK>;
   constexpr int DKT = DK / 32;  // tiles of S^T (one per wave w < DKT)
