@@ -43,7 +43,7 @@ def assert_close_scaled(got, ref, what, frac=2e-2, rtol=1e-2):
     return float(err.max() / scale) if scale > 0 else 0.0
 
 
-def _attn_case(seed, K, Hq, Hkv, d):
+def _attn_case(seed, K, Hq, Hkv, d, t=None, g=None):
     T = int(sum(K))
     cu = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
     dev = {n: to_device(activations(seed, o, shape, "bf16"))
@@ -51,8 +51,8 @@ def _attn_case(seed, K, Hq, Hkv, d):
                                ("dO", 4, (T, Hq, d)))}
     rng = np.random.default_rng(seed)
     s = rng.random(T).astype(np.float32)
-    t = rng.uniform(0.8, 1.2, Hq).astype(np.float32)
-    g = rng.uniform(0.0, 2.0, Hq).astype(np.float32)
+    t = rng.uniform(0.8, 1.2, Hq).astype(np.float32) if t is None else np.asarray(t, dtype=np.float32)
+    g = rng.uniform(0.0, 2.0, Hq).astype(np.float32) if g is None else np.asarray(g, dtype=np.float32)
     dev.update(s=torch.from_numpy(s).cuda(), t=torch.from_numpy(t).cuda(), g=torch.from_numpy(g).cuda(),
                cu=torch.from_numpy(cu).cuda())
     return dev, cu
@@ -67,8 +67,8 @@ def _attn_bwd(dev, max_k):
     return r
 
 
-def _check_attn(seed, K, Hq, Hkv, d):
-    dev, cu = _attn_case(seed, K, Hq, Hkv, d)
+def _check_attn(seed, K, Hq, Hkv, d, t=None, g=None):
+    dev, cu = _attn_case(seed, K, Hq, Hkv, d, t, g)
     max_k = int(max(K))
     r = _attn_bwd(dev, max_k)
     ref = O.gated_attention_backward(f64(dev["q"]), f64(dev["k"]), f64(dev["v"]), f64(dev["s"]),
@@ -88,6 +88,21 @@ def test_attention_backward_ragged(Hq, Hkv, d):
 
 def test_attention_backward_qwen_shapes_k2048():
     _check_attn(42, [2048], 16, 8, 128)
+
+
+def test_attention_backward_at_the_benchmark_shape():
+    """The backward leg's shape: one sequence of 4096 kept tokens, 16/8 heads x
+    128, every output against the full fp64 oracle."""
+    _check_attn(44, [4096], 16, 8, 128)
+
+
+def test_attention_backward_signed_temperature_and_zero_gain():
+    """Negative and zero temperatures and zero gains (the logit then loses its
+    q.k or its bias term): dt and dg still follow the oracle."""
+    t = [-1.1, 0.0, 0.9, -0.3, 1.0, 0.7, -0.8, 1.2]
+    g = [0.0, 1.5, 0.0, 2.0, -1.0, 0.0, 0.5, 1.0]
+    _check_attn(45, [300, 1, 0, 130], 8, 4, 64, t, g)
+    _check_attn(46, [200, 65], 8, 2, 128, t, g)
 
 
 def test_attention_backward_is_deterministic():

@@ -110,6 +110,21 @@ def test_gdn_long_sequence():
     say("  gdn 2048 tokens: max err o %.3g state %.3g" % (e, es))
 
 
+def test_gdn_at_the_benchmark_shape():
+    """The GDN leg's shape and call: one sequence of 4096 kept tokens, 16 heads,
+    dk = dv = 128, bf16, with a workspace sized by its query; every output and
+    the final state against the oracle."""
+    dev, cu = _case(77, [4096], 16, 128, 128, "bf16")
+    need = tg.lib().tg_gdn_workspace_size(4096, 1, 16, 128, 128, tg.dtype_code(torch.bfloat16))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o, st = tg.gdn_fwd(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["cu"], want_state=True, ws=ws)
+    torch.cuda.synchronize()
+    o_r, st_r = O.gdn_mixer(f64(dev["q"]), f64(dev["k"]), f64(dev["v"]), f64(dev["alpha"]), f64(dev["beta"]), cu)
+    e = assert_close(f64(o), o_r, "bf16", "gdn output")
+    es = assert_close(st.cpu().numpy(), st_r, "bf16", "gdn state")
+    say("  gdn 4096 tokens x 16 heads: max err o %.3g state %.3g" % (e, es))
+
+
 def test_gdn_no_tokens():
     """Every sequence empty (T = 0): the state passes through unchanged."""
     rng = np.random.default_rng(76)
