@@ -138,6 +138,12 @@ def test_scorer_backward_qwen8k():
     _scorer_check(workload("qwen8k"), 52)
 
 
+def test_scorer_backward_at_the_benchmark_shape():
+    """The backward leg's scorer: 32768 prompt tokens, 2048 -> 256."""
+    from learned_token_pruning_post_amd.workloads import workload
+    _scorer_check(workload("qwen32k"), 54)
+
+
 def test_gradient_path_scorer_select_attention():
     """Scores -> selection and compaction -> gated attention on the kept
     tokens -> its backward -> the prompt scores' gradient through the

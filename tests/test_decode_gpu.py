@@ -97,6 +97,12 @@ def test_decode_long_cache():
     _check("bf16", [131072 - 7], [7], 16, 16, 8, 128, seed=2)
 
 
+def test_decode_at_the_benchmark_shape():
+    """The decode leg's call: 16 sequences of 4096 kept prompt tokens plus 128
+    generated ones (segment B at capacity), 16/8 heads x 128."""
+    _check("bf16", [4096] * 16, [128] * 16, 128, 16, 8, 128, seed=5)
+
+
 def test_decode_many_sequences():
     rng = np.random.default_rng(3)
     B = 96
