@@ -163,9 +163,6 @@ struct KvSmem {
     // 32-key sub-tile ([d][key])
     float red[G > 1 ? WPK : 1][2][HD * 32];
   };
-  // K and V rows of the workgroup's key sub-tiles (B operands of S and dP)
-  __attribute__((aligned(16))) bf16 kt[WPK][32 * HD];
-  __attribute__((aligned(16))) bf16 vt[WPK][32 * HD];
   __attribute__((aligned(16))) float l2[2][G][32];
   __attribute__((aligned(16))) float dl[2][G][32];
   float dsr[4][32];
@@ -260,14 +257,6 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
 
     const int qt0 = (kt * BK) / 32;
     __syncthreads();  // the stage buffers (and the reduction area aliasing them) are free
-    if (gi == 0) {  // this sub-tile's K and V rows into LDS (the heads of the group share them)
-#pragma unroll
-      for (int s_ = 0; s_ < NS; ++s_) {
-        const int off = l31 * TL::RB + (((2 * s_ + grp) ^ TL::swz(l31)) << 4);
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(&S.kt[ksub][0]) + off) = kfr[s_];
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(&S.vt[ksub][0]) + off) = vfr[s_];
-      }
-    }
     issue(qt0, 0);
     fetch_ld(qt0);
     put_ld(0);
@@ -287,19 +276,17 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
         const bf16* sq = S.st[sb].q[gi];
         const bf16* so = S.st[sb].o[gi];
         f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
-        const bf16* skt = S.kt[ksub];
-        const bf16* svt = S.vt[ksub];
 #pragma unroll
         for (int s_ = 0; s_ < NS; ++s_) {
-          sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), TL::chunk(skt, l31, 2 * s_ + grp), sacc);
-          pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), TL::chunk(svt, l31, 2 * s_ + grp), pacc);
+          sacc = mfma32(TL::chunk(sq, l31, 2 * s_ + grp), kfr[s_], sacc);
+          pacc = mfma32(TL::chunk(so, l31, 2 * s_ + grp), vfr[s_], pacc);
         }
-        // the fragment reads (four per k-step) run two k-steps ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // the fragment reads run two k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int s_ = 0; s_ < NS - 2; ++s_) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
