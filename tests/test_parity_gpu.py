@@ -756,6 +756,32 @@ def test_attention_many_short_sequences(G, d):
     assert_close(lse.cpu().numpy(), lse_r, "bf16", "lse")
 
 
+@pytest.mark.parametrize("dtype,G,d", [("bf16", 2, 128), ("bf16", 4, 64), ("f32", 2, 64)])
+def test_attention_signed_temperature_and_large_gain(dtype, G, d):
+    """Negative temperatures (the sign moves into q), a zero temperature (only
+    the bias is left: the scale is floored, the bias weight grows to match),
+    zero, negative and large gains, against the oracle."""
+    lens = [1, 200, 0, 129, 64]
+    T, Hkv = sum(lens), 2
+    Hq = Hkv * G
+    q = activations(56, 1, (T, Hq, d), dtype)
+    k = activations(56, 2, (T, Hkv, d), dtype)
+    v = activations(56, 3, (T, Hkv, d), dtype)
+    rng = np.random.default_rng(56)
+    s_c = rng.random(T).astype(np.float32)
+    t = np.array([-1.1, 0.0, 0.9, -0.3, 1.0, 0.7, -0.8, 1.2][:Hq], dtype=np.float32)
+    g = np.array([0.0, 1.5, 12.0, -2.0, -1.0, 0.0, 0.5, 6.0][:Hq], dtype=np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dev = "cuda"
+    o, lse = tg.gated_attn_fwd(to_device(q), to_device(k), to_device(v), torch.from_numpy(s_c).to(dev),
+                               torch.from_numpy(t).to(dev), torch.from_numpy(g).to(dev),
+                               torch.from_numpy(cu).to(dev), max(lens), want_lse=True)
+    torch.cuda.synchronize()
+    o_r, lse_r = O.gated_attention(q.value, k.value, v.value, s_c, t, g, cu)
+    assert_close(f64(o), o_r, dtype, "attention out")
+    assert_close(lse.cpu().numpy(), lse_r, dtype, "lse")
+
+
 def test_attention_bias_reduces_to_plain_when_gain_zero():
     """g = 0: the kernel's result must not depend on s_c at all."""
     lens = [300, 257]
