@@ -159,6 +159,11 @@ __device__ __forceinline__ void t_times_x(PrepSmem<DK>& S, int w, int lane, Fn&&
   }
 }
 
+// Both kernels are bounded to two waves per SIMD (256 registers per wave): with
+// that bound the compiler accumulates the MFMAs in ordinary vector registers;
+// allowed the whole register file it used the accumulation registers and
+// copied every accumulator in and out around the MFMAs (their results are
+// read by vector instructions right after).
 template <int DK>
 __global__ __launch_bounds__(NT, 2) void prep_kernel(Args A) {
   using R = Rec<DK>;

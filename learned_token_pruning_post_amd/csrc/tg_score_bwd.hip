@@ -134,7 +134,9 @@ __device__ __forceinline__ bf16x8 slab_frag(const bf16 (*slab)[PADW], int ks, in
 // pass 4: part[split][m][n] = sum over the split's tokens t of A[t][m] B[t][n]
 // (A = dz [T, M], B = h [T, N]); 4 waves of 64 x 64 on a 128 x 128 tile; the
 // next slab's rows are loaded into registers while the current one is
-// multiplied, then written to the other LDS buffer (one barrier per slab)
+// multiplied, then written to the other LDS buffer (one barrier per slab).
+// Two waves per SIMD at most: the MFMAs then accumulate in vector registers
+// instead of being copied to and from the accumulation registers.
 __global__ __launch_bounds__(NT, 2) void tn_kernel(const bf16* __restrict__ A, const bf16* __restrict__ Bm,
                                                 int64_t T, int M, int N, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) bf16 sa[2][SLAB][PADW];
