@@ -26,7 +26,8 @@
 //  * dQ: mirrors the forward's layout (S^T = K Q^T, one query per lane), one
 //    workgroup per (sequence, kv head, pair of query tiles), K, V and scores
 //    of each 32-key tile staged in LDS; dQ^T += K^T dL^T (K^T by transposing
-//    LDS reads);
+//    LDS reads); like the forward, two groups of four waves take the two
+//    halves of the key range and their partial dQ meet in LDS;
 //  * staging: direct-to-LDS buffer loads over the sequence's rows (reads past
 //    its end give zeros), double-buffered: the next step's tiles are in flight
 //    while the current one is computed, one barrier per step;
@@ -424,23 +425,36 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(Args a) {
 
 template <int HD>
 struct QSmem {
-  bf16 k[2][32 * HD];
-  bf16 v[2][32 * HD];
-  __attribute__((aligned(16))) float s[2][64];
+  struct Ring {  // double-buffered K and V rows and scores of one key-half group
+    bf16 k[2][32 * HD];
+    bf16 v[2][32 * HD];
+    __attribute__((aligned(16))) float s[2][64];
+  };
+  union {
+    Ring r[2];
+    // after the key loop: the second group's dQ^T partials, [wave][d block][register][lane]
+    float red[4][HD / 32][16][64];
+  };
 };
 
 template <int G, int HD>
-__global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
+__global__ __launch_bounds__(2 * NT, 1) void dq_kernel(Args a) {
   constexpr int WPH = 4 / G;  // 32-query sub-tiles per query tile
   constexpr int BQ = 32 * WPH;
   constexpr int NS = HD / 16, ND = HD / 32;
   constexpr int NBLK = 32 * Tile<HD>::RB / 1024;  // 1 KB blocks per 32-row tile
   constexpr int BPW = 2 * NBLK / 4;               // of them per wave and step (K and V)
   using TL = Tile<HD>;
-  __shared__ __attribute__((aligned(1024))) QSmem<HD> S;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char dq_smem[];
+  QSmem<HD>& SQ = *reinterpret_cast<QSmem<HD>*>(dq_smem);
 
+  // two groups of four waves split each query tile's key range in halves (two
+  // waves per SIMD); the second group's dQ partials join the first's through
+  // LDS at the end, in a fixed order
   const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, grp = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w8 >> 2, w = w8 & 3;  // key-half group, wave inside the group
+  auto& S = SQ.r[kg];
   const int gi = w / WPH, qs = w % WPH;
   const int npair = (a.n_qt + 1) >> 1;
   const int wg = blockIdx.x;
@@ -492,18 +506,18 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
     for (int db = 0; db < ND; ++db) dqT[db] = zero_f32x16();
     const int last_key = min(qt * BQ + BQ, Kb) - 1;
     const int nkt = last_key / 32 + 1;
-    __syncthreads();  // the previous pass's readers are done with the buffers
-    issue(0, 0);
+    const int nh = (nkt + 1) >> 1;        // key tiles of group 0 (also the loop count)
+    const int t0 = kg ? nh : 0;           // first key tile of this group
+    const int nt = kg ? nkt - nh : nh;    // key tiles of this group
+    __syncthreads();  // the previous pass's readers (and the merge) are done with the buffers
+    if (nt > 0) issue(t0, 0);
     wait_vmcnt<0>();
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int sb = kt & 1;
-      // the accumulators stay in AGPRs across steps (no copies at the loop back edge)
-#pragma unroll
-      for (int db = 0; db < ND; ++db) asm volatile("" : "+a"(dqT[db]));
-      if (kt + 1 < nkt) issue(kt + 1, sb ^ 1);
-      const int k0 = kt * 32;
-      {  // a tile no key of which precedes a query of this wave gives P = 0 through the mask
+    for (int j = 0; j < nh; ++j) {
+      const int sb = j & 1;
+      if (j + 1 < nt) issue(t0 + j + 1, sb ^ 1);
+      const int k0 = (t0 + j) * 32;
+      if (j < nt) {  // uniform per group; a tile no key of which precedes a query of this wave gives P = 0 through the mask
         const bf16* sk = S.k[sb];
         f32x16 sacc = zero_f32x16(), pacc = zero_f32x16();
 #pragma unroll
@@ -559,7 +573,21 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(Args a) {
       wait_vmcnt<0>();
       __syncthreads();
     }
-    if (qval) {
+    // the key halves meet: group 1 leaves its partials in the idle rings, group 0 adds them
+    if (kg == 1) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) SQ.red[w][db][r][lane] = dqT[db][r];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqT[db][r] += SQ.red[w][db][r][lane];
+    }
+    if (kg == 0 && qval) {
       float* dqr = a.dq + ((size_t)(seq0 + qi) * a.Hq + h) * HD;
 #pragma unroll
       for (int db = 0; db < ND; ++db)
@@ -642,7 +670,10 @@ hipError_t launch_gh(Args a, int max_k, void* ws, hipStream_t stream) {
   if (e != hipSuccess) return e;
   dkdv_kernel<G, HD><<<dim3((unsigned)nwg_kv), dim3(NT), smem, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dq_kernel<G, HD><<<dim3((unsigned)nwg_q), dim3(NT), 0, stream>>>(a);
+  const int smem_q = (int)sizeof(QSmem<HD>);
+  e = ensure_dynamic_lds<dq_kernel<G, HD>>(smem_q);
+  if (e != hipSuccess) return e;
+  dq_kernel<G, HD><<<dim3((unsigned)nwg_q), dim3(2 * NT), smem_q, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   reduce_ds_kernel<<<dim3((unsigned)((a.T + NT - 1) / NT)), dim3(NT), 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
