@@ -127,8 +127,11 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   constexpr int SN = TN / 32, SM = TM / 32;   // MFMA blocks per wave
   constexpr int STAGE = (BN + BM) * 128;      // bytes per LDS stage
   constexpr int NBLK = (BN + BM) / 8;         // 1 KB load blocks per stage
-  constexpr int LPW = NBLK / NW;              // load instructions per wave per stage
-  static_assert(NBLK % NW == 0, "load blocks must split evenly over waves");
+  // the tile loads are issued by one wave per SIMD (waves 0 .. NW/2 - 1); the
+  // other wave of each SIMD only reads fragments and multiplies
+  constexpr int NI = NW / 2;
+  constexpr int LPW = NBLK / NI;              // load instructions per issuing wave per stage
+  static_assert(NBLK % NI == 0, "load blocks must split evenly over the issuing waves");
   static_assert(MODE != MODE_SWIGLU || SN % 2 == 0, "SwiGLU pairs gate/up subtiles");
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -202,14 +205,15 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
     }
     rs.x = make_rsrc(p.X, (uint32_t)p.M * kb);
   }
-  // This wave's load blocks are blk = wave + NW*i. Their source (resource and
-  // first row) does not depend on the k-tile, so it is resolved once; the
+  // An issuing wave's load blocks are blk = wave + NI*i. Their source (resource
+  // and first row) does not depend on the k-tile, so it is resolved once; the
   // k-tile's byte offset goes in the instruction's scalar offset.
+  const bool issuer = wave < NI;
   i32x4 brs[LPW];
   uint32_t bvoff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int blk = wave + NW * i;
+    const int blk = (issuer ? wave : 0) + NI * i;
     int which, r0;
     block_src<MODE, BN, TN>(p, n0, m0, blk, which, r0);
     brs[i] = which == 3 ? rs.x : (which == 2 ? rs.w[2] : (which == 1 ? rs.w[1] : rs.w[0]));
@@ -217,10 +221,12 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
   }
   auto issue = [&](int kt, int st) {
     const uint32_t base_lds = lds0 + st * STAGE + wave * 1024;
+    if (issuer) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      buf_dma16_soff(brs[i], bvoff[i], (uint32_t)kt * 128u,
-                     __builtin_amdgcn_readfirstlane(base_lds + NW * i * 1024));
+      for (int i = 0; i < LPW; ++i)
+        buf_dma16_soff(brs[i], bvoff[i], (uint32_t)kt * 128u,
+                       __builtin_amdgcn_readfirstlane(base_lds + NI * i * 1024));
+    }
   };
 
   // fused RMSNorm (QKV, SwiGLU): threads 2t and 2t+1 request one half each of
@@ -290,12 +296,12 @@ __global__ __launch_bounds__(WN* WM * 64) void gemm_bf16_kernel(GemmParams p, in
       for (int j = 0; j < SN; ++j)
 #pragma unroll
         for (int i = 0; i < SM; ++i) acc[j][i] = mfma32(wf[ks & 1][j], xf[ks & 1][i], acc[j][i]);
-      if (ISSUE) {
+      if (ISSUE && issuer) {
 #pragma unroll
         for (int i = ks * LPK; i < (ks + 1) * LPK; ++i)
           if (i < LPW)
             buf_dma16_soff(brs[i], bvoff[i], (uint32_t)kn * 128u,
-                           __builtin_amdgcn_readfirstlane(base_lds + NW * i * 1024));
+                           __builtin_amdgcn_readfirstlane(base_lds + NI * i * 1024));
       }
     }
     // Issue order of reads and MFMAs (the scheduler would otherwise put each
