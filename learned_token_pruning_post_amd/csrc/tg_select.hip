@@ -689,7 +689,10 @@ __device__ __forceinline__ Decision decide(Smem& S, const Ws& ws, int b, int in0
   }
   // ---- tie prefix, kept counts, output offsets ----
   const uint32_t tex = bscan(eq, S.tmp, tot);  // ties in earlier chunks
-  const uint32_t take = D.needT > tex ? min(D.needT - tex, eq) : 0u;
+  // ties kept in this chunk, written without a guarded subtraction (a form
+  // the compiler has been seen to miscompile: speculated with a no-wrap
+  // flag that then folded a neighbouring min)
+  const uint32_t take = min(D.needT, tex + eq) - min(D.needT, tex);
   const uint32_t kv = own ? S.a[t] + ab + take : 0u;  // forced + keys > T + kept ties
   const uint32_t kex = bscan(kv, S.tmp, tot);
   if (own) {
@@ -808,11 +811,11 @@ __global__ __launch_bounds__(NT) void sc_emit_kernel(
       uint32_t tot;
       const uint32_t ex = bscan((uint32_t)__popc(sure) | ((uint32_t)__popc(tie) << 16), S.tmp, tot);
       const uint32_t tie_before = S.lp[c] + (ex >> 16);  // ties of the sequence before this thread's
-      const uint32_t take = D.needT > tie_before ? min(D.needT - tie_before, (uint32_t)__popc(tie)) : 0u;
+      const uint32_t take = min(D.needT, tie_before + (uint32_t)__popc(tie)) - min(D.needT, tie_before);
       uint32_t rest = tie;  // drop the lowest `take` tie bits: those are kept
       for (uint32_t q = 0; q < take; ++q) rest &= rest - 1u;
       uint32_t keep = sure | (tie ^ rest);
-      const uint32_t kept_before_chunk_ties = D.needT > S.lp[c] ? min(D.needT - S.lp[c], (ex >> 16)) : 0u;
+      const uint32_t kept_before_chunk_ties = min(D.needT, S.lp[c] + (ex >> 16)) - min(D.needT, S.lp[c]);
       int o = (int)(S.a[c] + (ex & 0xffffu) + kept_before_chunk_ties);
       while (keep) {
         const int j = __builtin_ctz(keep);

@@ -482,6 +482,65 @@ def test_select_ties_specials_ragged():
     assert np.array_equal(kept, kept2)
 
 
+def test_select_small_batch_ties_specials_ragged():
+    """A batch of 8 sequences of at most 32768 tokens: ties, NaN, +-0, +-inf
+    and forced tokens mixed in, unaligned sequence starts, one token, an
+    empty sequence, budget = length and budget = forced count; bit-exact with
+    the oracle, flags included, and the same result on a second call."""
+    rng = np.random.default_rng(51)
+    N = [1, 7, 1001, 5000, 32768, 0, 2049, 20003]
+    K = [1, 3, 100, 5000, 4096, 0, 40, 1]
+    T_in = sum(N)
+    s = scores_with_ties(51, T_in, 37)
+    special = rng.choice(T_in, 4000, replace=False)
+    s[special[:1000]] = np.nan
+    s[special[1000:2000]] = -0.0
+    s[special[2000:3000]] = 0.0
+    s[special[3000:3500]] = np.inf
+    s[special[3500:]] = -np.inf
+    mask = np.zeros(T_in, np.uint8)
+    cu = np.concatenate([[0], np.cumsum(N)])
+    for b in range(len(N)):
+        nf = 40 if b == 6 else min(K[b], max(0, N[b] // 50))   # sequence 6: K = F
+        if nf:
+            mask[cu[b] + rng.choice(N[b], nf, replace=False)] = 1
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, flags = O.topk_select(s.astype(np.float32), mask, cu_in, cu_k)
+    assert np.array_equal(status, flags.astype(np.int32))
+    assert np.array_equal(kept, ref.astype(np.int32))
+    kept2, _, _, _ = _select_case(N, K, mask, s)
+    assert np.array_equal(kept, kept2)
+
+
+def test_select_one_bin_nan_threshold_and_flags():
+    """Every candidate key in one bin (all scores equal: the first indices
+    win), the threshold among NaN candidates, and flagged budgets (forced
+    count above the budget, budget above the length) next to good
+    sequences."""
+    N = [32768, 3000, 100, 100, 700]
+    K = [4096, 2990, 10, 101, 650]
+    T_in = sum(N)
+    cu = np.concatenate([[0], np.cumsum(N)])
+    s = np.full(T_in, 0.5, np.float32)
+    s[cu[1]:cu[2]] = np.linspace(-1, 1, N[1], dtype=np.float32)
+    s[cu[1] + np.arange(0, N[1], 100)] = np.nan          # 30 NaN: 20 of them kept
+    s[cu[4]:cu[5]] = np.float32(0.25)
+    s[cu[4] + 3] = np.float32(0.75)
+    mask = np.zeros(T_in, np.uint8)
+    mask[cu[2]:cu[2] + 20] = 1                           # 20 forced > K = 10
+    mask[cu[4] + 600:cu[5]] = 1
+    kept, status, cu_in, cu_k = _select_case(N, K, mask, s)
+    ref, flags = O.topk_select(s, mask, cu_in, cu_k)
+    assert np.array_equal(status, flags.astype(np.int32))
+    assert status[2] & 1 and status[3] & 2
+    for b in range(len(N)):
+        lo, hi = cu_k[b], cu_k[b + 1]
+        if flags[b] & 3:
+            assert (kept[lo:hi] == -1).all(), b
+        else:
+            assert np.array_equal(kept[lo:hi], ref[lo:hi].astype(np.int32)), b
+
+
 def test_select_all_equal_and_budget_extremes():
     N = [4096, 4096, 4096, 5000]
     K = [100, 4096, 512, 4999]

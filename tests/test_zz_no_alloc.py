@@ -62,6 +62,9 @@ def test_noalloc_select_matches_workspace_select_twice():
     calls = [
         ("first", 71, [70001, 45000, 9000], [6000, 45000, 700], 512, 70001),
         ("second, smaller", 72, [40000], [3000], 256, 40000),
+        # sequences of at most 32768 tokens (one chunk size), then a smaller call
+        ("third, short sequences", 73, [30000, 2000, 9000], [3000, 500, 9000], 128, 30000),
+        ("fourth, smaller", 74, [5000], [700], 64, 5000),
     ]
     for what, seed, N, K, F, max_n in calls:
         print("noalloc select:", what, "N", N, "K", K, "max_n", max_n, flush=True)
