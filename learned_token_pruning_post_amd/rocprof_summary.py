@@ -10,6 +10,16 @@
         `bench.py --calib-copy` issues in the same process; writes PREFIX.json (read by
         bench.py) and PREFIX.md
 
+    python -m learned_token_pruning_post_amd.rocprof_summary mfma PMC_DIR --kernel SUBSTR ... --cmd "..."
+        matrix-core use per kernel from one --pmc run (with --kernel-trace) of
+        SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (the
+        latter summed over the XCDs in rocprofv3's per-dispatch row, so divided by
+        their count from agent_info.csv): bf16
+        MFMA flops per dispatch (MOPS x 512), flop rate against the 2.5 PFLOP/s dense bf16
+        peak, busy fraction of the matrix cores over the kernel's active cycles (busy
+        cycles / (GUI_ACTIVE x 1024 SIMDs), rocprofv3's MfmaUtil), and the clock it ran at
+        (GUI_ACTIVE / duration)
+
 The JSON carries a hash of the measured kernel's sources (its own .hip file and the shared
 device headers); bench.py reports the traffic only while those still hash the same, i.e.
 while the counters describe the kernel being timed.
@@ -146,6 +156,67 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, stage=None):
     }
 
 
+SIMD_NUM = 1024            # 256 CUs x 4 SIMDs
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+
+def _by_dispatch(rows, counter):
+    """{dispatch: value} of one counter summed over its rows (rocprofv3 writes
+    one row per dispatch, already summed over the XCDs); names alongside."""
+    vals, names = {}, {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"]
+    return vals, names
+
+
+def _num_xcc(pmc_dir):
+    """XCDs of the GPU agent (agent_info.csv), whose GRBM_GUI_ACTIVE cycle counts
+    the per-dispatch value sums; 8 on MI355X when the file is absent."""
+    try:
+        for r in _rows(_find_csv(pmc_dir, "agent_info.csv")):
+            if r.get("Agent_Type") == "GPU" and int(r.get("Num_Xcc") or 0) > 0:
+                return int(r["Num_Xcc"])
+    except SystemExit:
+        pass
+    return 8
+
+
+def mfma_table(pmc_dir, kernels):
+    """Per kernel-name substring: dispatches, average duration (kernel trace of the
+    same run), bf16 MFMA flops per dispatch, TFLOP/s and fraction of the bf16 peak,
+    MFMA busy % and the clock in GHz."""
+    rows = _rows(_find_csv(pmc_dir, "counter_collection.csv"))
+    mops, names = _by_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy, _ = _by_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui, _ = _by_dispatch(rows, "GRBM_GUI_ACTIVE")
+    xcc = _num_xcc(pmc_dir)
+    gui = {d: v / xcc for d, v in gui.items()}  # cycles of one XCD = of the GPU clock
+    dur = {}
+    for r in _rows(_find_csv(pmc_dir, "kernel_trace.csv")):
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        dur[key] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = []
+    for k in kernels:
+        keys = [d for d, n in names.items() if k in n and d in dur and d in busy and d in gui]
+        if not keys:
+            raise SystemExit("no dispatches of kernels matching %r with every counter" % k)
+        n = len(keys)
+        ns = sum(dur[d] for d in keys) / n
+        flops = sum(mops[d] for d in keys) * 512.0 / n
+        cyc = sum(gui[d] for d in keys) / n
+        util = 100.0 * sum(busy[d] for d in keys) / (sum(gui[d] for d in keys) * SIMD_NUM)
+        tf = flops / ns / 1e3
+        out.append({"kernel_match": k, "kernel_name": names[keys[0]], "dispatches": n,
+                    "avg_us": round(ns / 1e3, 2), "mfma_gflop_per_dispatch": round(flops / 1e9, 3),
+                    "tflops": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "mfma_busy_pct": round(util, 1), "clock_ghz": round(cyc / ns, 3)})
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -163,7 +234,24 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--cmd", required=True, help="the two commands, separated by ' ; '")
     t.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("--kernel", required=True, action="append", help="kernel name substring (repeat)")
+    m.add_argument("--label", action="append", help="row label per --kernel (default: the substring)")
+    m.add_argument("--cmd", required=True, help="the command that produced the run")
+    m.add_argument("--title", default="Matrix-core use")
     a = ap.parse_args(argv)
+    if a.cmd_name == "mfma":
+        res = mfma_table(a.pmc_dir, a.kernel)
+        labels = a.label or a.kernel
+        print("# %s\n\nCommand:\n\n```\n%s\n```\n" % (a.title, a.cmd))
+        print("| kernel | dispatches | avg us (counters on) | MFMA GFLOP / dispatch | TFLOP/s | of 2.5 PF | MFMA busy % | clock GHz |")
+        print("|---|---:|---:|---:|---:|---:|---:|---:|")
+        for lab, r in zip(labels, res):
+            print("| %s | %d | %.2f | %.3f | %.1f | %.3f | %.1f | %.3f |" % (
+                lab, r["dispatches"], r["avg_us"], r["mfma_gflop_per_dispatch"], r["tflops"],
+                r["frac_bf16_peak"], r["mfma_busy_pct"], r["clock_ghz"]))
+        return
     if a.cmd_name == "stats":
         print("# %s\n\nCommand:\n\n```\n%s\n```\n\n%s" % (a.title, a.cmd, stats_table(a.csv, a.top)))
         return

@@ -90,3 +90,37 @@ def test_bench_reports_traffic_only_for_unchanged_sources(tmp_path, monkeypatch)
     with open(tmp_path / "profiles" / "traffic_gate_up_swiglu_w.json", "w") as fh:
         json.dump(rec, fh)
     assert bench.measured_traffic("gate_up_swiglu", "w") is None
+
+
+def test_mfma_table_joins_counters_and_trace(tmp_path):
+    """MOPS x 512 flops per dispatch, busy cycles over GUI_ACTIVE x 1024 SIMDs,
+    GUI_ACTIVE per XCD (its per-dispatch sum over the agent's two XCDs here)
+    over the traced duration."""
+    d = tmp_path / "m"
+    os.makedirs(d)
+    with open(d / "p_agent_info.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Agent_Type", "Num_Xcc"])
+        w.writeheader()
+        w.writerow({"Agent_Type": "CPU", "Num_Xcc": 1})
+        w.writerow({"Agent_Type": "GPU", "Num_Xcc": 2})
+    with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for disp, name in ((1, "void attn<2, 128>(P)"), (2, "void attn<2, 128>(P)"), (3, "other")):
+            for counter, parts in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", (1e6, 1e6)),
+                                   ("SQ_VALU_MFMA_BUSY_CYCLES", (102400.0, 102400.0)),
+                                   ("GRBM_GUI_ACTIVE", (2000.0, 2000.0))):
+                for v in parts:
+                    w.writerow({"Correlation_Id": disp, "Dispatch_Id": disp, "Kernel_Name": name,
+                                "Counter_Name": counter, "Counter_Value": v})
+    with open(d / "p_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for disp in (1, 2, 3):
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": "k", "Start_Timestamp": 1000, "End_Timestamp": 2000})
+    (r,) = R.mfma_table(str(d), ["attn<2, 128>"])
+    assert r["dispatches"] == 2
+    assert r["mfma_gflop_per_dispatch"] == pytest.approx(2e6 * 512 / 1e9)
+    assert r["tflops"] == pytest.approx(2e6 * 512 / 1000 / 1e3)
+    assert r["mfma_busy_pct"] == pytest.approx(100 * 204800 / (2000 * 1024))
+    assert r["clock_ghz"] == pytest.approx(2.0)
