@@ -437,9 +437,10 @@ tg_status tg_full_prefill(const void* h, const int32_t* pos, const uint8_t* keep
  *  Outputs, fp32: dq [T, Hq, d], dk, dv [T, Hkv, d], ds [T] (gradient of the
  *  kept tokens' scores), dt, dg [Hq]. Every element is written (none is
  *  accumulated into), and the results do not depend on timing.
- * Supported: bf16, d in {64, 128}, Hq / Hkv in {1, 2, 4}; q, k, v, o, dO,
- * dq, dk, dv 16-byte aligned. Workspace: tg_gated_attn_bwd_workspace_size()
- * bytes, 256-byte aligned.
+ * Supported: bf16, d in {64, 128}, Hq / Hkv in {1, 2, 4}, one sequence's q
+ * rows below 4 GiB (max_k * Hq * d * 2 bytes, else TG_ERR_UNSUPPORTED); q, k,
+ * v, o, dO, dq, dk, dv 16-byte aligned. Workspace:
+ * tg_gated_attn_bwd_workspace_size() bytes, 256-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t tg_gated_attn_bwd_workspace_size(int B, int64_t T, int max_k, int Hq, int Hkv, int d,
                                         tg_dtype dtype);

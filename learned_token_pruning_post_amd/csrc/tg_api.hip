@@ -301,6 +301,8 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const f
   TG_CHECK(dtype == TG_BF16, TG_ERR_UNSUPPORTED);
   TG_CHECK(tg::attn_bwd_supported(Hq, Hkv, d), TG_ERR_UNSUPPORTED);
   TG_CHECK((int64_t)T * Hq * (d / 8) / 256 < INT_MAX, TG_ERR_UNSUPPORTED);  // prep grid
+  // one sequence's q / dO rows (Hq heads; k / v have Hkv <= Hq) through 32-bit buffer ranges
+  TG_CHECK(fits32(max_k, (int64_t)Hq * d), TG_ERR_UNSUPPORTED);
   if (B == 0 || T == 0 || max_k == 0) return TG_OK;
   TG_CHECK(q && k && v && s_c && t && g && d_cu_kept && o && lse && dO, TG_ERR_INVALID_ARG);
   TG_CHECK(dq && dk && dv && ds && dt && dg, TG_ERR_INVALID_ARG);

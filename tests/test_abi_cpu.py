@@ -205,6 +205,7 @@ def test_attention_backward_argument_errors(L):
     assert call(dt=0) == UNSUP                      # bf16 only
     assert call(Hkv=2) == UNSUP                     # group of 8
     assert call(d=96) == UNSUP
+    assert call(max_k=1 << 20) == UNSUP             # q rows of one sequence reach 4 GiB (32-bit ranges)
     assert call(T=-1) == INVALID
     assert call(q=None) == INVALID
     assert call(dq=None) == INVALID
