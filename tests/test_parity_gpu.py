@@ -425,6 +425,23 @@ def test_fold_norm_weights_ragged_shapes(dtype):
         assert torch.equal(got.cpu(), ref), (rows, cols)
 
 
+def test_scorer_2048x256_ragged_token_counts():
+    """The 2048 -> 256 scorer on batches whose token count is not a multiple
+    of its 128-token tiles (a tail tile with 1, 127 and 129 tokens) and on a
+    single token, against the oracle on every row."""
+    dims = ModelDims(D=2048, Hq=16, Hkv=8, d=128, I=6144, H1=256, dtype="bf16")
+    for seed, N in ((24, [1]), (25, [129]), (26, [1000, 383]), (27, [127, 128, 1])):
+        w = custom(seed, N=N, K=[1] * len(N), F=0, dims=dims)
+        dw = DeviceWorkload(w, n_layers=0, keep_host=True)
+        gp = GatedPrefill(dw)
+        gp.score()
+        torch.cuda.synchronize()
+        gi = dw.host_gate
+        ref = O.gate_score(gi.h.value, gi.W1.value, gi.b1.value, gi.w2.value, gi.b2.value)
+        e = assert_close(gp.s.cpu().numpy(), ref, "bf16", "scores N=%s" % N)
+        say("  scorer 2048x256 N=%s max err %.3g" % (N, e))
+
+
 def test_scorer_wide_hidden_uses_partials():
     dims = ModelDims(D=128, Hq=2, Hkv=1, d=64, I=128, H1=600, dtype="bf16")
     w = custom(23, N=[777], K=[10], F=2, dims=dims)
