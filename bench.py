@@ -632,6 +632,8 @@ def main():
         "gate_up_swiglu": 2.0 * T * D * 2 * I,
         "down_proj_resid": 2.0 * T * I * D,
     }
+    step_flop = kflop["gate_score"] + w.layers * sum(
+        kflop[n] for n in ("qkv_rope_kv", "gated_attn", "o_proj_resid", "gate_up_swiglu", "down_proj_resid"))
     kbytes = {
         "gate_score": w.T_in * D * elt + 4.0 * w.T_in + H1 * D * elt,
         # selection (scores and mask bytes in, kept indices out) + compaction (rows
@@ -724,6 +726,11 @@ def main():
         "ms_per_step_with_kernel_events": round(ms_instr, 4) if ms_instr else None,
         "ms_per_step_hip_graph": round(ms_graph, 4) if ms_graph else None,
         "kept_tokens_per_s": round(w.T / (ms_per_step / 1e3), 1),
+        # algorithmic flops of one step (scorer on the prompt, every upper layer's
+        # projections and gated attention on the kept tokens) over the timed step
+        "path_tflops": round(step_flop / (ms_per_step * 1e-3) / 1e12, 1),
+        "path_frac_mfma_peak": round(step_flop / (ms_per_step * 1e-3) / 1e12 /
+                                     (PEAK_BF16_TFLOPS if dm.dtype == "bf16" else PEAK_F32_TFLOPS), 4),
         "peak_device_mem_gb": round(peak_mem / 1e9, 3),
     }
     if use_ev:
