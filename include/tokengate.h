@@ -118,10 +118,10 @@ tg_status tg_gate_score(const void* h, int64_t T_in, int D, int H1,
  *  d_status  [B]      int32 device out, TG_DEV_* flags of each sequence
  *                     (overwritten, 0 when fine); may be NULL
  *  ws, ws_bytes       scratch of tg_topk_select_workspace_size(B, T_in, max_n)
- *                     bytes, 256-byte aligned, contents irrelevant (about 8
+ *                     bytes, 256-byte aligned, contents irrelevant (about 12
  *                     bytes per input token: per chunk of the sequences a
- *                     record, a list of its score bins and its keys sorted by
- *                     bin). Too small or NULL: TG_ERR_WORKSPACE; misaligned:
+ *                     record, two lists of its score bins and its keys sorted
+ *                     by bin). Too small or NULL: TG_ERR_WORKSPACE; misaligned:
  *                     TG_ERR_INVALID_ARG.
  * Two kernels: per chunk of up to 4096 tokens a summary (forced count, NaN
  * flag, key range, the non-empty bins of the keys' top 16 bits, the keys
@@ -159,7 +159,7 @@ tg_status tg_select_compact(const float* s, const uint8_t* keep_mask,
  * hipMalloc): no ws argument. In place of the workspace this call uses a
  * scratch array of TG_SELECT_NOALLOC_SCRATCH_BYTES that the library holds in
  * device memory, one per GPU for the life of the process, and calls no
- * allocating routine (about half a million input tokens per call).
+ * allocating routine (about 340 thousand input tokens per call).
  * Arguments, outputs and results are those of tg_topk_select. Errors: as
  * tg_topk_select, plus TG_ERR_WORKSPACE when
  * tg_topk_select_workspace_size(B, T_in, max_n) exceeds the scratch size

@@ -102,11 +102,12 @@ def test_topk_select_noalloc_argument_errors(L):
 def test_topk_select_workspace(L):
     """The selection's scratch: per chunk slot (T_in / CH + B + 1 of them) a
     32-byte record, two bin lists and a key array of CH words each, each block
-    256-byte aligned; CH = 256 tokens per chunk, doubled until a sequence of
+    256-byte aligned; CH = 512 tokens per chunk, doubled until a sequence of
     max_n tokens has at most 256 chunks (at most 4096)."""
     a = lambda x: (x + 255) // 256 * 256
-    for B, T_in, max_n, CH in ((3, 200000, 100000, 512), (1, 32768, 32768, 256),
-                               (8, 131072, 16384, 256), (2, 1 << 21, 1 << 20, 4096)):
+    for B, T_in, max_n, CH in ((3, 200000, 100000, 512), (1, 32768, 32768, 512), (1, 8192, 100, 512),
+                               (8, 131072, 16384, 512), (1, 300000, 262145, 2048),
+                               (2, 1 << 21, 1 << 20, 4096)):
         slots = T_in // CH + B + 1
         need = L.tg_topk_select_workspace_size(B, T_in, max_n)
         assert need == a(slots * 32) + 3 * a(slots * CH * 4), (B, T_in, max_n)
